@@ -1,0 +1,217 @@
+"""Benchmark of the ring all-reduce hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one ring all-reduce (R-1 reduce-scatter hops, then R-1 all-gather
+hops, over S slices) of the data-parallel gradient bucket: 8 virtual ranks x
+25 Mi bf16 elements (50 MiB per rank), values normal(0, 1e-3), fp32 adds with
+per-hop bf16 rounding.  Inputs are resident in HBM before the timed region.
+
+Printed: one JSON line with
+  value       bus bandwidth (nccl-tests convention: (b*N/t) * 2(R-1)/R), GB/s
+  hbm         algorithmic HBM bytes of the ring (reduce 3b, copy 2b per
+              element per hop) / time, and the fraction of 8 TB/s
+  roofline    the reduce kernel alone: algorithmic bytes per launch / mean
+              launch duration, measured with HIP events on its own stream
+  gemm        slowdown of a concurrent 8192^3 bf16 GEMM while all-reduces run
+              on a second stream, with kernel copies vs SDMA copies
+  cpu_baseline the CPU oracle on the same workload (1 thread)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "all-reduce busBW GB/s and % HBM peak on 1 MI355X; concurrent-GEMM slowdown %"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def ring_bytes(R, count, esize):
+    """Algorithmic HBM bytes of one ring all-reduce on one GPU."""
+    return (3 + 2) * esize * count * (R - 1)
+
+
+def time_steps(fn, steps, stream=None):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, dim=8192):
+    """Median-free, single-window protocol: G back-to-back GEMMs on stream g,
+    alone and then with all-reduces looping on stream c over the same window.
+    Both streams are released together by an event after a short GPU sleep,
+    so the host has enqueued everything before either starts."""
+    import torch
+    A = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
+    B = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
+    C = torch.empty(dim, dim, dtype=torch.bfloat16, device="cuda")
+    g, c, s0 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+
+    def gemms():
+        for _ in range(n_gemm):
+            torch.matmul(A, B, out=C)
+
+    def window(with_coll, ctx=None, n_coll=0):
+        torch.cuda.synchronize()
+        go = torch.cuda.Event()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s0):
+            torch.cuda._sleep(20_000_000)
+            go.record(s0)
+        g.wait_event(go)
+        c.wait_event(go)
+        with torch.cuda.stream(g):
+            e0.record(g)
+            gemms()
+            e1.record(g)
+        if with_coll:
+            with torch.cuda.stream(c):
+                c0.record(c)
+                for _ in range(n_coll):
+                    ccr.ccr_allreduce(ctx, bufs, stream=c)
+                c1.record(c)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), (c0.elapsed_time(c1) if with_coll else 0.0)
+
+    with torch.cuda.stream(g):
+        gemms()
+    window(False)
+    alone = min(window(False)[0] for _ in range(3))
+    out = {"gemm": f"{dim}x{dim}x{dim} bf16 x{n_gemm}", "gemm_alone_ms": alone}
+    for mode in ("kernel", "sdma"):
+        with ccr.Context(0, ccr.Config(**{**cfg, "copy_mode": mode})) as ctx:
+            t1 = time_steps(lambda: ccr.ccr_allreduce(ctx, bufs), 3)
+            n_coll = max(2, int(1.3 * alone / (t1 * 1e3)) + 1)
+            conc, coll_ms = window(True, ctx, n_coll)
+            out[mode] = {"gemm_ms": conc, "slowdown_pct": 100.0 * (conc / alone - 1.0),
+                         "allreduce_alone_ms": t1 * 1e3, "allreduces": n_coll,
+                         "allreduce_window_ms": coll_ms}
+    return out
+
+
+def cpu_baseline(xs, R, count, esize, S, budget_s=12.0):
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.ring_allreduce(xs, S=S)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s or n >= 20:
+            break
+    t = (time.perf_counter() - t0) / n
+    bus = esize * count / t * 2 * (R - 1) / R / 1e9
+    return {"value": bus, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full workload, {n} all-reduce(s), single-threaded C oracle",
+            "ms_per_step": t * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--slices", type=int, default=None)
+    ap.add_argument("--overlap", type=int, default=0)
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import collective_communication_reduce_amd as ccr
+    import workloads
+
+    w = workloads.DP_BUCKET_BF16
+    R, count, esize = w.R, w.count, 2
+    S = args.slices or w.slices
+    log(f"bench: {w.name}: generating inputs")
+    xs = workloads.ring_inputs(w)
+    bufs = [to_dev(x) for x in xs]
+    cfg = dict(slices=S, overlap=bool(args.overlap))
+    ctx = ccr.Context(0, ccr.Config(**cfg))
+    step = lambda: ccr.ccr_allreduce(ctx, bufs)  # noqa: E731
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t = time_steps(step, args.steps)
+    bus = esize * count / t * 2 * (R - 1) / R / 1e9
+    algo = ring_bytes(R, count, esize) / t / 1e9
+
+    log("bench: per-launch reduce kernel timing")
+    ccr.ccr_profile_enable(ctx, True)
+    for _ in range(args.steps):
+        step()
+    red = ccr.ccr_profile_read(ctx, "reduce")
+    cpy = ccr.ccr_profile_read(ctx, "copy_kernel")
+    ccr.ccr_profile_enable(ctx, False)
+    red_gbs = red["bytes"] / (red["ms"] * 1e6)
+    cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
+
+    gemm = None
+    if not args.no_gemm:
+        log("bench: concurrent GEMM slowdown")
+        gemm = gemm_slowdown(ccr, cfg, bufs)
+
+    cpu = None
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(xs, R, count, esize, S)
+
+    line = {
+        "metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "ranks": R, "count_per_rank": count, "slices": S,
+                   "overlap": bool(args.overlap), "copy_mode": "kernel",
+                   "values": "normal(0, 1e-3)", "accumulation": "fp32 add, bf16 per hop"},
+        "hbm": {"algorithmic_gbs": round(algo, 1), "frac_of_8tbs": round(algo / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pieces_kernel<ReduceBf16> (one reduce-scatter hop over all ranks)",
+                     "launches": red["launches"],
+                     "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
+                     "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
+        "copy_kernel": None if cpy_gbs is None else {
+            "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
+            "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
+        "gemm_slowdown": gemm,
+        "cpu_baseline": cpu,
+    }
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,337 @@
+"""Python binding of libccr, the MI355X ring all-reduce hot path.
+
+A thin ctypes layer over the C ABI in ``include/ccr.h``: every function here
+only marshals arguments (torch tensors -> device pointers, sizes, dtype
+codes, the current HIP stream) and calls the C entry point of the same name.
+All of the work runs in the library's HIP kernels and SDMA copies; there is
+no Python or CPU fallback, and importing this package fails loudly if the
+library has not been built (``python collective_communication_reduce_amd/build.py``).
+
+PyTorch only provides device memory (tensors) and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libccr.so")
+
+CCR_OK, CCR_ERR_INVALID_ARG, CCR_ERR_UNSUPPORTED, CCR_ERR_HIP, CCR_ERR_OOM, CCR_ERR_TIMEOUT = range(6)
+CCR_F32, CCR_BF16 = 0, 1
+CCR_COPY_KERNEL, CCR_COPY_SDMA = 0, 1
+CCR_BF16_ACC_PER_HOP, CCR_BF16_ACC_FP32_PARTIALS = 0, 1
+_STATUS = {1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "out of memory", 5: "timeout"}
+
+
+class CcrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ccr_config_t(ctypes.Structure):
+    _fields_ = [("copy_mode", ctypes.c_int32), ("cu_budget", ctypes.c_int32),
+                ("slices", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("staging_chunk_bytes", ctypes.c_int64), ("staging_slots", ctypes.c_int32),
+                ("bf16_acc", ctypes.c_int32)]
+
+
+class ccr_ring_op_t(ctypes.Structure):
+    _fields_ = [("phase", ctypes.c_int32), ("slice", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("dst_rank", ctypes.c_int32), ("src_rank", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("lo", ctypes.c_int64), ("hi", ctypes.c_int64)]
+
+
+RING_OP_DTYPE = np.dtype([("phase", np.int32), ("slice", np.int32), ("step", np.int32),
+                          ("dst_rank", np.int32), ("src_rank", np.int32), ("chunk", np.int32),
+                          ("lo", np.int64), ("hi", np.int64)])
+
+# Every exported entry point and its argument types.
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+_SIGNATURES = {
+    "ccr_config_default": [ctypes.POINTER(ccr_config_t)],
+    "ccr_ctx_create": [_i32, ctypes.POINTER(ccr_config_t), ctypes.POINTER(_vp)],
+    "ccr_ctx_destroy": [_vp],
+    "ccr_ctx_set_config": [_vp, ctypes.POINTER(ccr_config_t)],
+    "ccr_ctx_get_config": [_vp, ctypes.POINTER(ccr_config_t)],
+    "ccr_ring_schedule": [_i32, _i64, _i32, _i32, _i32, _vp, _i64, ctypes.POINTER(_i64)],
+    "ccr_allreduce": [_vp, _vp, _i32, _i64, _i32, _vp],
+    "ccr_reduce_scatter": [_vp, _vp, _i32, _i64, _i32, _vp],
+    "ccr_all_gather": [_vp, _vp, _i32, _i64, _i32, _vp],
+    "ccr_sendrecv": [_vp, _vp, _vp, _i32, _i64, _vp],
+    "ccr_alltoall": [_vp, _vp, _vp, _i32, _vp, _i64, _vp],
+    "ccr_permute_rows": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "ccr_moe_topk": [_vp, _vp, _vp, _i64, _i32, _i32, _vp],
+    "ccr_moe_plan": [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp],
+    "ccr_moe_dispatch": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp],
+    "ccr_moe_combine": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp],
+    "ccr_last_error": [],
+    "ccr_version": [],
+    "ccr_probe_cu_ids": [_vp, _vp, _i32, _vp],
+    "ccr_profile_enable": [_vp, _i32],
+    "ccr_profile_read": [_vp, _i32, _vp],
+}
+
+
+def _hip_runtimes():
+    """Paths of every HIP runtime library mapped into this process."""
+    try:
+        maps = open("/proc/self/maps").read().splitlines()
+    except OSError:
+        return set()
+    return {l.split()[-1] for l in maps if "libamdhip64.so" in l}
+
+
+def _load():
+    # torch ships its own HIP runtime.  Load it first, so that libccr's
+    # dependency (soname libamdhip64.so.7) resolves to that same runtime:
+    # tensors, streams and libccr's kernels must share one HIP runtime.
+    import torch  # noqa: F401
+    import torch.cuda  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python collective_communication_reduce_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    if len(_hip_runtimes()) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(_hip_runtimes())}); import "
+                          "torch before anything that loads /opt/rocm's libamdhip64")
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("ccr_last_error", "ccr_version") else ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != CCR_OK:
+        raise CcrError(status, _lib.ccr_last_error().decode())
+
+
+def ccr_version() -> str:
+    return _lib.ccr_version().decode()
+
+
+def ccr_last_error() -> str:
+    return _lib.ccr_last_error().decode()
+
+
+# ------------------------------------------------------------------ config
+@dataclass
+class Config:
+    copy_mode: str = "kernel"        # "kernel" | "sdma"
+    cu_budget: int = 0               # 0 = all compute units
+    slices: int = 1
+    overlap: bool = False
+    staging_chunk_bytes: int = 4 << 20
+    staging_slots: int = 2
+    bf16_acc: str = "per_hop"        # "per_hop" | "fp32_partials"
+
+    def to_c(self) -> ccr_config_t:
+        return ccr_config_t(CCR_COPY_SDMA if self.copy_mode == "sdma" else CCR_COPY_KERNEL,
+                            self.cu_budget, self.slices, int(self.overlap),
+                            self.staging_chunk_bytes, self.staging_slots,
+                            CCR_BF16_ACC_FP32_PARTIALS if self.bf16_acc == "fp32_partials"
+                            else CCR_BF16_ACC_PER_HOP)
+
+    @staticmethod
+    def from_c(c: ccr_config_t) -> "Config":
+        return Config("sdma" if c.copy_mode == CCR_COPY_SDMA else "kernel", c.cu_budget,
+                      c.slices, bool(c.overlap), c.staging_chunk_bytes, c.staging_slots,
+                      "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop")
+
+
+def ccr_config_default() -> Config:
+    c = ccr_config_t()
+    _check(_lib.ccr_config_default(ctypes.byref(c)))
+    return Config.from_c(c)
+
+
+class Context:
+    """Owns a ccr_ctx_t (side streams, events, staging slots)."""
+
+    def __init__(self, device: int = 0, config: Optional[Config] = None):
+        self.handle = ctypes.c_void_p()
+        c = config.to_c() if config is not None else None
+        _check(_lib.ccr_ctx_create(device, ctypes.byref(c) if c is not None else None,
+                                   ctypes.byref(self.handle)))
+        self.device = device
+
+    def set_config(self, config: Config):
+        c = config.to_c()
+        _check(_lib.ccr_ctx_set_config(self.handle, ctypes.byref(c)))
+
+    def config(self) -> Config:
+        c = ccr_config_t()
+        _check(_lib.ccr_ctx_get_config(self.handle, ctypes.byref(c)))
+        return Config.from_c(c)
+
+    def close(self):
+        if self.handle:
+            _check(_lib.ccr_ctx_destroy(self.handle))
+            self.handle = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _lib.ccr_ctx_destroy(self.handle)
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------- marshalling
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return CCR_F32
+    if t.dtype == torch.bfloat16:
+        return CCR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptrs(tensors) -> ctypes.Array:
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _same(tensors):
+    n, dt = tensors[0].numel(), tensors[0].dtype
+    if any(t.numel() != n or t.dtype != dt for t in tensors):
+        raise ValueError("all ranks need the same element count and dtype")
+    return n
+
+
+# --------------------------------------------------------------- C entries
+def ccr_ring_schedule(R: int, count: int, slices: int, dtype: int, which: int = 0) -> np.ndarray:
+    n = ctypes.c_int64()
+    _check(_lib.ccr_ring_schedule(R, count, slices, dtype, which, None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, RING_OP_DTYPE)
+    _check(_lib.ccr_ring_schedule(R, count, slices, dtype, which,
+                                  out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
+    return out
+
+
+def ccr_allreduce(ctx: Context, bufs: Sequence, stream=None):
+    n = _same(bufs)
+    _check(_lib.ccr_allreduce(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
+                              _stream(stream)))
+
+
+def ccr_reduce_scatter(ctx: Context, bufs: Sequence, stream=None):
+    n = _same(bufs)
+    _check(_lib.ccr_reduce_scatter(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
+                                   _stream(stream)))
+
+
+def ccr_all_gather(ctx: Context, bufs: Sequence, stream=None):
+    n = _same(bufs)
+    _check(_lib.ccr_all_gather(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
+                               _stream(stream)))
+
+
+def ccr_sendrecv(ctx: Context, send: Sequence, recv: Sequence, stream=None):
+    if len(send) != len(recv):
+        raise ValueError("send and recv need the same number of transfers")
+    nbytes = send[0].numel() * send[0].element_size() if send else 0
+    if any(t.numel() * t.element_size() != nbytes for t in list(send) + list(recv)):
+        raise ValueError("every transfer moves the same number of bytes")
+    _check(_lib.ccr_sendrecv(ctx.handle, _ptrs(send), _ptrs(recv), len(send), nbytes,
+                             _stream(stream)))
+
+
+def ccr_alltoall(ctx: Context, send: Sequence, recv: Sequence, counts, row_bytes: int,
+                 stream=None):
+    R = len(send)
+    counts = np.ascontiguousarray(counts, dtype=np.int64).reshape(R, R)
+    _check(_lib.ccr_alltoall(ctx.handle, _ptrs(send), _ptrs(recv), R, counts.ctypes.data,
+                             row_bytes, _stream(stream)))
+
+
+def ccr_permute_rows(ctx: Context, dst, src, idx, stream=None):
+    row_bytes = (src.numel() // max(1, src.shape[0])) * src.element_size()
+    _check(_lib.ccr_permute_rows(ctx.handle, dst.data_ptr(), src.data_ptr(), idx.data_ptr(),
+                                 idx.numel(), src.shape[0], row_bytes, _stream(stream)))
+
+
+def ccr_moe_topk(ctx: Context, logits, topk, stream=None):
+    T, E = logits.shape
+    _check(_lib.ccr_moe_topk(ctx.handle, logits.data_ptr(), topk.data_ptr(), T, E,
+                             topk.shape[1], _stream(stream)))
+
+
+def ccr_moe_plan(ctx: Context, topk, E: int, R: int, src_tok, slot, stream=None) -> np.ndarray:
+    """Blocking: returns the host int64 [E] row counts per expert."""
+    T, K = topk.shape
+    ecnt = np.zeros(E, np.int64)
+    _check(_lib.ccr_moe_plan(ctx.handle, topk.data_ptr(), T, E, K, R, src_tok.data_ptr(),
+                             slot.data_ptr(), ecnt.ctypes.data, _stream(stream)))
+    return ecnt
+
+
+def ccr_moe_dispatch(ctx: Context, x: Sequence, src_tok: Sequence, ecnt, K: int,
+                     send: Sequence, recv: Sequence, exp: Sequence, stream=None):
+    R = len(x)
+    T = x[0].shape[0]
+    row_bytes = x[0][0].numel() * x[0].element_size()
+    ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
+    _check(_lib.ccr_moe_dispatch(ctx.handle, _ptrs(x), _ptrs(src_tok), ecnt.ctypes.data, R, T,
+                                 ecnt.shape[1], K, row_bytes, _ptrs(send), _ptrs(recv),
+                                 _ptrs(exp), _stream(stream)))
+
+
+def ccr_moe_combine(ctx: Context, exp: Sequence, slot: Sequence, ecnt, T: int, K: int,
+                    recv: Sequence, send: Sequence, out: Sequence, stream=None):
+    R = len(exp)
+    row_bytes = exp[0][0].numel() * exp[0].element_size()
+    ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
+    _check(_lib.ccr_moe_combine(ctx.handle, _ptrs(exp), _ptrs(slot), ecnt.ctypes.data, R, T,
+                                ecnt.shape[1], K, row_bytes, _ptrs(recv), _ptrs(send),
+                                _ptrs(out), _stream(stream)))
+
+
+def ccr_probe_cu_ids(ctx: Context, nblocks: int, stream=None):
+    """(nblocks, 3) int32 tensor of (XCC id, SE id, CU id) per workgroup."""
+    import torch
+    out = torch.zeros(nblocks, 3, dtype=torch.int32, device=f"cuda:{ctx.device}")
+    _check(_lib.ccr_probe_cu_ids(ctx.handle, out.data_ptr(), nblocks, _stream(stream)))
+    return out
+
+
+class ccr_kernel_stats_t(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64), ("bytes", ctypes.c_int64), ("ms", ctypes.c_double)]
+
+
+PROFILE_KINDS = {"reduce": 0, "copy_kernel": 1, "sdma": 2}
+
+
+def ccr_profile_enable(ctx: Context, on: bool = True):
+    _check(_lib.ccr_profile_enable(ctx.handle, int(on)))
+
+
+def ccr_profile_read(ctx: Context, kind: str) -> dict:
+    st = ccr_kernel_stats_t()
+    _check(_lib.ccr_profile_read(ctx.handle, PROFILE_KINDS[kind], ctypes.byref(st)))
+    return {"launches": st.launches, "bytes": st.bytes, "ms": st.ms}

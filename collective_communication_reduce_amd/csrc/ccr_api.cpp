@@ -1,0 +1,934 @@
+// Host runtime of the ring all-reduce hot path: context, argument checks,
+// the ring chunk scheduler, and the stream manager that orders reduce
+// kernels, copy kernels and SDMA copies against the caller's stream.
+//
+// Method: "HOCCL: Offloading Collective Communication from GPU Cores to
+// Accelerate Distributed Training".  What is taken from it:
+//  - copies may run on DMA (SDMA) engines instead of compute units
+//    (Fig. 1c; §2.3 DMA Engines), while reductions stay on the compute units
+//    (§5 Limitations);
+//  - communication keeps its place in the caller's stream order relative
+//    to the kernels before and after it (§3.2 Stream Manager); here events
+//    between the caller's stream and the library's side streams do this;
+//  - P2P transfers are staged through a pool of chunk slots whose fill and
+//    drain overlap, each slot going idle -> filling -> draining -> idle
+//    (§3.3.1 DMA-RNIC chunk pipelining; Fig. 4 state machine);
+//  - a collective is a schedule of P2P flows, cut into chunks (§3.4).
+// The ring order itself is the textbook ring (the paper describes none).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ccr.h"
+#include "ccr_internal.h"
+
+using namespace ccr;
+
+// ------------------------------------------------------------------ errors
+namespace {
+
+thread_local std::string g_last_error;
+
+ccr_status_t fail(ccr_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ccr_status_t hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();  // clear the sticky per-thread error
+  return fail(e == hipErrorOutOfMemory ? CCR_ERR_OOM : CCR_ERR_HIP, "%s failed: %s (%d)", what,
+              hipGetErrorString(e), (int)e);
+}
+
+#define HIP_TRY(expr)                                  \
+  do {                                                 \
+    hipError_t _e = (expr);                            \
+    if (_e != hipSuccess) return hip_fail(_e, #expr);  \
+  } while (0)
+
+#define CCR_TRY(expr)                    \
+  do {                                   \
+    ccr_status_t _s = (expr);            \
+    if (_s != CCR_OK) return _s;         \
+  } while (0)
+
+constexpr int kMaxRanks = 64;
+static_assert(kMaxRanks <= kMaxPieces, "one hop of every rank fits one launch");
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align_up(int64_t a, int64_t v) { return ceil_div(a, v) * v; }
+int wrap(int a, int m) { return ((a % m) + m) % m; }
+
+int dtype_size(int dtype) { return dtype == CCR_F32 ? 4 : dtype == CCR_BF16 ? 2 : 0; }
+
+}  // namespace
+
+// ----------------------------------------------------------------- context
+struct ccr_ctx {
+  int device = 0;
+  int num_cus = 0;
+  ccr_config_t cfg{};
+  bool masked = false;          // s_a / s_b carry a CU mask
+  hipStream_t s_a = nullptr;    // reduce / fill / exchange side stream
+  hipStream_t s_b = nullptr;    // all-gather (overlap) / drain side stream
+  std::vector<hipEvent_t> ev;   // event pool, grown on demand
+  char* staging = nullptr;      // staging_slots x staging_chunk_bytes
+  int64_t staging_bytes = 0;
+  int64_t* d_ecnt = nullptr;    // MoE plan counts scratch
+  int64_t d_ecnt_len = 0;
+  int64_t* h_pinned = nullptr;  // pinned mirror of d_ecnt
+  // per-launch timing (ccr_profile_enable): event pairs and payload bytes
+  bool prof_on = false;
+  struct Timed {
+    int kind;
+    hipEvent_t start, stop;
+    int64_t bytes;
+  };
+  std::vector<Timed> timed;
+  std::vector<hipEvent_t> timing_pool;
+};
+
+namespace {
+
+ccr_status_t check_config(const ccr_config_t* c) {
+  if (c->copy_mode != CCR_COPY_KERNEL && c->copy_mode != CCR_COPY_SDMA)
+    return fail(CCR_ERR_INVALID_ARG, "copy_mode %d is not kernel (0) or sdma (1)", c->copy_mode);
+  if (c->cu_budget < 0) return fail(CCR_ERR_INVALID_ARG, "cu_budget %d < 0", c->cu_budget);
+  if (c->slices < 1 || c->slices > 1024)
+    return fail(CCR_ERR_INVALID_ARG, "slices %d outside [1, 1024]", c->slices);
+  if (c->overlap != 0 && c->overlap != 1)
+    return fail(CCR_ERR_INVALID_ARG, "overlap %d is not 0 or 1", c->overlap);
+  if (c->staging_chunk_bytes <= 0 || c->staging_chunk_bytes % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "staging_chunk_bytes %lld is not a positive multiple of 16",
+                (long long)c->staging_chunk_bytes);
+  if (c->staging_slots < 1 || c->staging_slots > 64)
+    return fail(CCR_ERR_INVALID_ARG, "staging_slots %d outside [1, 64]", c->staging_slots);
+  if (c->bf16_acc != CCR_BF16_ACC_PER_HOP && c->bf16_acc != CCR_BF16_ACC_FP32_PARTIALS)
+    return fail(CCR_ERR_INVALID_ARG, "bf16_acc %d is not per_hop (0) or fp32_partials (1)",
+                c->bf16_acc);
+  return CCR_OK;
+}
+
+// Compute units of the CU mask for a budget of B: mask bit i is handed to
+// XCC (i mod num_xcc) by the driver, so the lowest B bits spread the budget
+// evenly over the XCDs.
+std::vector<uint32_t> cu_mask_for_budget(int budget, int num_cus) {
+  std::vector<uint32_t> mask((size_t)(num_cus + 31) / 32, 0u);
+  for (int i = 0; i < budget && i < num_cus; i++) mask[(size_t)i / 32] |= 1u << (i % 32);
+  return mask;
+}
+
+ccr_status_t destroy_streams(ccr_ctx* ctx) {
+  if (ctx->s_a) HIP_TRY(hipStreamSynchronize(ctx->s_a));
+  if (ctx->s_b) HIP_TRY(hipStreamSynchronize(ctx->s_b));
+  if (ctx->s_a) HIP_TRY(hipStreamDestroy(ctx->s_a));
+  if (ctx->s_b) HIP_TRY(hipStreamDestroy(ctx->s_b));
+  ctx->s_a = ctx->s_b = nullptr;
+  ctx->masked = false;
+  return CCR_OK;
+}
+
+ccr_status_t make_streams(ccr_ctx* ctx) {
+  CCR_TRY(destroy_streams(ctx));
+  const int budget = ctx->cfg.cu_budget;
+  if (budget > 0 && budget < ctx->num_cus) {
+    std::vector<uint32_t> mask = cu_mask_for_budget(budget, ctx->num_cus);
+    HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_a, (uint32_t)mask.size(), mask.data()));
+    HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_b, (uint32_t)mask.size(), mask.data()));
+    ctx->masked = true;
+  } else {
+    HIP_TRY(hipStreamCreateWithFlags(&ctx->s_a, hipStreamNonBlocking));
+    HIP_TRY(hipStreamCreateWithFlags(&ctx->s_b, hipStreamNonBlocking));
+  }
+  return CCR_OK;
+}
+
+ccr_status_t events(ccr_ctx* ctx, size_t n) {
+  while (ctx->ev.size() < n) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->ev.push_back(e);
+  }
+  return CCR_OK;
+}
+
+// Make `to` wait for everything enqueued on `from` so far.
+ccr_status_t order_after(ccr_ctx* ctx, size_t ev_index, hipStream_t from, hipStream_t to) {
+  if (from == to) return CCR_OK;
+  CCR_TRY(events(ctx, ev_index + 1));
+  HIP_TRY(hipEventRecord(ctx->ev[ev_index], from));
+  HIP_TRY(hipStreamWaitEvent(to, ctx->ev[ev_index], 0));
+  return CCR_OK;
+}
+
+ccr_status_t check_ctx(ccr_ctx* ctx) {
+  if (!ctx) return fail(CCR_ERR_INVALID_ARG, "ctx is NULL");
+  HIP_TRY(hipSetDevice(ctx->device));
+  return CCR_OK;
+}
+
+// A 16-byte aligned device pointer on this context's device whose next
+// nbytes bytes lie inside one HIP allocation.
+ccr_status_t check_dev_ptr(ccr_ctx* ctx, const void* p, int64_t nbytes, const char* what,
+                           int index) {
+  if (!p) return fail(CCR_ERR_INVALID_ARG, "%s[%d] is NULL", what, index);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p is not 16-byte aligned", what, index, p);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p is not HIP memory", what, index, p);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p is not device memory", what, index, p);
+  if (attr.device != ctx->device)
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p lives on device %d, not %d", what, index, p,
+                attr.device, ctx->device);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p: allocation range unknown", what, index, p);
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  if (q < b || (uint64_t)nbytes > (uint64_t)(b + size - q))
+    return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p: %lld bytes run past the end of its allocation",
+                what, index, p, (long long)nbytes);
+  return CCR_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  int id;
+};
+
+ccr_status_t check_disjoint(std::vector<Range> r, const char* what) {
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); i++)
+    if (r[i].lo < r[i - 1].hi)
+      return fail(CCR_ERR_INVALID_ARG, "%s: buffers %d and %d overlap", what, r[i - 1].id,
+                  r[i].id);
+  return CCR_OK;
+}
+
+// ----------------------------------------------------------- ring schedule
+// Chunk c of `count` elements over R ranks, 16-byte aligned (V elements).
+void chunk_range(int64_t count, int R, int V, int c, int64_t* lo, int64_t* hi) {
+  const int64_t L = align_up(ceil_div(count, R), V);
+  *lo = std::min<int64_t>(count, (int64_t)c * L);
+  *hi = std::min<int64_t>(count, (int64_t)(c + 1) * L);
+}
+
+// Slice s of the element range [clo, chi), cut into S aligned slices.
+void slice_range(int64_t clo, int64_t chi, int S, int V, int s, int64_t* lo, int64_t* hi) {
+  const int64_t len = chi - clo;
+  const int64_t L = align_up(ceil_div(len, S), V);
+  *lo = clo + std::min<int64_t>(len, (int64_t)s * L);
+  *hi = clo + std::min<int64_t>(len, (int64_t)(s + 1) * L);
+}
+
+enum { kRS = 0, kAG = 1 };
+
+// The R operations of one hop: rank q works on chunk (q-k-2) mod R for a
+// reduce-scatter hop and chunk (q-k-1) mod R for an all-gather hop, reading
+// rank q-1 (mod R).  Within a hop no chunk of any rank is both read and
+// written, so the R operations run as one launch.
+void hop_ops(int phase, int k, int s, int R, int64_t count, int S, int V,
+             std::vector<ccr_ring_op_t>* out) {
+  for (int q = 0; q < R; q++) {
+    const int c = wrap(q - k - (phase == kRS ? 2 : 1), R);
+    int64_t clo, chi, lo, hi;
+    chunk_range(count, R, V, c, &clo, &chi);
+    slice_range(clo, chi, S, V, s, &lo, &hi);
+    out->push_back(ccr_ring_op_t{phase, s, k, q, wrap(q - 1, R), c, lo, hi});
+  }
+}
+
+enum { kWhichAllreduce = 0, kWhichRS = 1, kWhichAG = 2 };
+
+void ring_schedule(int R, int64_t count, int S, int V, int which,
+                   std::vector<ccr_ring_op_t>* out) {
+  for (int s = 0; s < S; s++) {
+    if (which != kWhichAG)
+      for (int k = 0; k + 1 < R; k++) hop_ops(kRS, k, s, R, count, S, V, out);
+    if (which != kWhichRS)
+      for (int k = 0; k + 1 < R; k++) hop_ops(kAG, k, s, R, count, S, V, out);
+  }
+}
+
+LaunchTuning tuning() {
+  // Overridable for tuning sweeps; defaults chosen by measurement.
+  static LaunchTuning t = [] {
+    LaunchTuning x{4, 0};
+    if (const char* e = getenv("CCR_UNROLL")) x.unroll = atoi(e);
+    if (const char* e = getenv("CCR_NONTEMPORAL")) x.nontemporal = atoi(e);
+    return x;
+  }();
+  return t;
+}
+
+enum { kProfReduce = 0, kProfCopyKernel = 1, kProfSdma = 2 };
+
+ccr_status_t timing_event(ccr_ctx* ctx, hipEvent_t* e) {
+  if (!ctx->timing_pool.empty()) {
+    *e = ctx->timing_pool.back();
+    ctx->timing_pool.pop_back();
+    return CCR_OK;
+  }
+  HIP_TRY(hipEventCreate(e));
+  return CCR_OK;
+}
+
+// Bracket one launch with timing events when profiling is on.
+struct TimedScope {
+  ccr_ctx* ctx;
+  hipStream_t s;
+  int kind;
+  int64_t bytes;
+  hipEvent_t start = nullptr;
+  ccr_status_t begin() {
+    if (!ctx->prof_on) return CCR_OK;
+    CCR_TRY(timing_event(ctx, &start));
+    HIP_TRY(hipEventRecord(start, s));
+    return CCR_OK;
+  }
+  ccr_status_t end() {
+    if (!ctx->prof_on) return CCR_OK;
+    hipEvent_t stop;
+    CCR_TRY(timing_event(ctx, &stop));
+    HIP_TRY(hipEventRecord(stop, s));
+    ctx->timed.push_back(ccr_ctx::Timed{kind, start, stop, bytes});
+    return CCR_OK;
+  }
+};
+
+int64_t payload(const Piece* p, size_t n) {
+  int64_t b = 0;
+  for (size_t i = 0; i < n; i++) b += p[i].nbytes;
+  return b;
+}
+
+ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hipStream_t s) {
+  const bool reduce = kind != HopKind::kCopy;
+  TimedScope t{ctx, s, reduce ? kProfReduce : kProfCopyKernel, payload(p, (size_t)n) * (reduce ? 3 : 2)};
+  CCR_TRY(t.begin());
+  HIP_TRY(launch_pieces(kind, p, n, tuning(), s));
+  return t.end();
+}
+
+// Copy `n` pieces on `s`: one kernel launch per kMaxPieces pieces, or one
+// SDMA transfer per piece.
+ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) {
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
+    for (size_t i = 0; i < n; i++) {
+      if (p[i].nbytes <= 0) continue;
+      TimedScope t{ctx, s, kProfSdma, 2 * p[i].nbytes};
+      CCR_TRY(t.begin());
+      HIP_TRY(hipMemcpyAsync(p[i].dst, p[i].src, (size_t)p[i].nbytes,
+                             hipMemcpyDeviceToDeviceNoCU, s));
+      CCR_TRY(t.end());
+    }
+    return CCR_OK;
+  }
+  for (size_t i = 0; i < n; i += kMaxPieces) {
+    const int m = (int)std::min<size_t>(kMaxPieces, n - i);
+    CCR_TRY(launch_timed(ctx, HopKind::kCopy, p + i, m, s));
+  }
+  return CCR_OK;
+}
+
+ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
+                      int which, hipStream_t caller) {
+  CCR_TRY(check_ctx(ctx));
+  if (!bufs) return fail(CCR_ERR_INVALID_ARG, "bufs is NULL");
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (count < 0) return fail(CCR_ERR_INVALID_ARG, "count %lld < 0", (long long)count);
+  const int esize = dtype_size(dtype);
+  if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
+  if (dtype == CCR_BF16 && which != kWhichAG && ctx->cfg.bf16_acc != CCR_BF16_ACC_PER_HOP)
+    return fail(CCR_ERR_UNSUPPORTED, "bf16 fp32-partials accumulation is not built");
+  if (count == 0) return CCR_OK;
+  std::vector<Range> ranges;
+  for (int q = 0; q < R; q++) {
+    CCR_TRY(check_dev_ptr(ctx, bufs[q], count * esize, "bufs", q));
+    const uintptr_t p = reinterpret_cast<uintptr_t>(bufs[q]);
+    ranges.push_back(Range{p, p + (uintptr_t)(count * esize), q});
+  }
+  CCR_TRY(check_disjoint(ranges, "bufs"));
+  if (R == 1) return CCR_OK;
+
+  const int V = 16 / esize, S = ctx->cfg.slices;
+  const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
+  // Reduce-scatter runs on the CU-masked stream when a budget is set, else
+  // directly on the caller's stream.  All-gather follows it on the same
+  // stream, or on the second side stream when overlap is on.
+  hipStream_t rs = ctx->masked ? ctx->s_a : caller;
+  hipStream_t ag = ctx->cfg.overlap ? ctx->s_b : rs;
+  const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
+  CCR_TRY(events(ctx, ev_slice0 + (size_t)S));
+  if (rs != caller || ag != caller) {
+    HIP_TRY(hipEventRecord(ctx->ev[ev_fork], caller));
+    if (rs != caller) HIP_TRY(hipStreamWaitEvent(rs, ctx->ev[ev_fork], 0));
+    if (ag != caller && ag != rs) HIP_TRY(hipStreamWaitEvent(ag, ctx->ev[ev_fork], 0));
+  }
+
+  std::vector<ccr_ring_op_t> ops;
+  ops.reserve((size_t)R);
+  std::vector<Piece> pieces((size_t)R);
+  auto to_pieces = [&](int* n) {
+    *n = 0;
+    for (const ccr_ring_op_t& o : ops) {
+      if (o.hi <= o.lo) continue;
+      pieces[(size_t)(*n)++] = Piece{static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize,
+                                     static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize,
+                                     (o.hi - o.lo) * esize};
+    }
+  };
+  for (int s = 0; s < S; s++) {
+    if (which != kWhichAG) {
+      for (int k = 0; k + 1 < R; k++) {
+        ops.clear();
+        hop_ops(kRS, k, s, R, count, S, V, &ops);
+        int n;
+        to_pieces(&n);
+        CCR_TRY(launch_timed(ctx, reduce, pieces.data(), n, rs));
+      }
+    }
+    if (which != kWhichRS) {
+      if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
+      for (int k = 0; k + 1 < R; k++) {
+        ops.clear();
+        hop_ops(kAG, k, s, R, count, S, V, &ops);
+        int n;
+        to_pieces(&n);
+        CCR_TRY(copy_pieces(ctx, pieces.data(), (size_t)n, ag));
+      }
+    }
+  }
+  CCR_TRY(order_after(ctx, ev_join_rs, rs, caller));
+  if (ag != rs) CCR_TRY(order_after(ctx, ev_join_ag, ag, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ensure_staging(ccr_ctx* ctx) {
+  const int64_t need = ctx->cfg.staging_chunk_bytes * ctx->cfg.staging_slots;
+  if (ctx->staging && ctx->staging_bytes >= need) return CCR_OK;
+  if (ctx->staging) {
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipFree(ctx->staging));
+    ctx->staging = nullptr;
+  }
+  HIP_TRY(hipMalloc(reinterpret_cast<void**>(&ctx->staging), (size_t)need));
+  ctx->staging_bytes = need;
+  return CCR_OK;
+}
+
+ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* recv, int R,
+                          const int64_t* counts, int64_t row_bytes, hipStream_t s) {
+  std::vector<Piece> p;
+  p.reserve((size_t)R * R);
+  std::vector<int64_t> roff((size_t)R, 0);
+  for (int r = 0; r < R; r++) {
+    int64_t soff = 0;
+    for (int d = 0; d < R; d++) {
+      const int64_t c = counts[(size_t)r * R + d];
+      if (c > 0)
+        p.push_back(Piece{static_cast<char*>(recv[d]) + roff[(size_t)d] * row_bytes,
+                          static_cast<const char*>(send[r]) + soff * row_bytes, c * row_bytes});
+      soff += c;
+      roff[(size_t)d] += c;
+    }
+  }
+  return copy_pieces(ctx, p.data(), p.size(), s);
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+  const char* e = getenv(name);
+  return e && *e ? strtoll(e, nullptr, 0) : dflt;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+const char* ccr_last_error(void) { return g_last_error.c_str(); }
+
+const char* ccr_version(void) { return "ccr 0.1.0 gfx950"; }
+
+ccr_status_t ccr_config_default(ccr_config_t* cfg) {
+  if (!cfg) return fail(CCR_ERR_INVALID_ARG, "cfg is NULL");
+  cfg->copy_mode = CCR_COPY_KERNEL;
+  cfg->cu_budget = 0;
+  cfg->slices = 1;
+  cfg->overlap = 0;
+  cfg->staging_chunk_bytes = 4 << 20;
+  cfg->staging_slots = 2;
+  cfg->bf16_acc = CCR_BF16_ACC_PER_HOP;
+  if (const char* e = getenv("CCR_COPY_MODE"); e && *e)
+    cfg->copy_mode = strcmp(e, "sdma") == 0 ? CCR_COPY_SDMA : CCR_COPY_KERNEL;
+  if (const char* e = getenv("CCR_BF16_ACC"); e && *e)
+    cfg->bf16_acc = strcmp(e, "fp32_partials") == 0 ? CCR_BF16_ACC_FP32_PARTIALS
+                                                    : CCR_BF16_ACC_PER_HOP;
+  cfg->cu_budget = (int32_t)env_int("CCR_CU_BUDGET", cfg->cu_budget);
+  cfg->slices = (int32_t)env_int("CCR_SLICES", cfg->slices);
+  cfg->overlap = (int32_t)env_int("CCR_OVERLAP", cfg->overlap);
+  cfg->staging_chunk_bytes = env_int("CCR_STAGING_CHUNK", cfg->staging_chunk_bytes);
+  cfg->staging_slots = (int32_t)env_int("CCR_STAGING_SLOTS", cfg->staging_slots);
+  return check_config(cfg);
+}
+
+ccr_status_t ccr_ctx_create(int device, const ccr_config_t* cfg, ccr_ctx_t* out) {
+  if (!out) return fail(CCR_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  ccr_config_t c;
+  if (cfg) {
+    c = *cfg;
+    CCR_TRY(check_config(&c));
+  } else {
+    CCR_TRY(ccr_config_default(&c));
+  }
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev)
+    return fail(CCR_ERR_INVALID_ARG, "device %d outside [0, %d)", device, ndev);
+  HIP_TRY(hipSetDevice(device));
+  ccr_ctx* ctx = new ccr_ctx();
+  ctx->device = device;
+  ctx->cfg = c;
+  hipError_t e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
+  ccr_status_t st = e == hipSuccess ? make_streams(ctx) : hip_fail(e, "hipDeviceGetAttribute");
+  if (st == CCR_OK) st = events(ctx, 8);
+  if (st != CCR_OK) {
+    std::string msg = g_last_error;
+    ccr_ctx_destroy(ctx);
+    g_last_error = msg;
+    return st;
+  }
+  *out = ctx;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
+  if (!ctx) return CCR_OK;
+  (void)hipSetDevice(ctx->device);
+  ccr_status_t st = destroy_streams(ctx);
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
+  for (auto& t : ctx->timed) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (hipEvent_t e : ctx->timing_pool) (void)hipEventDestroy(e);
+  if (ctx->staging) (void)hipFree(ctx->staging);
+  if (ctx->d_ecnt) (void)hipFree(ctx->d_ecnt);
+  if (ctx->h_pinned) (void)hipHostFree(ctx->h_pinned);
+  delete ctx;
+  return st;
+}
+
+ccr_status_t ccr_ctx_set_config(ccr_ctx_t ctx, const ccr_config_t* cfg) {
+  CCR_TRY(check_ctx(ctx));
+  if (!cfg) return fail(CCR_ERR_INVALID_ARG, "cfg is NULL");
+  CCR_TRY(check_config(cfg));
+  const bool restream = cfg->cu_budget != ctx->cfg.cu_budget;
+  HIP_TRY(hipStreamSynchronize(ctx->s_a));
+  HIP_TRY(hipStreamSynchronize(ctx->s_b));
+  ctx->cfg = *cfg;
+  if (restream) CCR_TRY(make_streams(ctx));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_ctx_get_config(ccr_ctx_t ctx, ccr_config_t* cfg) {
+  if (!ctx || !cfg) return fail(CCR_ERR_INVALID_ARG, "ctx or cfg is NULL");
+  *cfg = ctx->cfg;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int which,
+                               ccr_ring_op_t* ops, int64_t max_ops, int64_t* n_ops) {
+  if (!n_ops) return fail(CCR_ERR_INVALID_ARG, "n_ops is NULL");
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (count < 0 || slices < 1 || slices > 1024 || max_ops < 0)
+    return fail(CCR_ERR_INVALID_ARG, "bad count, slices or max_ops");
+  if (which < 0 || which > 2) return fail(CCR_ERR_INVALID_ARG, "which %d outside [0, 2]", which);
+  const int esize = dtype_size(dtype);
+  if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
+  std::vector<ccr_ring_op_t> v;
+  ring_schedule(R, count, slices, 16 / esize, which, &v);
+  *n_ops = (int64_t)v.size();
+  if (ops) std::copy(v.begin(), v.begin() + std::min<int64_t>(max_ops, (int64_t)v.size()), ops);
+  return CCR_OK;
+}
+
+ccr_status_t ccr_allreduce(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
+                           void* stream) {
+  return run_ring(ctx, bufs, R, count, dtype, kWhichAllreduce, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_reduce_scatter(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
+                                void* stream) {
+  return run_ring(ctx, bufs, R, count, dtype, kWhichRS, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
+                            void* stream) {
+  return run_ring(ctx, bufs, R, count, dtype, kWhichAG, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* recv, int n,
+                          int64_t nbytes, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (n < 0 || nbytes < 0) return fail(CCR_ERR_INVALID_ARG, "n or nbytes < 0");
+  if (nbytes % 16 != 0) return fail(CCR_ERR_INVALID_ARG, "nbytes %lld is not a multiple of 16", (long long)nbytes);
+  if (n == 0 || nbytes == 0) return CCR_OK;
+  if (!send || !recv) return fail(CCR_ERR_INVALID_ARG, "send or recv is NULL");
+  std::vector<Range> ranges;
+  for (int m = 0; m < n; m++) {
+    CCR_TRY(check_dev_ptr(ctx, send[m], nbytes, "send", m));
+    CCR_TRY(check_dev_ptr(ctx, recv[m], nbytes, "recv", m));
+    const uintptr_t a = reinterpret_cast<uintptr_t>(send[m]), b = reinterpret_cast<uintptr_t>(recv[m]);
+    ranges.push_back(Range{a, a + (uintptr_t)nbytes, 2 * m});
+    ranges.push_back(Range{b, b + (uintptr_t)nbytes, 2 * m + 1});
+  }
+  CCR_TRY(check_disjoint(ranges, "send/recv"));
+  CCR_TRY(ensure_staging(ctx));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t fill = ctx->s_a, drain = ctx->s_b;
+  const int P = ctx->cfg.staging_slots;
+  const int64_t C = ctx->cfg.staging_chunk_bytes;
+  // events: 0 fork, 1-2 joins, then filled[p] = 3 + p, drained[p] = 3 + P + p
+  CCR_TRY(events(ctx, (size_t)(3 + 2 * P)));
+  CCR_TRY(order_after(ctx, 0, caller, fill));
+  HIP_TRY(hipStreamWaitEvent(drain, ctx->ev[0], 0));
+  std::vector<bool> used((size_t)P, false);
+  int64_t chunk = 0;
+  for (int m = 0; m < n; m++) {
+    for (int64_t off = 0; off < nbytes; off += C, chunk++) {
+      const int p = (int)(chunk % P);
+      const int64_t len = std::min<int64_t>(C, nbytes - off);
+      char* slot = ctx->staging + (int64_t)p * C;
+      hipEvent_t filled = ctx->ev[(size_t)(3 + p)], drained = ctx->ev[(size_t)(3 + P + p)];
+      // idle -> filling: only once the slot's previous chunk has drained
+      if (used[(size_t)p]) HIP_TRY(hipStreamWaitEvent(fill, drained, 0));
+      Piece in{slot, static_cast<const char*>(send[m]) + off, len};
+      CCR_TRY(copy_pieces(ctx, &in, 1, fill));
+      HIP_TRY(hipEventRecord(filled, fill));
+      // filling -> draining -> idle
+      HIP_TRY(hipStreamWaitEvent(drain, filled, 0));
+      Piece out{static_cast<char*>(recv[m]) + off, slot, len};
+      CCR_TRY(copy_pieces(ctx, &out, 1, drain));
+      HIP_TRY(hipEventRecord(drained, drain));
+      used[(size_t)p] = true;
+    }
+  }
+  CCR_TRY(order_after(ctx, 1, fill, caller));
+  CCR_TRY(order_after(ctx, 2, drain, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
+                          const int64_t* counts, int64_t row_bytes, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (!send || !recv || !counts) return fail(CCR_ERR_INVALID_ARG, "send, recv or counts is NULL");
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "row_bytes %lld is not a positive multiple of 16", (long long)row_bytes);
+  std::vector<int64_t> sent((size_t)R, 0), got((size_t)R, 0);
+  for (int r = 0; r < R; r++)
+    for (int d = 0; d < R; d++) {
+      const int64_t c = counts[(size_t)r * R + d];
+      if (c < 0) return fail(CCR_ERR_INVALID_ARG, "counts[%d][%d] < 0", r, d);
+      sent[(size_t)r] += c;
+      got[(size_t)d] += c;
+    }
+  std::vector<Range> ranges;
+  for (int r = 0; r < R; r++) {
+    if (sent[(size_t)r] > 0) {
+      CCR_TRY(check_dev_ptr(ctx, send[r], sent[(size_t)r] * row_bytes, "send", r));
+      const uintptr_t a = reinterpret_cast<uintptr_t>(send[r]);
+      ranges.push_back(Range{a, a + (uintptr_t)(sent[(size_t)r] * row_bytes), r});
+    }
+    if (got[(size_t)r] > 0) {
+      CCR_TRY(check_dev_ptr(ctx, recv[r], got[(size_t)r] * row_bytes, "recv", r));
+      const uintptr_t b = reinterpret_cast<uintptr_t>(recv[r]);
+      ranges.push_back(Range{b, b + (uintptr_t)(got[(size_t)r] * row_bytes), R + r});
+    }
+  }
+  CCR_TRY(check_disjoint(ranges, "send/recv"));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  CCR_TRY(run_alltoall(ctx, send, recv, R, counts, row_bytes, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void* dst, const void* src, const int32_t* d_idx,
+                              int64_t nrows, int64_t nsrc, int64_t row_bytes, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (nrows < 0 || nsrc < 0) return fail(CCR_ERR_INVALID_ARG, "nrows or nsrc < 0");
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "row_bytes %lld is not a positive multiple of 16", (long long)row_bytes);
+  if (nrows == 0) return CCR_OK;
+  CCR_TRY(check_dev_ptr(ctx, dst, nrows * row_bytes, "dst", 0));
+  CCR_TRY(check_dev_ptr(ctx, d_idx, nrows * 4, "d_idx", 0));
+  if (nsrc > 0) CCR_TRY(check_dev_ptr(ctx, src, nsrc * row_bytes, "src", 0));
+  std::vector<Range> ranges{{reinterpret_cast<uintptr_t>(dst),
+                             reinterpret_cast<uintptr_t>(dst) + (uintptr_t)(nrows * row_bytes), 0},
+                            {reinterpret_cast<uintptr_t>(src),
+                             reinterpret_cast<uintptr_t>(src) + (uintptr_t)(nsrc * row_bytes), 1}};
+  CCR_TRY(check_disjoint(ranges, "dst/src"));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  HIP_TRY(launch_permute_rows(static_cast<char*>(dst), static_cast<const char*>(src), d_idx, nrows,
+                              nsrc, row_bytes, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_moe_topk(ccr_ctx_t ctx, const float* logits, int32_t* topk, int64_t T, int E,
+                          int K, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (T < 0 || E < 1 || E > 1024 || K < 1 || K > 16 || K > E)
+    return fail(CCR_ERR_INVALID_ARG, "need T >= 0, 1 <= E <= 1024, 1 <= K <= min(E, 16)");
+  if (T == 0) return CCR_OK;
+  CCR_TRY(check_dev_ptr(ctx, logits, T * E * 4, "logits", 0));
+  CCR_TRY(check_dev_ptr(ctx, topk, T * K * 4, "topk", 0));
+  HIP_TRY(launch_moe_topk(logits, topk, T, E, K, static_cast<hipStream_t>(stream)));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_moe_plan(ccr_ctx_t ctx, const int32_t* topk, int64_t T, int E, int K, int R,
+                          int32_t* src_tok, int32_t* slot, int64_t* h_ecnt, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (T < 0 || T > INT32_MAX / 16 || E < 1 || E > 1024 || K < 1 || K > 16 || K > E || R < 1 ||
+      R > kMaxRanks || E % R != 0)
+    return fail(CCR_ERR_INVALID_ARG, "need 0 <= T, 1 <= K <= min(E, 16), E <= 1024, R | E");
+  if (!h_ecnt) return fail(CCR_ERR_INVALID_ARG, "h_ecnt is NULL");
+  if (T > 0) {
+    CCR_TRY(check_dev_ptr(ctx, topk, T * K * 4, "topk", 0));
+    CCR_TRY(check_dev_ptr(ctx, src_tok, T * K * 4, "src_tok", 0));
+    CCR_TRY(check_dev_ptr(ctx, slot, T * K * 4, "slot", 0));
+  }
+  if (ctx->d_ecnt_len < E) {
+    if (ctx->d_ecnt) HIP_TRY(hipFree(ctx->d_ecnt));
+    if (ctx->h_pinned) HIP_TRY(hipHostFree(ctx->h_pinned));
+    ctx->d_ecnt = nullptr;
+    ctx->h_pinned = nullptr;
+    ctx->d_ecnt_len = 0;
+    HIP_TRY(hipMalloc(reinterpret_cast<void**>(&ctx->d_ecnt), sizeof(int64_t) * 1024));
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&ctx->h_pinned), sizeof(int64_t) * 1024,
+                          hipHostMallocDefault));
+    ctx->d_ecnt_len = 1024;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_TRY(launch_moe_plan(topk, T, E, K, E / R, ctx->d_ecnt, src_tok, slot, s));
+  HIP_TRY(hipMemcpyAsync(ctx->h_pinned, ctx->d_ecnt, sizeof(int64_t) * E, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  memcpy(h_ecnt, ctx->h_pinned, sizeof(int64_t) * E);
+  return CCR_OK;
+}
+
+namespace {
+
+struct MoeShape {
+  int R, E, K, eloc;
+  int64_t T, row_bytes;
+  std::vector<int64_t> cnt;  // cnt[r*R + d]: rows r -> d
+};
+
+ccr_status_t moe_shape(ccr_ctx* ctx, const int64_t* h_ecnt, int R, int64_t T, int E, int K,
+                       int64_t row_bytes, MoeShape* m) {
+  CCR_TRY(check_ctx(ctx));
+  if (R < 1 || R > kMaxRanks || E < 1 || E % R != 0 || K < 1 || K > E || T < 0)
+    return fail(CCR_ERR_INVALID_ARG, "need 1 <= R <= %d, R | E, 1 <= K <= E, T >= 0", kMaxRanks);
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "row_bytes %lld is not a positive multiple of 16", (long long)row_bytes);
+  if (!h_ecnt) return fail(CCR_ERR_INVALID_ARG, "h_ecnt is NULL");
+  m->R = R; m->E = E; m->K = K; m->eloc = E / R; m->T = T; m->row_bytes = row_bytes;
+  m->cnt.assign((size_t)R * R, 0);
+  for (int r = 0; r < R; r++) {
+    int64_t tot = 0;
+    for (int e = 0; e < E; e++) {
+      const int64_t c = h_ecnt[(size_t)r * E + e];
+      if (c < 0) return fail(CCR_ERR_INVALID_ARG, "h_ecnt[%d][%d] < 0", r, e);
+      m->cnt[(size_t)r * R + e / m->eloc] += c;
+      tot += c;
+    }
+    if (tot != T * K)
+      return fail(CCR_ERR_INVALID_ARG, "rank %d's expert counts sum to %lld, not T*K = %lld", r,
+                  (long long)tot, (long long)(T * K));
+  }
+  return CCR_OK;
+}
+
+// The unpack of rank d as block copies: for local expert l, for source r,
+// the rows of r's segment that go to expert (d, l) land contiguously.
+void unpack_pieces(const MoeShape& m, const int64_t* h_ecnt, void* const* recv, void* const* exp,
+                   bool inverse, std::vector<Piece>* out) {
+  const int R = m.R, E = m.E, eloc = m.eloc;
+  for (int d = 0; d < R; d++) {
+    std::vector<int64_t> seg((size_t)R, 0);  // start of r's segment in recv[d]
+    for (int r = 1; r < R; r++) seg[(size_t)r] = seg[(size_t)r - 1] + m.cnt[(size_t)(r - 1) * R + d];
+    int64_t pos = 0;
+    for (int l = 0; l < eloc; l++) {
+      for (int r = 0; r < R; r++) {
+        int64_t start = seg[(size_t)r];
+        for (int ll = 0; ll < l; ll++) start += h_ecnt[(size_t)r * E + d * eloc + ll];
+        const int64_t c = h_ecnt[(size_t)r * E + d * eloc + l];
+        if (c > 0) {
+          char* rp = static_cast<char*>(recv[d]) + start * m.row_bytes;
+          char* ep = static_cast<char*>(exp[d]) + pos * m.row_bytes;
+          out->push_back(inverse ? Piece{rp, ep, c * m.row_bytes} : Piece{ep, rp, c * m.row_bytes});
+        }
+        pos += c;
+      }
+    }
+  }
+}
+
+ccr_status_t launch_copies(const std::vector<Piece>& p, hipStream_t s) {
+  for (size_t i = 0; i < p.size(); i += kMaxPieces) {
+    const int n = (int)std::min<size_t>(kMaxPieces, p.size() - i);
+    HIP_TRY(launch_pieces(HopKind::kCopy, p.data() + i, n, tuning(), s));
+  }
+  return CCR_OK;
+}
+
+// Per-rank device pointers; nbytes[r] (or nbytes[0] for all ranks when
+// per_rank is false) bytes must fit behind each.
+ccr_status_t check_rank_ptrs(ccr_ctx* ctx, const void* const* p, int R, const int64_t* nbytes,
+                             bool per_rank, const char* what) {
+  if (!p) return fail(CCR_ERR_INVALID_ARG, "%s is NULL", what);
+  for (int r = 0; r < R; r++) CCR_TRY(check_dev_ptr(ctx, p[r], nbytes[per_rank ? r : 0], what, r));
+  return CCR_OK;
+}
+
+}  // namespace
+
+ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t* const* src_tok,
+                              const int64_t* h_ecnt, int R, int64_t T, int E, int K,
+                              int64_t row_bytes, void* const* send, void* const* recv,
+                              void* const* exp, void* stream) {
+  MoeShape m;
+  CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
+  if (T == 0) return CCR_OK;
+  const int64_t xb = T * row_bytes, sb = T * K * row_bytes, ib = T * K * 4;
+  std::vector<int64_t> rb((size_t)R, 0);
+  for (int d = 0; d < R; d++)
+    for (int r = 0; r < R; r++) rb[(size_t)d] += m.cnt[(size_t)r * R + d] * row_bytes;
+  CCR_TRY(check_rank_ptrs(ctx, x, R, &xb, false, "x"));
+  CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(src_tok), R, &ib, false, "src_tok"));
+  CCR_TRY(check_rank_ptrs(ctx, send, R, &sb, false, "send"));
+  CCR_TRY(check_rank_ptrs(ctx, recv, R, rb.data(), true, "recv"));
+  CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  // pack: send[r] row j = x[r] row src_tok[r][j]
+  for (int r = 0; r < R; r++)
+    HIP_TRY(launch_permute_rows(static_cast<char*>(send[r]), static_cast<const char*>(x[r]),
+                                src_tok[r], T * K, T, row_bytes, s));
+  // exchange
+  CCR_TRY(run_alltoall(ctx, const_cast<const void* const*>(send), recv, R, m.cnt.data(), row_bytes, s));
+  // unpack to (local expert, source rank, token)
+  std::vector<Piece> p;
+  unpack_pieces(m, h_ecnt, recv, exp, false, &p);
+  CCR_TRY(launch_copies(p, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_t* const* slot,
+                             const int64_t* h_ecnt, int R, int64_t T, int E, int K,
+                             int64_t row_bytes, void* const* recv, void* const* send,
+                             void* const* out, void* stream) {
+  MoeShape m;
+  CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
+  if (T == 0) return CCR_OK;
+  const int64_t sb = T * K * row_bytes, ib = T * K * 4;
+  std::vector<int64_t> rb((size_t)R, 0);
+  for (int d = 0; d < R; d++)
+    for (int r = 0; r < R; r++) rb[(size_t)d] += m.cnt[(size_t)r * R + d] * row_bytes;
+  CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
+  CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(slot), R, &ib, false, "slot"));
+  CCR_TRY(check_rank_ptrs(ctx, recv, R, rb.data(), true, "recv"));
+  CCR_TRY(check_rank_ptrs(ctx, send, R, &sb, false, "send"));
+  CCR_TRY(check_rank_ptrs(ctx, out, R, &sb, false, "out"));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  // inverse unpack: expert-major rows back to source-segment order
+  std::vector<Piece> p;
+  unpack_pieces(m, h_ecnt, recv, const_cast<void* const*>(exp), true, &p);
+  CCR_TRY(launch_copies(p, s));
+  // reverse exchange: rank d returns to r what it received from r
+  std::vector<int64_t> back((size_t)R * R);
+  for (int r = 0; r < R; r++)
+    for (int d = 0; d < R; d++) back[(size_t)d * R + r] = m.cnt[(size_t)r * R + d];
+  CCR_TRY(run_alltoall(ctx, const_cast<const void* const*>(recv), send, R, back.data(), row_bytes, s));
+  // out[r] row (t, k) = send[r] row slot[r][t*K + k]
+  for (int r = 0; r < R; r++)
+    HIP_TRY(launch_permute_rows(static_cast<char*>(out[r]), static_cast<const char*>(send[r]),
+                                slot[r], T * K, T * K, row_bytes, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
+  return CCR_OK;
+}
+
+ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on) {
+  CCR_TRY(check_ctx(ctx));
+  HIP_TRY(hipDeviceSynchronize());
+  for (auto& t : ctx->timed) {
+    ctx->timing_pool.push_back(t.start);
+    ctx->timing_pool.push_back(t.stop);
+  }
+  ctx->timed.clear();
+  ctx->prof_on = on != 0;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t* out) {
+  CCR_TRY(check_ctx(ctx));
+  if (!out || kind < 0 || kind > 2) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 2]");
+  HIP_TRY(hipDeviceSynchronize());
+  ccr_kernel_stats_t st{0, 0, 0.0};
+  for (const auto& t : ctx->timed) {
+    if (t.kind != kind) continue;
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, t.start, t.stop));
+    st.launches++;
+    st.bytes += t.bytes;
+    st.ms += ms;
+  }
+  *out = st;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t* out, int nblocks, void* stream) {
+  CCR_TRY(check_ctx(ctx));
+  if (nblocks < 0 || nblocks > (1 << 20)) return fail(CCR_ERR_INVALID_ARG, "nblocks outside [0, 2^20]");
+  if (nblocks == 0) return CCR_OK;
+  CCR_TRY(check_dev_ptr(ctx, out, (int64_t)nblocks * 12, "out", 0));
+  hipStream_t caller = static_cast<hipStream_t>(stream);
+  CCR_TRY(order_after(ctx, 0, caller, ctx->s_a));
+  HIP_TRY(launch_probe_cu_ids(out, nblocks, ctx->s_a));
+  CCR_TRY(order_after(ctx, 1, ctx->s_a, caller));
+  return CCR_OK;
+}
+
+}  // extern "C"

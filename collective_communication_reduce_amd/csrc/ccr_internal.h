@@ -1,0 +1,55 @@
+// Internal interface between the host runtime (ccr_api.cpp) and the device
+// kernels (ccr_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ccr {
+
+// One contiguous piece of work of a batched launch: `dst` (op) `src` over
+// nbytes bytes.  For a reduce, dst = dst + src element-wise; for a copy,
+// dst = src.  Pointers and nbytes are 16-byte multiples except for the tail
+// of the very last piece of a buffer, whose length is a multiple of the
+// element size.
+struct Piece {
+  char* dst;
+  const char* src;
+  int64_t nbytes;
+};
+
+// Up to kMaxPieces pieces go into one launch, passed by value as kernel
+// arguments (no device-side table, no upload per call).
+constexpr int kMaxPieces = 64;
+
+// Threads per workgroup of the streaming kernels: four wave64 wavefronts.
+constexpr int kBlock = 256;
+
+enum class HopKind : int { kReduceF32 = 0, kReduceBf16 = 1, kCopy = 2 };
+
+struct LaunchTuning {
+  int unroll;       // 16-byte vectors per thread per pass: 1, 2, 4 or 8
+  int nontemporal;  // 1 = streaming (non-temporal) loads and stores
+};
+
+// Enqueue one batched launch over `n` pieces (n <= kMaxPieces).
+hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
+                         hipStream_t stream);
+
+// dst row i = src row idx[i] for i < nrows; rows of row_bytes (multiple of
+// 16); entries outside [0, nsrc) are skipped.
+hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,
+                               int64_t nsrc, int64_t row_bytes, hipStream_t stream);
+
+// Top-K expert ids per token (E <= 1024, K <= 16).
+hipError_t launch_moe_topk(const float* logits, int32_t* topk, int64_t T, int E, int K,
+                           hipStream_t stream);
+
+// Dispatch plan of one rank: ecnt[E] rows per expert, src_tok[T*K], slot[T*K].
+hipError_t launch_moe_plan(const int32_t* topk, int64_t T, int E, int K, int eloc,
+                           int64_t* ecnt, int32_t* src_tok, int32_t* slot, hipStream_t stream);
+
+// One wave64 workgroup per block; writes (XCC id, SE id, CU id) per block.
+hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream);
+
+}  // namespace ccr

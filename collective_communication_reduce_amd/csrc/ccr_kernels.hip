@@ -1,0 +1,387 @@
+// Device kernels of the ring all-reduce hot path, written for gfx950
+// (CDNA4: wave64, 256 CUs in 8 XCDs, HBM3E).
+//
+// Every hot step here is a streaming pass over HBM (one fp32 add per 12
+// bytes moved, one bf16 add per 6), so the kernels are built for bandwidth:
+// 16-byte vector loads/stores, consecutive lanes on consecutive 16-byte
+// vectors (a wave moves 1 KiB per instruction), several independent vectors
+// in flight per thread, and no LDS or MFMA.  Batches of pieces are passed by
+// value in the kernel arguments, so a hop needs no table upload.
+//
+// Method: "HOCCL: Offloading Collective Communication from GPU Cores to
+// Accelerate Distributed Training".  The reduction stays on the compute
+// units (§5 Limitations); copies have a compute-unit kernel here and an SDMA
+// path in the host runtime (Fig. 1c, §2.3).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ccr_internal.h"
+
+namespace ccr {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct PieceArgs {
+  Piece p[kMaxPieces];
+  int32_t tile_start[kMaxPieces + 1];  // first workgroup of each piece
+  int32_t n;
+};
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Eight bf16 hops at once: fp32 add, then round to nearest even with
+// gfx950's v_cvt_pk_bf16_f32 (two results per instruction).  The fp32 sum of
+// two bf16 values rounded to bf16 is the correctly rounded bf16 sum.
+__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f32x2 fa = {bf16_lo(a[j]), bf16_hi(a[j])};
+    f32x2 fb = {bf16_lo(b[j]), bf16_hi(b[j])};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(fa + fb, bf16x2));
+  }
+  return r;
+}
+
+__device__ __forceinline__ u32x4 add_f32x4(u32x4 a, u32x4 b) {
+  f32x4 s = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
+  return __builtin_bit_cast(u32x4, s);
+}
+
+template <HopKind K>
+__device__ __forceinline__ u32x4 apply16(u32x4 local, u32x4 incoming) {
+  if constexpr (K == HopKind::kReduceF32) return add_f32x4(local, incoming);
+  else if constexpr (K == HopKind::kReduceBf16) return add_bf16x8(local, incoming);
+  else return incoming;
+}
+
+// The last (ragged) few elements of a piece, one element per thread.
+template <HopKind K>
+__device__ __forceinline__ void apply_tail(char* dst, const char* src, int unit) {
+  if constexpr (K == HopKind::kReduceF32) {
+    float* d = reinterpret_cast<float*>(dst) + unit;
+    *d = *d + reinterpret_cast<const float*>(src)[unit];
+  } else if constexpr (K == HopKind::kReduceBf16) {
+    uint16_t* d = reinterpret_cast<uint16_t*>(dst) + unit;
+    float s = bf16_lo(*d) + bf16_lo(reinterpret_cast<const uint16_t*>(src)[unit]);
+    *d = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
+  } else {
+    reinterpret_cast<uint16_t*>(dst)[unit] = reinterpret_cast<const uint16_t*>(src)[unit];
+  }
+}
+
+template <HopKind K>
+constexpr int tail_unit_bytes() {
+  return K == HopKind::kReduceF32 ? 4 : 2;
+}
+
+// One workgroup = one tile of kBlock * U 16-byte vectors of one piece.
+// Thread t handles vectors tile_base + u * kBlock + t, u < U, so every load
+// instruction of a wave covers 1 KiB of contiguous memory.  All loads of a
+// tile are issued before the first add so U vectors per operand are in
+// flight.
+template <HopKind K, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs a) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_start[mid] <= b) lo = mid;
+    else hi = mid;
+  }
+  char* const dst = a.p[lo].dst;
+  const char* const src = a.p[lo].src;
+  const int64_t nbytes = a.p[lo].nbytes;
+  const int64_t nvec = nbytes >> 4;
+  const int64_t tile = b - a.tile_start[lo];
+  const int64_t first = tile * (int64_t)(kBlock * U);  // first vector of the tile
+  const int64_t v0 = first + threadIdx.x;
+  u32x4* const d16 = reinterpret_cast<u32x4*>(dst);
+  const u32x4* const s16 = reinterpret_cast<const u32x4*>(src);
+
+  if (first + kBlock * U <= nvec) {  // whole tile in range (uniform): no bounds checks
+    u32x4 in[U];
+    u32x4 loc[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      in[u] = load16<NT>(s16 + v0 + u * kBlock);
+      if constexpr (K != HopKind::kCopy) loc[u] = load16<NT>(d16 + v0 + u * kBlock);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) store16<NT>(d16 + v0 + u * kBlock, apply16<K>(loc[u], in[u]));
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = v0 + u * kBlock;
+      if (v < nvec) {
+        u32x4 loc = {0, 0, 0, 0};
+        if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
+        store16<NT>(d16 + v, apply16<K>(loc, load16<NT>(s16 + v)));
+      }
+    }
+  }
+  // Ragged end: the bytes past the last whole vector belong to the tile
+  // that would hold vector index nvec (never a whole in-range tile).
+  const int tail_units = (int)(nbytes & 15) / tail_unit_bytes<K>();
+  if (tail_units > 0 && tile == nvec / (kBlock * U) && (int)threadIdx.x < tail_units)
+    apply_tail<K>(dst + (nvec << 4), src + (nvec << 4), threadIdx.x);
+}
+
+template <HopKind K, int U>
+hipError_t launch_kind(const PieceArgs& a, bool nt, hipStream_t s) {
+  const int grid = a.tile_start[a.n];
+  if (nt) pieces_kernel<K, U, true><<<grid, kBlock, 0, s>>>(a);
+  else pieces_kernel<K, U, false><<<grid, kBlock, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <HopKind K>
+hipError_t launch_unroll(const PieceArgs& a, int unroll, bool nt, hipStream_t s) {
+  switch (unroll) {
+    case 1: return launch_kind<K, 1>(a, nt, s);
+    case 2: return launch_kind<K, 2>(a, nt, s);
+    case 8: return launch_kind<K, 8>(a, nt, s);
+    default: return launch_kind<K, 4>(a, nt, s);
+  }
+}
+
+// ---------------------------------------------------------------- permute
+// dst row i = src row idx[i].  One workgroup moves RPB rows; thread t moves
+// 16-byte column t (and t + kBlock, ...) of each, with the RPB loads of a
+// column issued together.
+template <int RPB>
+__global__ __launch_bounds__(kBlock) void permute_rows_kernel(u32x4* dst, const u32x4* src,
+                                                              const int32_t* idx, int64_t nrows,
+                                                              int64_t nsrc, int64_t vpr) {
+  const int64_t r0 = (int64_t)blockIdx.x * RPB;
+  int64_t from[RPB];
+#pragma unroll
+  for (int j = 0; j < RPB; j++) {
+    const int64_t r = r0 + j;
+    const int64_t s = r < nrows ? (int64_t)idx[r] : -1;
+    from[j] = (s >= 0 && s < nsrc) ? s : -1;
+  }
+  for (int64_t c = threadIdx.x; c < vpr; c += kBlock) {
+    u32x4 v[RPB];
+#pragma unroll
+    for (int j = 0; j < RPB; j++)
+      if (from[j] >= 0) v[j] = src[from[j] * vpr + c];
+#pragma unroll
+    for (int j = 0; j < RPB; j++)
+      if (from[j] >= 0) dst[(r0 + j) * vpr + c] = v[j];
+  }
+}
+
+// ------------------------------------------------------------------- topk
+// One wave per token: lane l holds the logits of experts l, l+64, ...
+// Each of the K rounds takes the largest remaining logit (lowest expert id
+// among equals) with a butterfly reduction over the wave.
+constexpr int kTopkMaxPerLane = 16;  // E <= 1024
+
+__global__ __launch_bounds__(kBlock) void topk_kernel(const float* logits, int32_t* topk,
+                                                      int64_t T, int E, int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  const float* row = logits + t * E;
+  float v[kTopkMaxPerLane];
+  uint32_t avail = 0;  // bit j: expert j*64+lane exists and is not yet taken
+#pragma unroll
+  for (int j = 0; j < kTopkMaxPerLane; j++) {
+    const int e = j * 64 + lane;
+    v[j] = e < E ? row[e] : 0.0f;
+    if (e < E) avail |= 1u << j;
+  }
+  for (int k = 0; k < K; k++) {
+    float bv = 0.0f;
+    int be = -1;
+#pragma unroll
+    for (int j = 0; j < kTopkMaxPerLane; j++)
+      if (((avail >> j) & 1u) && (be < 0 || v[j] > bv)) {
+        bv = v[j];
+        be = j * 64 + lane;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (oe >= 0 && (be < 0 || ov > bv || (ov == bv && oe < be))) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be >= 0 && lane == (be & 63)) avail &= ~(1u << (be >> 6));
+    if (lane == 0) topk[t * K + k] = be;
+  }
+}
+
+// ------------------------------------------------------------------- plan
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Workgroup e counts the (token, choice) pairs routed to expert e.
+__global__ __launch_bounds__(kBlock) void plan_count_kernel(const int32_t* topk, int64_t T, int K,
+                                                            int64_t* ecnt) {
+  __shared__ int part[kBlock / 64];
+  const int e = blockIdx.x;
+  int n = 0;
+  for (int64_t t = threadIdx.x; t < T; t += kBlock)
+    for (int k = 0; k < K; k++) n += topk[t * K + k] == e;
+  n = wave_sum(n);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t s = 0;
+    for (int w = 0; w < kBlock / 64; w++) s += part[w];
+    ecnt[e] = s;
+  }
+}
+
+// Workgroup e writes expert e's rows: they start after all rows of experts
+// < e (pack order (destination, local expert, token) is expert order), and
+// tokens keep their order through a workgroup-wide stable compaction.
+__global__ __launch_bounds__(kBlock) void plan_fill_kernel(const int32_t* topk, int64_t T, int K,
+                                                           const int64_t* ecnt, int32_t* src_tok,
+                                                           int32_t* slot) {
+  __shared__ int64_t s_base;
+  __shared__ int wcount[kBlock / 64];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) {
+    int64_t b = 0;
+    for (int x = 0; x < e; x++) b += ecnt[x];
+    s_base = b;
+  }
+  __syncthreads();
+  int64_t base = s_base;
+  for (int64_t t0 = 0; t0 < T; t0 += kBlock) {
+    const int64_t t = t0 + threadIdx.x;
+    int kk = -1;
+    if (t < T)
+      for (int k = 0; k < K; k++)
+        if (topk[t * K + k] == e) kk = k;
+    const uint64_t mask = __ballot(kk >= 0);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(mask);
+    __syncthreads();
+    int wbase = 0, total = 0;
+    for (int w = 0; w < kBlock / 64; w++) {
+      if (w < wave) wbase += wcount[w];
+      total += wcount[w];
+    }
+    if (kk >= 0) {
+      const int64_t j = base + wbase + before;
+      src_tok[j] = (int32_t)t;
+      slot[t * K + kk] = (int32_t)j;
+    }
+    base += total;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ probe
+__global__ __launch_bounds__(64) void probe_cu_ids_kernel(int32_t* out) {
+  unsigned hw, xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  if (threadIdx.x == 0) {
+    out[3 * blockIdx.x] = (int32_t)(xcc & 0xfu);
+    out[3 * blockIdx.x + 1] = (int32_t)((hw >> 13) & 0x7u);
+    out[3 * blockIdx.x + 2] = (int32_t)((hw >> 8) & 0xfu);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
+                         hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (n > kMaxPieces) return hipErrorInvalidValue;
+  PieceArgs a;
+  const int unroll = (tune.unroll == 1 || tune.unroll == 2 || tune.unroll == 8) ? tune.unroll : 4;
+  const int64_t per_tile = (int64_t)kBlock * unroll;
+  int64_t tiles = 0;
+  a.n = n;
+  for (int i = 0; i < n; i++) {
+    a.p[i] = pieces[i];
+    a.tile_start[i] = (int32_t)tiles;
+    const int64_t nvec = pieces[i].nbytes >> 4;
+    const int64_t units = nvec + ((pieces[i].nbytes & 15) ? 1 : 0);
+    tiles += (units + per_tile - 1) / per_tile;
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  }
+  a.tile_start[n] = (int32_t)tiles;
+  for (int i = n + 1; i <= kMaxPieces; i++) a.tile_start[i] = (int32_t)tiles;
+  if (tiles == 0) return hipSuccess;
+  const bool nt = tune.nontemporal != 0;
+  switch (kind) {
+    case HopKind::kReduceF32: return launch_unroll<HopKind::kReduceF32>(a, unroll, nt, stream);
+    case HopKind::kReduceBf16: return launch_unroll<HopKind::kReduceBf16>(a, unroll, nt, stream);
+    default: return launch_unroll<HopKind::kCopy>(a, unroll, nt, stream);
+  }
+}
+
+hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,
+                               int64_t nsrc, int64_t row_bytes, hipStream_t stream) {
+  if (nrows <= 0 || row_bytes <= 0) return hipSuccess;
+  constexpr int kRpb = 4;
+  const int64_t grid = (nrows + kRpb - 1) / kRpb;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  permute_rows_kernel<kRpb><<<(unsigned)grid, kBlock, 0, stream>>>(
+      reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), idx, nrows, nsrc,
+      row_bytes >> 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_topk(const float* logits, int32_t* topk, int64_t T, int E, int K,
+                           hipStream_t stream) {
+  if (T <= 0 || K <= 0) return hipSuccess;
+  if (E > 64 * kTopkMaxPerLane) return hipErrorInvalidValue;
+  const int64_t grid = (T + kBlock / 64 - 1) / (kBlock / 64);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  topk_kernel<<<(unsigned)grid, kBlock, 0, stream>>>(logits, topk, T, E, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_plan(const int32_t* topk, int64_t T, int E, int K, int eloc, int64_t* ecnt,
+                           int32_t* src_tok, int32_t* slot, hipStream_t stream) {
+  (void)eloc;
+  if (E <= 0) return hipSuccess;
+  plan_count_kernel<<<E, kBlock, 0, stream>>>(topk, T, K, ecnt);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || T <= 0 || K <= 0) return err;
+  plan_fill_kernel<<<E, kBlock, 0, stream>>>(topk, T, K, ecnt, src_tok, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream) {
+  if (nblocks <= 0) return hipSuccess;
+  probe_cu_ids_kernel<<<nblocks, 64, 0, stream>>>(out);
+  return hipGetLastError();
+}
+
+}  // namespace ccr

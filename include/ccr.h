@@ -1,0 +1,248 @@
+/*
+ * ccr.h -- C ABI of the MI355X ring all-reduce hot path.
+ *
+ * R "virtual ranks" live as R separate device buffers in one GPU's HBM.  A
+ * collective over them is executed the way a ring collective runs across R
+ * GPUs: as a sequence of point-to-point hops, each hop a separate pass over
+ * memory.  The reduce runs on compute units; copies run either as a
+ * compute-unit kernel or on the SDMA engines (no compute units).
+ *
+ * Source of the method: "HOCCL: Offloading Collective Communication from GPU
+ * Cores to Accelerate Distributed Training" (Fei et al.).  HOCCL moves copies
+ * off the GPU cores onto DMA engines (Abstract; §2.3 DMA Engines; Fig. 1c),
+ * keeps reductions on the cores (§5 Limitations), orders communication
+ * against surrounding kernels on the caller's stream (§3.2 Stream Manager),
+ * stages P2P transfers through a pool of chunk slots (§3.3.1, Fig. 4/5a) and
+ * expresses collectives as P2P flows (§3.4, Fig. 6).  The ring itself is the
+ * textbook ring: rank q sends to rank q+1 (mod R); reduce-scatter hop k makes
+ * every rank q add chunk (q-k-2) mod R of rank q-1 into its own copy;
+ * all-gather hop k copies chunk (q-k-1) mod R from rank q-1.
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: CCR_OK, or an error code with a message available from
+ *     ccr_last_error() on the same thread.  No entry point aborts or prints.
+ *   - Device pointers are caller-owned, must stay valid and unmodified until
+ *     the work enqueued on `stream` completes, and must be 16-byte aligned.
+ *     Host arrays of pointers or counts are read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     stream-ordered and asynchronous unless stated otherwise: they return
+ *     once the work is enqueued; any side stream the library uses is joined
+ *     back into `stream` before return, so later work on `stream` sees the
+ *     results (HOCCL §3.2: communication keeps operator order on the stream).
+ *   - A count of zero is a successful no-op.
+ *   - A context is bound to one device and must not be used from two host
+ *     threads at once.
+ */
+#ifndef CCR_H
+#define CCR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CCR_OK = 0,
+    CCR_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment, dtype, aliasing */
+    CCR_ERR_UNSUPPORTED = 2, /* valid request this build cannot run          */
+    CCR_ERR_HIP = 3,         /* a HIP runtime call failed                     */
+    CCR_ERR_OOM = 4,         /* device or pinned-host allocation failed       */
+    CCR_ERR_TIMEOUT = 5      /* a bounded wait expired                        */
+} ccr_status_t;
+
+typedef enum { CCR_F32 = 0, CCR_BF16 = 1 } ccr_dtype_t;
+
+/* How copy hops (all-gather, staging, exchange) move bytes.
+ * KERNEL: a compute-unit copy kernel.  SDMA: hipMemcpyAsync with
+ * hipMemcpyDeviceToDeviceNoCU, i.e. the SDMA engines and no compute unit
+ * (HOCCL Fig. 1c: DMA engine instead of SMs). */
+typedef enum { CCR_COPY_KERNEL = 0, CCR_COPY_SDMA = 1 } ccr_copy_mode_t;
+
+/* bf16 reduce-scatter accumulation.  PER_HOP: every hop computes
+ * bf16_rne(float(a) + float(b)); bf16 travels between ranks.
+ * FP32_PARTIALS: the running partial travels in fp32 and is rounded to
+ * bf16 once, at the last hop. */
+typedef enum { CCR_BF16_ACC_PER_HOP = 0, CCR_BF16_ACC_FP32_PARTIALS = 1 } ccr_bf16_acc_t;
+
+typedef struct {
+    int32_t copy_mode;           /* ccr_copy_mode_t                                 */
+    int32_t cu_budget;           /* compute units the collective may use; 0 = all   */
+    int32_t slices;              /* S >= 1 pipeline slices per ring chunk           */
+    int32_t overlap;             /* 1: all-gather of slice s runs on a second stream
+                                    while reduce-scatter continues with slice s+1   */
+    int64_t staging_chunk_bytes; /* P2P staging chunk (multiple of 16)              */
+    int32_t staging_slots;       /* number of staging slots (>= 1)                  */
+    int32_t bf16_acc;            /* ccr_bf16_acc_t                                  */
+} ccr_config_t;
+
+typedef struct ccr_ctx *ccr_ctx_t;
+
+/* Fill *cfg with the defaults (kernel copies, all CUs, S = 1, no overlap,
+ * 4 MiB x 2 staging slots, per-hop bf16), then apply the environment
+ * overrides CCR_COPY_MODE (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES,
+ * CCR_OVERLAP, CCR_STAGING_CHUNK, CCR_STAGING_SLOTS, CCR_BF16_ACC
+ * (per_hop|fp32_partials).  HOCCL §4 switches backends by an environment
+ * variable; this mirrors that. */
+ccr_status_t ccr_config_default(ccr_config_t *cfg);
+
+/* Create a context on HIP device `device`.  cfg NULL = ccr_config_default().
+ * The context owns its side streams (one of them CU-masked when cu_budget is
+ * set), events, staging slots and small device scratch.  Makes `device`
+ * current on the calling thread. */
+ccr_status_t ccr_ctx_create(int device, const ccr_config_t *cfg, ccr_ctx_t *out);
+/* Waits for the context's streams, then frees everything it owns. */
+ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx);
+/* Replace the configuration.  Synchronises the context's streams first. */
+ccr_status_t ccr_ctx_set_config(ccr_ctx_t ctx, const ccr_config_t *cfg);
+ccr_status_t ccr_ctx_get_config(ccr_ctx_t ctx, ccr_config_t *cfg);
+
+/* ----------------------------------------------------------------------
+ * Ring schedule (host only, no device work).
+ *
+ * One record per (hop, rank): the operation rank dst_rank performs in that
+ * hop, on elements [lo, hi) of chunk `chunk`, reading rank src_rank's buffer.
+ * phase 0 = reduce-scatter (dst += src), 1 = all-gather (dst = src).
+ * Chunks are 16-byte aligned: with V = 16 / element size,
+ * Lc = align_up(ceil(count / R), V), chunk c = [min(count, c*Lc),
+ * min(count, (c+1)*Lc)); a chunk of length l is cut into S slices with
+ * Ls = align_up(ceil(l / S), V) the same way.  Records come slice-major: for
+ * each slice, the R-1 reduce-scatter hops, then the R-1 all-gather hops.
+ * which: 0 = all-reduce, 1 = reduce-scatter only, 2 = all-gather only.
+ * Writes at most max_ops records; *n_ops receives the full count (query the
+ * size with ops = NULL, max_ops = 0).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t phase, slice, step, dst_rank, src_rank, chunk;
+    int64_t lo, hi;
+} ccr_ring_op_t;
+
+ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int which,
+                               ccr_ring_op_t *ops, int64_t max_ops, int64_t *n_ops);
+
+/* ----------------------------------------------------------------------
+ * Ring collectives, in place over R virtual ranks.
+ * bufs: host array of R device pointers, each to `count` elements of dtype;
+ * the R buffers must not overlap.  1 <= R <= 64.
+ *
+ * ccr_allreduce: every rank ends with the element-wise sum over all ranks.
+ *   Element i of chunk c is reduced in the order the partial travels round
+ *   the ring: ((x[c+1] + x[c+2]) + ... + x[c+R-1]) + x[c] (ranks mod R), so
+ *   fp32 results are deterministic and independent of S, the CU budget and
+ *   the copy mode.  bf16 follows the context's bf16_acc.
+ * ccr_reduce_scatter: afterwards chunk r of bufs[r] holds the reduced chunk
+ *   r; the other chunks hold partial sums.
+ * ccr_all_gather: on entry chunk r of bufs[r] is rank r's contribution;
+ *   afterwards every buffer holds all R chunks.  A pure copy.
+ * ---------------------------------------------------------------------- */
+ccr_status_t ccr_allreduce(ccr_ctx_t ctx, void *const *bufs, int R, int64_t count,
+                           int dtype, void *stream);
+ccr_status_t ccr_reduce_scatter(ccr_ctx_t ctx, void *const *bufs, int R, int64_t count,
+                                int dtype, void *stream);
+ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void *const *bufs, int R, int64_t count,
+                            int dtype, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Point-to-point transfers through the context's staging pool (HOCCL
+ * §3.3.1 DMA-RNIC chunk pipelining; slot states of Fig. 4).  Transfer m
+ * copies nbytes from send[m] to recv[m], chunk by chunk: chunk i is copied
+ * into slot i mod staging_slots (filling) on one stream and out of it
+ * (draining) on another, and a slot is refilled only after it has drained.
+ * Transfers run in order m = 0..n-1.  send/recv: host arrays of n device
+ * pointers; the 2n ranges must not overlap.  nbytes must be a multiple of 16.
+ * ---------------------------------------------------------------------- */
+ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void *const *send, void *const *recv, int n,
+                          int64_t nbytes, void *stream);
+
+/* ----------------------------------------------------------------------
+ * All-to-all of row segments over R ranks (HOCCL §6.2 / Fig. 8c-d
+ * All-to-All).  counts: host array, counts[r*R + d] = rows rank r sends to
+ * rank d.  send[r] holds its segments contiguously in destination order;
+ * recv[d] receives its segments contiguously in source order.  row_bytes
+ * must be a multiple of 16.
+ * ---------------------------------------------------------------------- */
+ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void *const *send, void *const *recv, int R,
+                          const int64_t *counts, int64_t row_bytes, void *stream);
+
+/* dst row i = src row d_idx[i], for i < nrows.  d_idx: device int32, each
+ * entry in [0, nsrc); an out-of-range entry leaves that dst row unwritten
+ * and is reported by the next ccr_permute_rows_check() call. */
+ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void *dst, const void *src, const int32_t *d_idx,
+                              int64_t nrows, int64_t nsrc, int64_t row_bytes, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Expert-parallel MoE dispatch and combine over R ranks (HOCCL §2.1: EP
+ * dispatch/combine are all-to-all traffic).  Expert e lives on rank
+ * e / (E/R) as local expert e % (E/R).
+ *
+ * ccr_moe_topk: topk[t*K + k] = the K experts with the largest logits of
+ *   token t (device fp32 [T x E]), by decreasing logit, ties to the lower
+ *   expert id.  Softmax is monotone, so this is also the top-K of the
+ *   softmax.  E <= 1024, K <= min(E, 16).
+ * ccr_moe_plan: one source rank's dispatch plan from its topk.  Rows are
+ *   packed in (destination rank, local expert, token) order.
+ *   src_tok[j] (device int32 [T*K]) = token carried by packed row j;
+ *   slot[t*K + k] (device int32 [T*K]) = packed row that carries (t, k);
+ *   h_ecnt (host int64 [E]) = rows for each expert.  Blocking: the counts
+ *   are copied back to the host, because the exchange is sized on the host
+ *   (DMA engines are driven from the CPU, HOCCL §1, §2.3).
+ * ccr_moe_dispatch: pack (send[r] row j = x[r] row src_tok[r][j]), exchange
+ *   (all-to-all, segments by destination), unpack (exp[d] rows ordered by
+ *   local expert, then source rank, then token).  h_ecnt: host int64
+ *   [R*E] (row r = ccr_moe_plan's counts of rank r).  Every rank sends
+ *   T*K rows of row_bytes; send/recv/exp[r] must each hold the rows it gets.
+ * ccr_moe_combine: the exact inverse; out[r] is [T x K x row_bytes] with
+ *   out[r] row (t, k) = the expert row that carried token t's k-th choice.
+ * ---------------------------------------------------------------------- */
+ccr_status_t ccr_moe_topk(ccr_ctx_t ctx, const float *logits, int32_t *topk, int64_t T, int E,
+                          int K, void *stream);
+ccr_status_t ccr_moe_plan(ccr_ctx_t ctx, const int32_t *topk, int64_t T, int E, int K, int R,
+                          int32_t *src_tok, int32_t *slot, int64_t *h_ecnt, void *stream);
+ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void *const *x, const int32_t *const *src_tok,
+                              const int64_t *h_ecnt, int R, int64_t T, int E, int K,
+                              int64_t row_bytes, void *const *send, void *const *recv,
+                              void *const *exp, void *stream);
+ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void *const *exp, const int32_t *const *slot,
+                             const int64_t *h_ecnt, int R, int64_t T, int E, int K,
+                             int64_t row_bytes, void *const *recv, void *const *send,
+                             void *const *out, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Diagnostics.
+ * ---------------------------------------------------------------------- */
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char *ccr_last_error(void);
+/* Library version string. */
+const char *ccr_version(void);
+/* Launch nblocks one-wave workgroups on the context's compute stream (the
+ * CU-masked one when cu_budget is set) and write, per workgroup, the
+ * hardware ids of the compute unit it ran on: out[3*b] = XCC id,
+ * out[3*b+1] = shader engine id, out[3*b+2] = CU id.  out: device int32
+ * [3*nblocks].  Used to show which compute units a CU budget leaves to the
+ * collective. */
+ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *stream);
+
+/* Per-launch timing of the collectives' own kernels and SDMA copies.
+ * While enabled, every reduce launch, copy launch and SDMA copy issued by
+ * the ring collectives, ccr_sendrecv and ccr_alltoall is bracketed by a pair
+ * of timing events recorded on the stream it runs on.  ccr_profile_read
+ * synchronises the context's streams and the device, then reports, for
+ * `kind` (0 = reduce kernels, 1 = copy kernels, 2 = SDMA copies), the number
+ * of launches since the last enable, the sum of their event-measured
+ * durations in milliseconds, and their algorithmic bytes (a reduce moves
+ * 3 bytes per byte of payload: read local, read incoming, write local; a
+ * copy moves 2).  Enabling (on = 1) also clears the counters. */
+typedef struct {
+    int64_t launches;
+    int64_t bytes;
+    double ms;
+} ccr_kernel_stats_t;
+
+ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on);
+ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CCR_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports
+every entry point the header declares, validates its configuration, and its
+ring scheduler emits the textbook ring (checked against the oracle's
+partition and against the ring's structural properties).  No GPU is used."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import collective_communication_reduce_amd as ccr
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "ccr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(ccr_[a-z0-9_]+)\s*\(", text))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 19
+    lib = ctypes.CDLL(ccr.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), f"libccr.so does not export {n}"
+    assert names == set(ccr._SIGNATURES), "binding and header disagree"
+    assert "gfx950" in ccr.ccr_version()
+
+
+def test_config_defaults_and_environment(monkeypatch):
+    for k in ("CCR_COPY_MODE", "CCR_CU_BUDGET", "CCR_SLICES", "CCR_OVERLAP",
+              "CCR_STAGING_CHUNK", "CCR_STAGING_SLOTS", "CCR_BF16_ACC"):
+        monkeypatch.delenv(k, raising=False)
+    c = ccr.ccr_config_default()
+    assert c == ccr.Config("kernel", 0, 1, False, 4 << 20, 2, "per_hop")
+    monkeypatch.setenv("CCR_COPY_MODE", "sdma")
+    monkeypatch.setenv("CCR_CU_BUDGET", "32")
+    monkeypatch.setenv("CCR_SLICES", "4")
+    monkeypatch.setenv("CCR_OVERLAP", "1")
+    monkeypatch.setenv("CCR_STAGING_CHUNK", str(1 << 20))
+    monkeypatch.setenv("CCR_STAGING_SLOTS", "3")
+    monkeypatch.setenv("CCR_BF16_ACC", "fp32_partials")
+    assert ccr.ccr_config_default() == ccr.Config("sdma", 32, 4, True, 1 << 20, 3, "fp32_partials")
+    monkeypatch.setenv("CCR_SLICES", "0")
+    with pytest.raises(ccr.CcrError) as e:
+        ccr.ccr_config_default()
+    assert e.value.status == ccr.CCR_ERR_INVALID_ARG and "slices" in ccr.ccr_last_error()
+    monkeypatch.setenv("CCR_SLICES", "2")
+    monkeypatch.setenv("CCR_STAGING_CHUNK", "100")
+    with pytest.raises(ccr.CcrError):
+        ccr.ccr_config_default()
+
+
+@pytest.mark.parametrize("R,count,S,dtype", [(1, 10, 1, 0), (2, 40, 1, 0), (3, 12, 1, 0),
+                                             (4, 1 << 20, 2, 0), (5, 1001, 3, 1), (8, 26214400, 4, 1),
+                                             (7, 3, 2, 0), (32, 8388608, 4, 0), (64, 1000, 2, 1),
+                                             (6, 0, 1, 0)])
+def test_ring_schedule_is_the_textbook_ring(R, count, S, dtype):
+    V = 4 if dtype == 0 else 8
+    ops = ccr.ccr_ring_schedule(R, count, S, dtype, which=0)
+    assert len(ops) == 2 * R * (R - 1) * S
+    # slice-major: all reduce-scatter hops of a slice, then its all-gather hops
+    i = 0
+    for s in range(S):
+        for phase in (0, 1):
+            for k in range(R - 1):
+                hop = ops[i:i + R]
+                i += R
+                assert np.all(hop["slice"] == s) and np.all(hop["phase"] == phase)
+                assert np.all(hop["step"] == k)
+                # a perfect matching: every rank receives once and sends once, to q+1
+                assert sorted(hop["dst_rank"].tolist()) == list(range(R))
+                assert np.all(hop["src_rank"] == (hop["dst_rank"] - 1) % R)
+                off = 2 if phase == 0 else 1
+                assert np.all(hop["chunk"] == (hop["dst_rank"] - k - off) % R)
+                # no (rank, chunk) is both written and read within a hop
+                written = {(int(o["dst_rank"]), int(o["chunk"])) for o in hop}
+                read = {(int(o["src_rank"]), int(o["chunk"])) for o in hop}
+                assert not (written & read)
+                for o in hop:
+                    clo, chi = oracle.chunk_bounds(count, R, V, int(o["chunk"]))
+                    assert (o["lo"], o["hi"]) == oracle.slice_bounds(clo, chi, S, V, s)
+    # completeness: chunk c is reduced on ranks c+2, ..., c (the partial
+    # travels c+1 -> c+2 -> ... -> c) and copied to every rank but c
+    for s in range(S):
+        for c in range(R):
+            rs = ops[(ops["phase"] == 0) & (ops["slice"] == s) & (ops["chunk"] == c)]
+            assert rs["dst_rank"].tolist() == [(c + 2 + k) % R for k in range(R - 1)]
+            ag = ops[(ops["phase"] == 1) & (ops["slice"] == s) & (ops["chunk"] == c)]
+            assert ag["dst_rank"].tolist() == [(c + 1 + k) % R for k in range(R - 1)]
+    only_rs = ccr.ccr_ring_schedule(R, count, S, dtype, which=1)
+    only_ag = ccr.ccr_ring_schedule(R, count, S, dtype, which=2)
+    assert np.all(only_rs["phase"] == 0) and np.all(only_ag["phase"] == 1)
+    assert len(only_rs) == len(only_ag) == R * (R - 1) * S
+
+
+def test_ring_schedule_rejects_bad_arguments():
+    for args in [(0, 10, 1, 0), (65, 10, 1, 0), (4, -1, 1, 0), (4, 10, 0, 0), (4, 10, 1, 7)]:
+        with pytest.raises(ccr.CcrError) as e:
+            ccr.ccr_ring_schedule(*args)
+        assert e.value.status == ccr.CCR_ERR_INVALID_ARG
+
+
+def test_null_arguments_are_rejected_without_a_device():
+    lib = ccr._lib
+    assert lib.ccr_allreduce(None, None, 4, 10, 0, None) == ccr.CCR_ERR_INVALID_ARG
+    assert "ctx" in ccr.ccr_last_error()
+    assert lib.ccr_ctx_create(0, None, None) == ccr.CCR_ERR_INVALID_ARG
+    assert lib.ccr_ctx_destroy(None) == ccr.CCR_OK
+    assert lib.ccr_config_default(None) == ccr.CCR_ERR_INVALID_ARG

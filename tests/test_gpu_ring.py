@@ -1,0 +1,171 @@
+"""GPU parity of the ring all-reduce / reduce-scatter / all-gather against
+the CPU oracle, element by element, bit for bit (fp32, and bf16 with per-hop
+rounding: both sides apply the same deterministic rule)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import say, to_dev, to_host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ccr_mod():
+    torch_cuda()
+    import collective_communication_reduce_amd as ccr
+    return ccr
+
+
+@pytest.fixture(scope="module")
+def ctx(ccr_mod):
+    c = ccr_mod.Context(0, ccr_mod.Config())
+    yield c
+    c.close()
+
+
+def _run(ccr, ctx, xs, which="allreduce"):
+    import torch
+    ts = [to_dev(x) for x in xs]
+    getattr(ccr, f"ccr_{which}")(ctx, ts)
+    torch.cuda.synchronize()
+    return [to_host(t) for t in ts]
+
+
+def _assert_bitwise(got, ref, what):
+    for q, (g, r) in enumerate(zip(got, ref)):
+        if g.tobytes() != r.tobytes():
+            bad = np.nonzero(g != r)[0]
+            raise AssertionError(f"{what}: rank {q} differs at {bad.size} elements, first {bad[:5]}")
+
+
+CASES = [(1, 100), (2, 1), (2, 7), (3, 8), (3, 1000), (4, 4096 * 3 + 5), (5, 4099),
+         (8, 65536 + 9), (17, 100003), (64, 2049), (7, 3)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("R,n", CASES)
+@pytest.mark.parametrize("S", [1, 3])
+def test_allreduce_bitwise(ccr_mod, ctx, dt, R, n, S):
+    ctx.set_config(ccr_mod.Config(slices=S))
+    xs = workloads.random_buffers(R, n, dt, seed=R * 131 + n, dist="normal", scale=1.0)
+    say(f"allreduce {dt} R={R} n={n} S={S}")
+    got = _run(ccr_mod, ctx, xs)
+    _assert_bitwise(got, oracle.ring_allreduce(xs, S=S), f"allreduce {dt} R={R} n={n}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("R,n", [(3, 1000), (8, 65536 + 9), (32, 40961)])
+def test_reduce_scatter_and_all_gather_bitwise(ccr_mod, ctx, dt, R, n):
+    ctx.set_config(ccr_mod.Config(slices=2))
+    xs = workloads.random_buffers(R, n, dt, seed=R + n, dist="uniform")
+    say(f"reduce_scatter / all_gather {dt} R={R} n={n}")
+    rs = _run(ccr_mod, ctx, xs, "reduce_scatter")
+    _assert_bitwise(rs, oracle.ring_reduce_scatter(xs, S=2), "reduce_scatter")
+    ag = _run(ccr_mod, ctx, xs, "all_gather")
+    _assert_bitwise(ag, oracle.ring_all_gather(xs, S=2), "all_gather")
+
+
+MODES = [dict(overlap=True, slices=4), dict(copy_mode="sdma", slices=2),
+         dict(copy_mode="sdma", overlap=True, slices=3), dict(cu_budget=64, slices=2),
+         dict(cu_budget=16, overlap=True, slices=2, copy_mode="sdma")]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: "-".join(f"{k}={v}" for k, v in m.items()))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_modes_do_not_change_bits(ccr_mod, ctx, mode, dt):
+    """Copy mode, overlap, slicing and CU budget leave the result bitwise
+    unchanged."""
+    ctx.set_config(ccr_mod.Config(**mode))
+    R, n = 6, 3 * 65536 + 11
+    xs = workloads.random_buffers(R, n, dt, seed=99, dist="normal", scale=1e-3)
+    say(f"allreduce {dt} R={R} n={n} mode={mode}")
+    got = _run(ccr_mod, ctx, xs)
+    _assert_bitwise(got, oracle.ring_allreduce(xs, S=1), f"mode {mode}")
+    rs = _run(ccr_mod, ctx, xs, "reduce_scatter")
+    _assert_bitwise(rs, oracle.ring_reduce_scatter(xs, S=mode.get("slices", 1)), "reduce_scatter")
+    ctx.set_config(ccr_mod.Config())
+
+
+def test_repeated_calls_on_one_stream(ccr_mod, ctx):
+    """Back-to-back collectives on one stream see each other's results."""
+    import torch
+    ctx.set_config(ccr_mod.Config(slices=2, overlap=True))
+    R, n = 4, 50000
+    xs = workloads.integer_buffers(R, n, "f32", seed=5, bound=8)
+    ts = [to_dev(x) for x in xs]
+    say("two allreduces in a row")
+    ccr_mod.ccr_allreduce(ctx, ts)
+    ccr_mod.ccr_allreduce(ctx, ts)
+    torch.cuda.synchronize()
+    expect = R * np.sum(np.stack(xs), axis=0)
+    for t in ts:
+        np.testing.assert_array_equal(to_host(t), expect)
+    ctx.set_config(ccr_mod.Config())
+
+
+def test_invalid_arguments(ccr_mod, ctx):
+    import torch
+    a = torch.zeros(1000, device="cuda")
+    b = torch.zeros(1000, device="cuda")
+    say("invalid arguments")
+    with pytest.raises(ccr_mod.CcrError) as e:   # misaligned (4-byte offset)
+        ccr_mod.ccr_allreduce(ctx, [a[1:], b[1:]])
+    assert "aligned" in str(e.value)
+    with pytest.raises(ccr_mod.CcrError) as e:   # overlapping ranks
+        ccr_mod.ccr_allreduce(ctx, [a[:500], a[400:900]])
+    assert e.value.status == ccr_mod.CCR_ERR_INVALID_ARG
+    host = np.zeros(1000, np.float32)
+    import ctypes
+    ptrs = (ctypes.c_void_p * 2)(host.ctypes.data, b.data_ptr())
+    st = ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 1000, 0, None)
+    assert st == ccr_mod.CCR_ERR_INVALID_ARG
+    ptrs = (ctypes.c_void_p * 2)(a.data_ptr(), b.data_ptr())
+    st = ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 1 << 34, 0, None)  # past the allocation
+    assert st == ccr_mod.CCR_ERR_INVALID_ARG and "past the end" in ccr_mod.ccr_last_error()
+    st = ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 1000, 5, None)
+    assert st == ccr_mod.CCR_ERR_INVALID_ARG
+    assert ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 0, 0, None) == ccr_mod.CCR_OK
+    ctx.set_config(ccr_mod.Config(bf16_acc="fp32_partials"))
+    h = [torch.zeros(64, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    with pytest.raises(ccr_mod.CcrError) as e:
+        ccr_mod.ccr_allreduce(ctx, h)
+    assert e.value.status == ccr_mod.CCR_ERR_UNSUPPORTED
+    ctx.set_config(ccr_mod.Config())
+
+
+# ------------------------------------------------ full-size workloads
+FULL = [(workloads.RING_SMALL_F32, "allreduce"), (workloads.DP_BUCKET_BF16, "allreduce"),
+        (workloads.RS_AG_R32_F32, "rs_then_ag")]
+
+
+@pytest.mark.parametrize("w,how", FULL, ids=[w.name for w, _ in FULL])
+def test_full_size_workloads(ccr_mod, w, how):
+    """The benchmark's sizes and launch configuration, compared bit for bit
+    with the oracle's closed-form fold on every element."""
+    import torch
+    say(f"full-size {w.name}: generating inputs")
+    xs = workloads.ring_inputs(w)
+    ref = oracle.fold(xs)
+    say(f"full-size {w.name}: running on the GPU (S={w.slices})")
+    with ccr_mod.Context(0, ccr_mod.Config(slices=w.slices)) as c:
+        ts = [to_dev(x) for x in xs]
+        if how == "allreduce":
+            ccr_mod.ccr_allreduce(c, ts)
+        else:
+            ccr_mod.ccr_reduce_scatter(c, ts)
+            ccr_mod.ccr_all_gather(c, ts)
+        torch.cuda.synchronize()
+        for q, t in enumerate(ts):
+            g = to_host(t)
+            if g.tobytes() != ref.tobytes():
+                bad = np.nonzero(g != ref)[0]
+                raise AssertionError(f"{w.name}: rank {q} differs at {bad.size} elements")
+    if w.dtype == "bf16":
+        exact = np.zeros(w.count, np.float64)
+        for x in xs:
+            exact += oracle.bf16_to_f32(x)
+        err = np.max(np.abs(oracle.bf16_to_f32(ref) - exact)) / np.max(np.abs(exact))
+        say(f"{w.name}: normalised max error vs fp64 = {err:.4f}")
+        assert err <= 1e-2
