@@ -44,9 +44,14 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def ring_bytes(R, count, esize):
-    """Algorithmic HBM bytes of one ring all-reduce on one GPU."""
-    return (3 + 2) * esize * count * (R - 1)
+def ring_bytes(R, count, esize, fused=True):
+    """Algorithmic HBM bytes of one ring all-reduce on one GPU: a reduce hop
+    reads two operands and writes one (3b per element), a copy hop reads one
+    and writes one (2b).  With the last reduce-scatter hop forwarding its
+    result (fused), that hop writes twice and all-gather has R-2 hops."""
+    if fused:
+        return esize * count * (3 * (R - 1) + 1 + 2 * (R - 2))
+    return esize * count * 5 * (R - 1)
 
 
 def time_steps(fn, steps, stream=None):
@@ -59,11 +64,14 @@ def time_steps(fn, steps, stream=None):
     return (time.perf_counter() - t0) / steps
 
 
-def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, dim=8192):
-    """Median-free, single-window protocol: G back-to-back GEMMs on stream g,
-    alone and then with all-reduces looping on stream c over the same window.
-    Both streams are released together by an event after a short GPU sleep,
-    so the host has enqueued everything before either starts."""
+def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, n_coll=6, dim=8192, budgets=(0, 64, 32)):
+    """Fixed-work protocol: G back-to-back GEMMs on stream g, alone and then
+    with the same number of all-reduces issued on stream c over the same
+    window, for kernel and SDMA copies and several CU budgets.  Both streams
+    are released together by an event after a short GPU sleep, so the host
+    has enqueued everything before either starts; the all-reduces finish
+    well inside the GEMM window in every mode, so every mode does the same
+    communication work while the GEMMs run."""
     import torch
     A = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
     B = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
@@ -74,7 +82,7 @@ def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, dim=8192):
         for _ in range(n_gemm):
             torch.matmul(A, B, out=C)
 
-    def window(with_coll, ctx=None, n_coll=0):
+    def window(ctx=None):
         torch.cuda.synchronize()
         go = torch.cuda.Event()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -88,29 +96,79 @@ def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, dim=8192):
             e0.record(g)
             gemms()
             e1.record(g)
-        if with_coll:
+        if ctx is not None:
             with torch.cuda.stream(c):
                 c0.record(c)
                 for _ in range(n_coll):
                     ccr.ccr_allreduce(ctx, bufs, stream=c)
                 c1.record(c)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1), (c0.elapsed_time(c1) if with_coll else 0.0)
+        return e0.elapsed_time(e1), (c0.elapsed_time(c1) if ctx is not None else 0.0)
 
     with torch.cuda.stream(g):
         gemms()
-    window(False)
-    alone = min(window(False)[0] for _ in range(3))
-    out = {"gemm": f"{dim}x{dim}x{dim} bf16 x{n_gemm}", "gemm_alone_ms": alone}
-    for mode in ("kernel", "sdma"):
-        with ccr.Context(0, ccr.Config(**{**cfg, "copy_mode": mode})) as ctx:
-            t1 = time_steps(lambda: ccr.ccr_allreduce(ctx, bufs), 3)
-            n_coll = max(2, int(1.3 * alone / (t1 * 1e3)) + 1)
-            conc, coll_ms = window(True, ctx, n_coll)
-            out[mode] = {"gemm_ms": conc, "slowdown_pct": 100.0 * (conc / alone - 1.0),
-                         "allreduce_alone_ms": t1 * 1e3, "allreduces": n_coll,
-                         "allreduce_window_ms": coll_ms}
+    window()
+    alone = sorted(window()[0] for _ in range(3))[1]
+    out = {"gemm": f"{dim}x{dim}x{dim} bf16 x{n_gemm}", "gemm_alone_ms": round(alone, 3),
+           "allreduces_per_window": n_coll, "runs": []}
+    for budget in budgets:
+        for mode in ("kernel", "sdma"):
+            with ccr.Context(0, ccr.Config(**{**cfg, "copy_mode": mode, "cu_budget": budget})) as ctx:
+                t1 = time_steps(lambda: ccr.ccr_allreduce(ctx, bufs), 3)
+                res = [window(ctx) for _ in range(3)]
+                conc, coll = sorted(res)[1]
+                out["runs"].append({"copy_mode": mode, "cu_budget": budget or 256,
+                                    "gemm_ms": round(conc, 3),
+                                    "slowdown_pct": round(100.0 * (conc / alone - 1.0), 2),
+                                    "allreduce_alone_ms": round(t1 * 1e3, 4),
+                                    "allreduces_ms_in_window": round(coll, 3)})
     return out
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "ring_allreduce_dp_bucket_r8_bf16_hbm_counters.md")
+KERNELS = os.path.join(ROOT, "collective_communication_reduce_amd", "csrc", "ccr_kernels.hip")
+
+
+def measured_traffic(key="reduce_hop_traffic_bytes_per_launch"):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when the kernel source has changed since the counters were
+    taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(": ", 1) for l in open(COUNTERS).read().splitlines() if ": " in l
+                      and not l.startswith(("|", "#", "`")))
+        sha = hashlib.sha256(open(KERNELS, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256", "").strip() != sha:
+        return None
+    return int(float(fields[key]))
+
+
+def cu_occupancy(ccr, budgets=(0, 64, 32, 16), nblocks=4096):
+    """Distinct compute units (XCC, SE, CU hardware ids) that a burst of
+    one-wave workgroups on the collective's stream lands on, per CU budget."""
+    out = {}
+    for b in budgets:
+        with ccr.Context(0, ccr.Config(cu_budget=b)) as ctx:
+            ids = ccr.ccr_probe_cu_ids(ctx, nblocks).cpu().numpy()
+        cus = {tuple(r) for r in ids.tolist()}
+        out[str(b or 256)] = {"cus": len(cus), "xccs": len({r[0] for r in cus})}
+    return out
+
+
+def copy_probe(ccr, nbytes, reps):
+    """A plain copy of nbytes through the library's copy kernel, reps times
+    (the calibration run for the HBM traffic counters)."""
+    import torch
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    with ccr.Context(0) as ctx:
+        for _ in range(reps):
+            ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+        torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    log(f"copy probe: {reps} x {nbytes} bytes")
 
 
 def cpu_baseline(xs, R, count, esize, S, budget_s=12.0):
@@ -138,6 +196,8 @@ def main():
     ap.add_argument("--overlap", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain BYTES copy through the copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "
@@ -149,6 +209,10 @@ def main():
 
     import collective_communication_reduce_amd as ccr
     import workloads
+
+    if args.copy_probe:
+        copy_probe(ccr, args.copy_probe, max(1, args.steps))
+        return
 
     w = workloads.DP_BUCKET_BF16
     R, count, esize = w.R, w.count, 2
@@ -166,22 +230,25 @@ def main():
     log(f"bench: timing {args.steps} steps")
     t = time_steps(step, args.steps)
     bus = esize * count / t * 2 * (R - 1) / R / 1e9
-    algo = ring_bytes(R, count, esize) / t / 1e9
+    algo = ring_bytes(R, count, esize, fused=True) / t / 1e9
 
     log("bench: per-launch reduce kernel timing")
     ccr.ccr_profile_enable(ctx, True)
     for _ in range(args.steps):
         step()
     red = ccr.ccr_profile_read(ctx, "reduce")
+    fwd = ccr.ccr_profile_read(ctx, "reduce_forward")
     cpy = ccr.ccr_profile_read(ctx, "copy_kernel")
     ccr.ccr_profile_enable(ctx, False)
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
 
-    gemm = None
+    gemm = occ = None
     if not args.no_gemm:
         log("bench: concurrent GEMM slowdown")
         gemm = gemm_slowdown(ccr, cfg, bufs)
+        log("bench: compute units reached under each CU budget")
+        occ = cu_occupancy(ccr)
 
     cpu = None
     if not args.no_cpu:
@@ -198,15 +265,22 @@ def main():
                    "values": "normal(0, 1e-3)", "accumulation": "fp32 add, bf16 per hop"},
         "hbm": {"algorithmic_gbs": round(algo, 1), "frac_of_8tbs": round(algo / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pieces_kernel<ReduceBf16> (one reduce-scatter hop over all ranks)",
+                     "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "pieces_kernel<kReduceBf16, 2, false>: one reduce-scatter hop, all 8 ranks",
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
                      "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
+        "reduce_forward_kernel": None if not fwd["ms"] else {
+            "achieved": round(fwd["bytes"] / (fwd["ms"] * 1e6), 1), "launches": fwd["launches"],
+            "mean_launch_us": round(fwd["ms"] * 1e3 / max(1, fwd["launches"]), 3)},
         "copy_kernel": None if cpy_gbs is None else {
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
+        "gemm_slowdown_pct": None if gemm is None else {
+            r["copy_mode"]: r["slowdown_pct"] for r in gemm["runs"] if r["cu_budget"] == 256},
         "gemm_slowdown": gemm,
+        "cu_occupancy": occ,
         "cpu_baseline": cpu,
     }
     ctx.close()

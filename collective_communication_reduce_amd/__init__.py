@@ -324,7 +324,7 @@ class ccr_kernel_stats_t(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("bytes", ctypes.c_int64), ("ms", ctypes.c_double)]
 
 
-PROFILE_KINDS = {"reduce": 0, "copy_kernel": 1, "sdma": 2}
+PROFILE_KINDS = {"reduce": 0, "copy_kernel": 1, "sdma": 2, "reduce_forward": 3}
 
 
 def ccr_profile_enable(ctx: Context, on: bool = True):

@@ -83,6 +83,7 @@ struct ccr_ctx {
   bool masked = false;          // s_a / s_b carry a CU mask
   hipStream_t s_a = nullptr;    // reduce / fill / exchange side stream
   hipStream_t s_b = nullptr;    // all-gather (overlap) / drain side stream
+  std::vector<hipStream_t> s_dma;  // SDMA copy lanes (no CU mask: SDMA uses no CUs)
   std::vector<hipEvent_t> ev;   // event pool, grown on demand
   char* staging = nullptr;      // staging_slots x staging_chunk_bytes
   int64_t staging_bytes = 0;
@@ -131,6 +132,7 @@ std::vector<uint32_t> cu_mask_for_budget(int budget, int num_cus) {
 }
 
 ccr_status_t destroy_streams(ccr_ctx* ctx) {
+  for (hipStream_t st : ctx->s_dma) HIP_TRY(hipStreamSynchronize(st));
   if (ctx->s_a) HIP_TRY(hipStreamSynchronize(ctx->s_a));
   if (ctx->s_b) HIP_TRY(hipStreamSynchronize(ctx->s_b));
   if (ctx->s_a) HIP_TRY(hipStreamDestroy(ctx->s_a));
@@ -151,6 +153,19 @@ ccr_status_t make_streams(ccr_ctx* ctx) {
   } else {
     HIP_TRY(hipStreamCreateWithFlags(&ctx->s_a, hipStreamNonBlocking));
     HIP_TRY(hipStreamCreateWithFlags(&ctx->s_b, hipStreamNonBlocking));
+  }
+  return CCR_OK;
+}
+
+// Number of streams SDMA copies are spread over.  Independent copies on
+// different lanes overlap their (large, fixed) per-copy start-up cost.
+constexpr int kDmaLanes = 8;
+
+ccr_status_t dma_lanes(ccr_ctx* ctx) {
+  while ((int)ctx->s_dma.size() < kDmaLanes) {
+    hipStream_t st;
+    HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    ctx->s_dma.push_back(st);
   }
   return CCR_OK;
 }
@@ -273,15 +288,16 @@ void ring_schedule(int R, int64_t count, int S, int V, int which,
 LaunchTuning tuning() {
   // Overridable for tuning sweeps; defaults chosen by measurement.
   static LaunchTuning t = [] {
-    LaunchTuning x{4, 0};
+    LaunchTuning x{2, 0, 0};  // 2 x 16 B per operand per thread: best of 1/2/4/8 on gfx950
     if (const char* e = getenv("CCR_UNROLL")) x.unroll = atoi(e);
     if (const char* e = getenv("CCR_NONTEMPORAL")) x.nontemporal = atoi(e);
+    if (const char* e = getenv("CCR_GRID")) x.grid = atoi(e);
     return x;
   }();
   return t;
 }
 
-enum { kProfReduce = 0, kProfCopyKernel = 1, kProfSdma = 2 };
+enum { kProfReduce = 0, kProfCopyKernel = 1, kProfSdma = 2, kProfReduceFwd = 3 };
 
 ccr_status_t timing_event(ccr_ctx* ctx, hipEvent_t* e) {
   if (!ctx->timing_pool.empty()) {
@@ -322,26 +338,58 @@ int64_t payload(const Piece* p, size_t n) {
   return b;
 }
 
+// A kernel launch; when profiling, its start/stop events are stamped by the
+// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel alone.
 ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hipStream_t s) {
+  if (!ctx->prof_on) {
+    HIP_TRY(launch_pieces(kind, p, n, tuning(), s));
+    return CCR_OK;
+  }
   const bool reduce = kind != HopKind::kCopy;
-  TimedScope t{ctx, s, reduce ? kProfReduce : kProfCopyKernel, payload(p, (size_t)n) * (reduce ? 3 : 2)};
+  const bool fwd = kind == HopKind::kReduceFwdF32 || kind == HopKind::kReduceFwdBf16;
+  hipEvent_t start, stop;
+  CCR_TRY(timing_event(ctx, &start));
+  CCR_TRY(timing_event(ctx, &stop));
+  HIP_TRY(launch_pieces(kind, p, n, tuning(), s, start, stop));
+  // algorithmic bytes: reduce reads 2 and writes 1 (forwarding writes 2),
+  // copy reads 1 and writes 1, per byte of payload
+  ctx->timed.push_back(ccr_ctx::Timed{fwd ? kProfReduceFwd : reduce ? kProfReduce : kProfCopyKernel,
+                                      start, stop, payload(p, (size_t)n) * (fwd ? 4 : reduce ? 3 : 2)});
+  return CCR_OK;
+}
+
+ccr_status_t sdma_copy(ccr_ctx* ctx, const Piece& p, hipStream_t s) {
+  if (p.nbytes <= 0) return CCR_OK;
+  TimedScope t{ctx, s, kProfSdma, 2 * p.nbytes};
   CCR_TRY(t.begin());
-  HIP_TRY(launch_pieces(kind, p, n, tuning(), s));
+  HIP_TRY(hipMemcpyAsync(p.dst, p.src, (size_t)p.nbytes, hipMemcpyDeviceToDeviceNoCU, s));
   return t.end();
+}
+
+// Fork the SDMA lanes off `from` (they wait for all work enqueued on it).
+ccr_status_t lanes_after(ccr_ctx* ctx, size_t ev_index, hipStream_t from) {
+  CCR_TRY(dma_lanes(ctx));
+  CCR_TRY(events(ctx, ev_index + 1));
+  HIP_TRY(hipEventRecord(ctx->ev[ev_index], from));
+  for (hipStream_t st : ctx->s_dma) HIP_TRY(hipStreamWaitEvent(st, ctx->ev[ev_index], 0));
+  return CCR_OK;
+}
+
+// Make `to` wait for every SDMA lane.
+ccr_status_t join_lanes(ccr_ctx* ctx, size_t ev_first, hipStream_t to) {
+  CCR_TRY(events(ctx, ev_first + ctx->s_dma.size()));
+  for (size_t i = 0; i < ctx->s_dma.size(); i++) {
+    HIP_TRY(hipEventRecord(ctx->ev[ev_first + i], ctx->s_dma[i]));
+    HIP_TRY(hipStreamWaitEvent(to, ctx->ev[ev_first + i], 0));
+  }
+  return CCR_OK;
 }
 
 // Copy `n` pieces on `s`: one kernel launch per kMaxPieces pieces, or one
 // SDMA transfer per piece.
 ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) {
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
-    for (size_t i = 0; i < n; i++) {
-      if (p[i].nbytes <= 0) continue;
-      TimedScope t{ctx, s, kProfSdma, 2 * p[i].nbytes};
-      CCR_TRY(t.begin());
-      HIP_TRY(hipMemcpyAsync(p[i].dst, p[i].src, (size_t)p[i].nbytes,
-                             hipMemcpyDeviceToDeviceNoCU, s));
-      CCR_TRY(t.end());
-    }
+    for (size_t i = 0; i < n; i++) CCR_TRY(sdma_copy(ctx, p[i], s));
     return CCR_OK;
   }
   for (size_t i = 0; i < n; i += kMaxPieces) {
@@ -373,13 +421,25 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
 
   const int V = 16 / esize, S = ctx->cfg.slices;
   const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
+  const HopKind reduce_fwd = dtype == CCR_F32 ? HopKind::kReduceFwdF32 : HopKind::kReduceFwdBf16;
+  // With compute-unit copies, an all-reduce's last reduce-scatter hop also
+  // forwards the reduced chunk to the next rank (rank q writes chunk q into
+  // bufs[q] and bufs[q+1] in one pass), which is all-gather hop 0.  Within
+  // that hop each forwarded element is written only by the thread that read
+  // the same element, and no other operation of the hop touches it.
+  const bool fuse = which == kWhichAllreduce && ctx->cfg.copy_mode == CCR_COPY_KERNEL;
   // Reduce-scatter runs on the CU-masked stream when a budget is set, else
   // directly on the caller's stream.  All-gather follows it on the same
   // stream, or on the second side stream when overlap is on.
+  // In SDMA mode the all-gather copies of chunk c form a chain (rank c ->
+  // c+1 -> ...) that runs in order on SDMA lane c mod kDmaLanes; copies are
+  // enqueued hop by hop so that the lanes interleave.
+  const bool sdma = ctx->cfg.copy_mode == CCR_COPY_SDMA && which != kWhichRS;
   hipStream_t rs = ctx->masked ? ctx->s_a : caller;
-  hipStream_t ag = ctx->cfg.overlap ? ctx->s_b : rs;
+  hipStream_t ag = (ctx->cfg.overlap && !sdma) ? ctx->s_b : rs;
   const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
-  CCR_TRY(events(ctx, ev_slice0 + (size_t)S));
+  const size_t ev_lanes = ev_slice0 + (size_t)S;
+  CCR_TRY(events(ctx, ev_lanes));
   if (rs != caller || ag != caller) {
     HIP_TRY(hipEventRecord(ctx->ev[ev_fork], caller));
     if (rs != caller) HIP_TRY(hipStreamWaitEvent(rs, ctx->ev[ev_fork], 0));
@@ -389,13 +449,14 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   std::vector<ccr_ring_op_t> ops;
   ops.reserve((size_t)R);
   std::vector<Piece> pieces((size_t)R);
-  auto to_pieces = [&](int* n) {
+  auto to_pieces = [&](int* n, bool forward) {
     *n = 0;
     for (const ccr_ring_op_t& o : ops) {
       if (o.hi <= o.lo) continue;
-      pieces[(size_t)(*n)++] = Piece{static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize,
-                                     static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize,
-                                     (o.hi - o.lo) * esize};
+      Piece pc{static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize,
+               static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize, (o.hi - o.lo) * esize};
+      if (forward) pc.dst2 = static_cast<char*>(bufs[(o.dst_rank + 1) % R]) + o.lo * esize;
+      pieces[(size_t)(*n)++] = pc;
     }
   };
   for (int s = 0; s < S; s++) {
@@ -403,24 +464,38 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
       for (int k = 0; k + 1 < R; k++) {
         ops.clear();
         hop_ops(kRS, k, s, R, count, S, V, &ops);
+        const bool forward = fuse && k == R - 2;
         int n;
-        to_pieces(&n);
-        CCR_TRY(launch_timed(ctx, reduce, pieces.data(), n, rs));
+        to_pieces(&n, forward);
+        CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs));
       }
     }
-    if (which != kWhichRS) {
-      if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
+    if (which != kWhichRS && sdma) {
+      CCR_TRY(lanes_after(ctx, ev_slice0 + (size_t)s, rs));
       for (int k = 0; k + 1 < R; k++) {
         ops.clear();
         hop_ops(kAG, k, s, R, count, S, V, &ops);
+        for (const ccr_ring_op_t& o : ops) {
+          if (o.hi <= o.lo) continue;
+          Piece pc{static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize,
+                   static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize, (o.hi - o.lo) * esize};
+          CCR_TRY(sdma_copy(ctx, pc, ctx->s_dma[(size_t)(o.chunk % kDmaLanes)]));
+        }
+      }
+    } else if (which != kWhichRS) {
+      if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
+      for (int k = fuse ? 1 : 0; k + 1 < R; k++) {
+        ops.clear();
+        hop_ops(kAG, k, s, R, count, S, V, &ops);
         int n;
-        to_pieces(&n);
+        to_pieces(&n, false);
         CCR_TRY(copy_pieces(ctx, pieces.data(), (size_t)n, ag));
       }
     }
   }
   CCR_TRY(order_after(ctx, ev_join_rs, rs, caller));
   if (ag != rs) CCR_TRY(order_after(ctx, ev_join_ag, ag, caller));
+  if (sdma) CCR_TRY(join_lanes(ctx, ev_lanes, caller));
   return CCR_OK;
 }
 
@@ -453,7 +528,12 @@ ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* re
       roff[(size_t)d] += c;
     }
   }
-  return copy_pieces(ctx, p.data(), p.size(), s);
+  if (ctx->cfg.copy_mode != CCR_COPY_SDMA) return copy_pieces(ctx, p.data(), p.size(), s);
+  // SDMA: the segment copies are independent; spread them over the lanes.
+  const size_t ev_fork = 8, ev_join = 9;
+  CCR_TRY(lanes_after(ctx, ev_fork, s));
+  for (size_t i = 0; i < p.size(); i++) CCR_TRY(sdma_copy(ctx, p[i], ctx->s_dma[i % kDmaLanes]));
+  return join_lanes(ctx, ev_join, s);
 }
 
 int64_t env_int(const char* name, int64_t dflt) {
@@ -527,6 +607,7 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   if (!ctx) return CCR_OK;
   (void)hipSetDevice(ctx->device);
   ccr_status_t st = destroy_streams(ctx);
+  for (hipStream_t x : ctx->s_dma) (void)hipStreamDestroy(x);
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   for (auto& t : ctx->timed) {
     (void)hipEventDestroy(t.start);
@@ -904,7 +985,7 @@ ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on) {
 
 ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t* out) {
   CCR_TRY(check_ctx(ctx));
-  if (!out || kind < 0 || kind > 2) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 2]");
+  if (!out || kind < 0 || kind > 3) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 3]");
   HIP_TRY(hipDeviceSynchronize());
   ccr_kernel_stats_t st{0, 0, 0.0};
   for (const auto& t : ctx->timed) {

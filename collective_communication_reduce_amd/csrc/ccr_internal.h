@@ -16,6 +16,7 @@ struct Piece {
   char* dst;
   const char* src;
   int64_t nbytes;
+  char* dst2 = nullptr;  // reduce-and-forward only: second copy of the result
 };
 
 // Up to kMaxPieces pieces go into one launch, passed by value as kernel
@@ -25,16 +26,31 @@ constexpr int kMaxPieces = 64;
 // Threads per workgroup of the streaming kernels: four wave64 wavefronts.
 constexpr int kBlock = 256;
 
-enum class HopKind : int { kReduceF32 = 0, kReduceBf16 = 1, kCopy = 2 };
+// kReduce*: dst = dst + src.  kReduceFwd*: the same, and the result is also
+// written to dst2 (the last reduce-scatter hop forwarding the reduced chunk
+// to the next rank, which replaces the first all-gather hop).  kCopy:
+// dst = src.
+enum class HopKind : int {
+  kReduceF32 = 0,
+  kReduceBf16 = 1,
+  kCopy = 2,
+  kReduceFwdF32 = 3,
+  kReduceFwdBf16 = 4
+};
 
 struct LaunchTuning {
   int unroll;       // 16-byte vectors per thread per pass: 1, 2, 4 or 8
   int nontemporal;  // 1 = streaming (non-temporal) loads and stores
+  int grid;         // 0 = one workgroup per tile; > 0 = that many workgroups
+                    // looping over the tiles
 };
 
-// Enqueue one batched launch over `n` pieces (n <= kMaxPieces).
+// Enqueue one batched launch over `n` pieces (n <= kMaxPieces).  With
+// start/stop events, the launch goes through hipExtLaunchKernelGGL so that
+// the events carry the kernel's own start and end timestamps.
 hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 
 // dst row i = src row idx[i] for i < nrows; rows of row_bytes (multiple of
 // 16); entries outside [0, nsrc) are skipped.

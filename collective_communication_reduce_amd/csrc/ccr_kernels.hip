@@ -13,6 +13,7 @@
 // units (§5 Limitations); copies have a compute-unit kernel here and an SDMA
 // path in the host runtime (Fig. 1c, §2.3).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,22 +71,39 @@ __device__ __forceinline__ u32x4 add_f32x4(u32x4 a, u32x4 b) {
 }
 
 template <HopKind K>
+constexpr bool is_f32() {
+  return K == HopKind::kReduceF32 || K == HopKind::kReduceFwdF32;
+}
+template <HopKind K>
+constexpr bool is_bf16() {
+  return K == HopKind::kReduceBf16 || K == HopKind::kReduceFwdBf16;
+}
+template <HopKind K>
+constexpr bool forwards() {
+  return K == HopKind::kReduceFwdF32 || K == HopKind::kReduceFwdBf16;
+}
+
+template <HopKind K>
 __device__ __forceinline__ u32x4 apply16(u32x4 local, u32x4 incoming) {
-  if constexpr (K == HopKind::kReduceF32) return add_f32x4(local, incoming);
-  else if constexpr (K == HopKind::kReduceBf16) return add_bf16x8(local, incoming);
+  if constexpr (is_f32<K>()) return add_f32x4(local, incoming);
+  else if constexpr (is_bf16<K>()) return add_bf16x8(local, incoming);
   else return incoming;
 }
 
 // The last (ragged) few elements of a piece, one element per thread.
 template <HopKind K>
-__device__ __forceinline__ void apply_tail(char* dst, const char* src, int unit) {
-  if constexpr (K == HopKind::kReduceF32) {
+__device__ __forceinline__ void apply_tail(char* dst, const char* src, char* dst2, int unit) {
+  if constexpr (is_f32<K>()) {
     float* d = reinterpret_cast<float*>(dst) + unit;
-    *d = *d + reinterpret_cast<const float*>(src)[unit];
-  } else if constexpr (K == HopKind::kReduceBf16) {
+    const float r = *d + reinterpret_cast<const float*>(src)[unit];
+    *d = r;
+    if constexpr (forwards<K>()) reinterpret_cast<float*>(dst2)[unit] = r;
+  } else if constexpr (is_bf16<K>()) {
     uint16_t* d = reinterpret_cast<uint16_t*>(dst) + unit;
-    float s = bf16_lo(*d) + bf16_lo(reinterpret_cast<const uint16_t*>(src)[unit]);
-    *d = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
+    const float s = bf16_lo(*d) + bf16_lo(reinterpret_cast<const uint16_t*>(src)[unit]);
+    const uint16_t r = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
+    *d = r;
+    if constexpr (forwards<K>()) reinterpret_cast<uint16_t*>(dst2)[unit] = r;
   } else {
     reinterpret_cast<uint16_t*>(dst)[unit] = reinterpret_cast<const uint16_t*>(src)[unit];
   }
@@ -93,76 +111,101 @@ __device__ __forceinline__ void apply_tail(char* dst, const char* src, int unit)
 
 template <HopKind K>
 constexpr int tail_unit_bytes() {
-  return K == HopKind::kReduceF32 ? 4 : 2;
+  return is_f32<K>() ? 4 : 2;
 }
 
-// One workgroup = one tile of kBlock * U 16-byte vectors of one piece.
-// Thread t handles vectors tile_base + u * kBlock + t, u < U, so every load
-// instruction of a wave covers 1 KiB of contiguous memory.  All loads of a
-// tile are issued before the first add so U vectors per operand are in
-// flight.
+// One tile = kBlock * U consecutive 16-byte vectors of one piece.  Thread t
+// handles vectors first + u * kBlock + t, u < U, so every load instruction
+// of a wave covers 1 KiB of contiguous memory.  All loads of a tile are
+// issued before the first add, so 2U vectors per thread are in flight.
+// Workgroup b processes tiles b, b + gridDim.x, ... (one tile when the grid
+// has one workgroup per tile).
 template <HopKind K, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs a) {
-  const int b = blockIdx.x;
-  int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_start[mid] <= b) lo = mid;
-    else hi = mid;
-  }
-  char* const dst = a.p[lo].dst;
-  const char* const src = a.p[lo].src;
-  const int64_t nbytes = a.p[lo].nbytes;
-  const int64_t nvec = nbytes >> 4;
-  const int64_t tile = b - a.tile_start[lo];
-  const int64_t first = tile * (int64_t)(kBlock * U);  // first vector of the tile
-  const int64_t v0 = first + threadIdx.x;
-  u32x4* const d16 = reinterpret_cast<u32x4*>(dst);
-  const u32x4* const s16 = reinterpret_cast<const u32x4*>(src);
-
-  if (first + kBlock * U <= nvec) {  // whole tile in range (uniform): no bounds checks
-    u32x4 in[U];
-    u32x4 loc[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      in[u] = load16<NT>(s16 + v0 + u * kBlock);
-      if constexpr (K != HopKind::kCopy) loc[u] = load16<NT>(d16 + v0 + u * kBlock);
+  const int ntiles = a.tile_start[a.n];
+  for (int b = blockIdx.x; b < ntiles; b += gridDim.x) {
+    int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tile_start[mid] <= b) lo = mid;
+      else hi = mid;
     }
+    char* const dst = a.p[lo].dst;
+    char* const dst2 = a.p[lo].dst2;
+    const char* const src = a.p[lo].src;
+    const int64_t nbytes = a.p[lo].nbytes;
+    const int64_t nvec = nbytes >> 4;
+    const int64_t tile = b - a.tile_start[lo];
+    const int64_t first = tile * (int64_t)(kBlock * U);  // first vector of the tile
+    const int64_t v0 = first + threadIdx.x;
+    u32x4* const d16 = reinterpret_cast<u32x4*>(dst);
+    u32x4* const f16 = reinterpret_cast<u32x4*>(dst2);
+    const u32x4* const s16 = reinterpret_cast<const u32x4*>(src);
+
+    if (first + kBlock * U <= nvec) {  // whole tile in range (uniform): no bounds checks
+      u32x4 in[U];
+      u32x4 loc[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) store16<NT>(d16 + v0 + u * kBlock, apply16<K>(loc[u], in[u]));
-  } else {
+      for (int u = 0; u < U; u++) {
+        in[u] = load16<NT>(s16 + v0 + u * kBlock);
+        if constexpr (K != HopKind::kCopy) loc[u] = load16<NT>(d16 + v0 + u * kBlock);
+      }
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int64_t v = v0 + u * kBlock;
-      if (v < nvec) {
-        u32x4 loc = {0, 0, 0, 0};
-        if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
-        store16<NT>(d16 + v, apply16<K>(loc, load16<NT>(s16 + v)));
+      for (int u = 0; u < U; u++) {
+        const u32x4 r = apply16<K>(loc[u], in[u]);
+        store16<NT>(d16 + v0 + u * kBlock, r);
+        if constexpr (forwards<K>()) store16<NT>(f16 + v0 + u * kBlock, r);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int64_t v = v0 + u * kBlock;
+        if (v < nvec) {
+          u32x4 loc = {0, 0, 0, 0};
+          if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
+          const u32x4 r = apply16<K>(loc, load16<NT>(s16 + v));
+          store16<NT>(d16 + v, r);
+          if constexpr (forwards<K>()) store16<NT>(f16 + v, r);
+        }
       }
     }
+    // Ragged end: the bytes past the last whole vector belong to the tile
+    // that would hold vector index nvec (never a whole in-range tile).
+    const int tail_units = (int)(nbytes & 15) / tail_unit_bytes<K>();
+    if (tail_units > 0 && tile == nvec / (kBlock * U) && (int)threadIdx.x < tail_units)
+      apply_tail<K>(dst + (nvec << 4), src + (nvec << 4), dst2 + (forwards<K>() ? (nvec << 4) : 0),
+                    threadIdx.x);
   }
-  // Ragged end: the bytes past the last whole vector belong to the tile
-  // that would hold vector index nvec (never a whole in-range tile).
-  const int tail_units = (int)(nbytes & 15) / tail_unit_bytes<K>();
-  if (tail_units > 0 && tile == nvec / (kBlock * U) && (int)threadIdx.x < tail_units)
-    apply_tail<K>(dst + (nvec << 4), src + (nvec << 4), threadIdx.x);
 }
 
-template <HopKind K, int U>
-hipError_t launch_kind(const PieceArgs& a, bool nt, hipStream_t s) {
-  const int grid = a.tile_start[a.n];
-  if (nt) pieces_kernel<K, U, true><<<grid, kBlock, 0, s>>>(a);
-  else pieces_kernel<K, U, false><<<grid, kBlock, 0, s>>>(a);
+struct Timing {
+  hipEvent_t start, stop;
+};
+
+template <HopKind K, int U, bool NT>
+hipError_t launch_one(const PieceArgs& a, hipStream_t s, Timing t, int grid_cap) {
+  int grid = a.tile_start[a.n];
+  if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+  if (t.start && t.stop)
+    hipExtLaunchKernelGGL(pieces_kernel<K, U, NT>, dim3(grid), dim3(kBlock), 0, s, t.start, t.stop,
+                          0, a);
+  else
+    pieces_kernel<K, U, NT><<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 
+template <HopKind K, int U>
+hipError_t launch_kind(const PieceArgs& a, bool nt, hipStream_t s, Timing t, int g) {
+  return nt ? launch_one<K, U, true>(a, s, t, g) : launch_one<K, U, false>(a, s, t, g);
+}
+
 template <HopKind K>
-hipError_t launch_unroll(const PieceArgs& a, int unroll, bool nt, hipStream_t s) {
+hipError_t launch_unroll(const PieceArgs& a, int unroll, bool nt, hipStream_t s, Timing t, int g) {
   switch (unroll) {
-    case 1: return launch_kind<K, 1>(a, nt, s);
-    case 2: return launch_kind<K, 2>(a, nt, s);
-    case 8: return launch_kind<K, 8>(a, nt, s);
-    default: return launch_kind<K, 4>(a, nt, s);
+    case 1: return launch_kind<K, 1>(a, nt, s, t, g);
+    case 2: return launch_kind<K, 2>(a, nt, s, t, g);
+    case 8: return launch_kind<K, 8>(a, nt, s, t, g);
+    default: return launch_kind<K, 4>(a, nt, s, t, g);
   }
 }
 
@@ -318,7 +361,7 @@ __global__ __launch_bounds__(64) void probe_cu_ids_kernel(int32_t* out) {
 }  // namespace
 
 hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (n <= 0) return hipSuccess;
   if (n > kMaxPieces) return hipErrorInvalidValue;
   PieceArgs a;
@@ -338,10 +381,16 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
   for (int i = n + 1; i <= kMaxPieces; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   const bool nt = tune.nontemporal != 0;
+  const Timing t{start, stop};
+  const int g = tune.grid;
   switch (kind) {
-    case HopKind::kReduceF32: return launch_unroll<HopKind::kReduceF32>(a, unroll, nt, stream);
-    case HopKind::kReduceBf16: return launch_unroll<HopKind::kReduceBf16>(a, unroll, nt, stream);
-    default: return launch_unroll<HopKind::kCopy>(a, unroll, nt, stream);
+    case HopKind::kReduceF32: return launch_unroll<HopKind::kReduceF32>(a, unroll, nt, stream, t, g);
+    case HopKind::kReduceBf16: return launch_unroll<HopKind::kReduceBf16>(a, unroll, nt, stream, t, g);
+    case HopKind::kReduceFwdF32:
+      return launch_unroll<HopKind::kReduceFwdF32>(a, unroll, nt, stream, t, g);
+    case HopKind::kReduceFwdBf16:
+      return launch_unroll<HopKind::kReduceFwdBf16>(a, unroll, nt, stream, t, g);
+    default: return launch_unroll<HopKind::kCopy>(a, unroll, nt, stream, t, g);
   }
 }
 

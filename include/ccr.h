@@ -228,11 +228,15 @@ ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *st
  * the ring collectives, ccr_sendrecv and ccr_alltoall is bracketed by a pair
  * of timing events recorded on the stream it runs on.  ccr_profile_read
  * synchronises the context's streams and the device, then reports, for
- * `kind` (0 = reduce kernels, 1 = copy kernels, 2 = SDMA copies), the number
- * of launches since the last enable, the sum of their event-measured
- * durations in milliseconds, and their algorithmic bytes (a reduce moves
- * 3 bytes per byte of payload: read local, read incoming, write local; a
- * copy moves 2).  Enabling (on = 1) also clears the counters. */
+ * `kind` (0 = reduce kernels, 1 = copy kernels, 2 = SDMA copies,
+ * 3 = reduce-and-forward kernels, the last reduce-scatter hop of an
+ * all-reduce with kernel copies), the number of launches since the last
+ * enable, the sum of their durations in milliseconds, and their algorithmic
+ * bytes (a reduce moves 3 bytes per byte of payload: read local, read
+ * incoming, write local; reduce-and-forward 4; a copy 2).  Kernel launches
+ * are timed by events attached to the launch itself (hipExtLaunchKernel),
+ * SDMA copies by events recorded around them.  Enabling (on = 1) also
+ * clears the counters. */
 typedef struct {
     int64_t launches;
     int64_t bytes;

@@ -40,7 +40,7 @@ class RingWorkload:
 # Ring all-reduce, 4 ranks x 1,048,576 fp32, uniform[-1, 1], 2 slices per chunk.
 RING_SMALL_F32 = RingWorkload("ring_allreduce_r4_1m_f32", 4, 1 << 20, "f32", "uniform", 1.0, 1, 2)
 # Data-parallel gradient bucket: 8 ranks x 25 Mi bf16 (50 MiB), normal(0, 1e-3).
-DP_BUCKET_BF16 = RingWorkload("dp_bucket_allreduce_r8_25m_bf16", 8, 25 * MiB, "bf16", "normal", 1e-3, 2, 4)
+DP_BUCKET_BF16 = RingWorkload("dp_bucket_allreduce_r8_25m_bf16", 8, 25 * MiB, "bf16", "normal", 1e-3, 2, 1)
 # Reduce-scatter then all-gather, 32 ranks x 8 Mi fp32 (1 GiB in total).
 RS_AG_R32_F32 = RingWorkload("rs_ag_r32_8m_f32", 32, 8 * MiB, "f32", "uniform", 1.0, 4, 4)
 
