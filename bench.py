@@ -64,19 +64,40 @@ def time_steps(fn, steps, stream=None):
     return (time.perf_counter() - t0) / steps
 
 
-def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, n_coll=6, dim=8192, budgets=(0, 64, 32)):
-    """Fixed-work protocol: G back-to-back GEMMs on stream g, alone and then
-    with the same number of all-reduces issued on stream c over the same
-    window, for kernel and SDMA copies and several CU budgets.  Both streams
-    are released together by an event after a short GPU sleep, so the host
-    has enqueued everything before either starts; the all-reduces finish
-    well inside the GEMM window in every mode, so every mode does the same
-    communication work while the GEMMs run."""
+def own_queue_stream():
+    """A torch stream with a hardware queue of its own.  Plain streams share
+    the runtime's few hardware queues round-robin, so unrelated streams can
+    end up serialised in one in-order queue; a CU-masked stream (mask: all
+    CUs) is given its own queue."""
+    import ctypes
     import torch
-    A = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
-    B = torch.randn(dim, dim, dtype=torch.bfloat16, device="cuda")
-    C = torch.empty(dim, dim, dtype=torch.bfloat16, device="cuda")
-    g, c, s0 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    hip = ctypes.CDLL("libamdhip64.so")  # the runtime torch already loaded
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n + 31) // 32
+    mask = (ctypes.c_uint32 * words)(*([0xFFFFFFFF] * words))
+    s = ctypes.c_void_p()
+    if hip.hipExtStreamCreateWithCUMask(ctypes.byref(s), words, mask) != 0:
+        raise RuntimeError("hipExtStreamCreateWithCUMask failed")
+    return torch.cuda.ExternalStream(s.value)
+
+
+def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
+    """Fixed-work overlap protocol.  G back-to-back GEMMs on stream g, alone
+    and then with n_coll calls of `collective(ctx, stream)` issued on
+    stream c over the same window.  Both streams get hardware queues of their
+    own and are released together by an event after a short GPU sleep, so
+    the host has enqueued everything before either starts; every mode does
+    the same communication work.  Reported per run: the GEMMs' slowdown,
+    the time the collectives took under load, and the makespan (time until
+    both the GEMMs and the collectives are done) against the GEMMs alone."""
+    import torch
+    M, N, K = gemm_dims
+    A = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+    B = torch.randn(K, N, dtype=torch.bfloat16, device="cuda")
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    g, c, s0 = own_queue_stream(), own_queue_stream(), own_queue_stream()
 
     def gemms():
         for _ in range(n_gemm):
@@ -85,44 +106,63 @@ def gemm_slowdown(ccr, cfg, bufs, n_gemm=20, n_coll=6, dim=8192, budgets=(0, 64,
     def window(ctx=None):
         torch.cuda.synchronize()
         go = torch.cuda.Event()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         with torch.cuda.stream(s0):
             torch.cuda._sleep(20_000_000)
             go.record(s0)
         g.wait_event(go)
         c.wait_event(go)
         with torch.cuda.stream(g):
-            e0.record(g)
+            ev[0].record(g)
             gemms()
-            e1.record(g)
+            ev[1].record(g)
         if ctx is not None:
             with torch.cuda.stream(c):
-                c0.record(c)
+                ev[2].record(c)
                 for _ in range(n_coll):
-                    ccr.ccr_allreduce(ctx, bufs, stream=c)
-                c1.record(c)
+                    collective(ctx, c)
+                ev[3].record(c)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1), (c0.elapsed_time(c1) if ctx is not None else 0.0)
+        gemm = ev[0].elapsed_time(ev[1])
+        if ctx is None:
+            return gemm, 0.0, gemm
+        coll = ev[2].elapsed_time(ev[3])
+        span = max(ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[3]))
+        return gemm, coll, span
 
     with torch.cuda.stream(g):
         gemms()
     window()
     alone = sorted(window()[0] for _ in range(3))[1]
-    out = {"gemm": f"{dim}x{dim}x{dim} bf16 x{n_gemm}", "gemm_alone_ms": round(alone, 3),
-           "allreduces_per_window": n_coll, "runs": []}
-    for budget in budgets:
-        for mode in ("kernel", "sdma"):
-            with ccr.Context(0, ccr.Config(**{**cfg, "copy_mode": mode, "cu_budget": budget})) as ctx:
-                t1 = time_steps(lambda: ccr.ccr_allreduce(ctx, bufs), 3)
-                res = [window(ctx) for _ in range(3)]
-                conc, coll = sorted(res)[1]
-                out["runs"].append({"copy_mode": mode, "cu_budget": budget or 256,
-                                    "gemm_ms": round(conc, 3),
-                                    "slowdown_pct": round(100.0 * (conc / alone - 1.0), 2),
-                                    "allreduce_alone_ms": round(t1 * 1e3, 4),
-                                    "allreduces_ms_in_window": round(coll, 3)})
+    out = {"gemm": f"{M}x{N}x{K} bf16 x{n_gemm}", "gemm_alone_ms": round(alone, 3),
+           "collectives_per_window": n_coll, "runs": []}
+    for conf in runs:
+        with ccr.Context(0, ccr.Config(**conf)) as ctx:
+            collective(ctx, c)  # first use starts the SDMA proxy
+            torch.cuda.synchronize()
+            t1 = time_steps(lambda: collective(ctx, c), 3)
+            gemm, coll, span = sorted(window(ctx) for _ in range(3))[1]
+            out["runs"].append({
+                "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
+                "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
+                "gemm_ms": round(gemm, 3), "slowdown_pct": round(100.0 * (gemm / alone - 1.0), 2),
+                "collective_alone_ms": round(t1 * 1e3, 4),
+                "collectives_under_load_ms": round(coll, 3),
+                "makespan_ms": round(span, 3),
+                "makespan_over_gemm_alone_pct": round(100.0 * (span / alone - 1.0), 2)})
     return out
+
+
+def host_call_us(ccr, call, reps=50):
+    """Host time per enqueue (HOCCL Fig. 9 measures CPU launch time per op)."""
+    import torch
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        call()
+    dt = (time.perf_counter() - t) / reps
+    torch.cuda.synchronize()
+    return round(dt * 1e6, 2)
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "ring_allreduce_dp_bucket_r8_bf16_hbm_counters.md")
@@ -243,12 +283,34 @@ def main():
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
 
-    gemm = occ = None
+    gemm = pp = occ = launch = None
     if not args.no_gemm:
-        log("bench: concurrent GEMM slowdown")
-        gemm = gemm_slowdown(ccr, cfg, bufs)
-        log("bench: compute units reached under each CU budget")
+        log("bench: concurrent GEMM, gradient-bucket all-reduce")
+        runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32) for m in ("kernel", "sdma")]
+        runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
+        gemm = overlap_runs(ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs,
+                            (8192, 8192, 8192), 20, 6)
+        log("bench: concurrent GEMM, pipeline-parallel send/recv through staging")
+        pw = workloads.PP_STAGING_BF16
+        mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
+               for _ in range(pw.microbatches)]
+        outs = [torch.empty_like(x) for x in mbs]
+        stg = dict(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
+        pp = overlap_runs(ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
+                          [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma")],
+                          (4096, 4096, 16384), 20, 20)
+        pp["workload"] = pw.name
+        log("bench: compute units reached under each CU budget; host time per call")
         occ = cu_occupancy(ccr)
+        launch = {}
+        for m in ("kernel", "sdma"):
+            with ccr.Context(0, ccr.Config(**dict(cfg, copy_mode=m))) as c2:
+                ccr.ccr_allreduce(c2, bufs)
+                launch[f"allreduce_{m}"] = host_call_us(ccr, lambda: ccr.ccr_allreduce(c2, bufs), 20)
+            with ccr.Context(0, ccr.Config(**dict(stg, copy_mode=m))) as c2:
+                ccr.ccr_sendrecv(c2, mbs[:1], outs[:1])
+                launch[f"sendrecv_16MiB_{m}"] = host_call_us(
+                    ccr, lambda: ccr.ccr_sendrecv(c2, mbs[:1], outs[:1]), 20)
 
     cpu = None
     if not args.no_cpu:
@@ -278,9 +340,12 @@ def main():
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
         "gemm_slowdown_pct": None if gemm is None else {
-            r["copy_mode"]: r["slowdown_pct"] for r in gemm["runs"] if r["cu_budget"] == 256},
+            r["copy_mode"]: r["slowdown_pct"] for r in gemm["runs"]
+            if r["cu_budget"] == 256 and r["dma_sync"] in (None, "host_func")},
         "gemm_slowdown": gemm,
+        "pp_staging_gemm_slowdown": pp,
         "cu_occupancy": occ,
+        "host_us_per_call": launch,
         "cpu_baseline": cpu,
     }
     ctx.close()

@@ -38,7 +38,8 @@ class ccr_config_t(ctypes.Structure):
     _fields_ = [("copy_mode", ctypes.c_int32), ("cu_budget", ctypes.c_int32),
                 ("slices", ctypes.c_int32), ("overlap", ctypes.c_int32),
                 ("staging_chunk_bytes", ctypes.c_int64), ("staging_slots", ctypes.c_int32),
-                ("bf16_acc", ctypes.c_int32)]
+                ("bf16_acc", ctypes.c_int32), ("dma_stripe", ctypes.c_int32),
+                ("dma_chunk_bytes", ctypes.c_int64), ("dma_sync", ctypes.c_int32)]
 
 
 class ccr_ring_op_t(ctypes.Structure):
@@ -75,6 +76,10 @@ _SIGNATURES = {
     "ccr_probe_cu_ids": [_vp, _vp, _i32, _vp],
     "ccr_profile_enable": [_vp, _i32],
     "ccr_profile_read": [_vp, _i32, _vp],
+    "ccr_dma_info": [_vp, _vp, _vp],
+    "ccr_sendrecv_slot_log": [_vp, _vp, _i64, ctypes.POINTER(_i64)],
+    "ccr_stream_wait": [_vp, _vp, _i32],
+    "ccr_dma_hold_finish": [_vp, _i32],
 }
 
 
@@ -134,19 +139,25 @@ class Config:
     staging_chunk_bytes: int = 4 << 20
     staging_slots: int = 2
     bf16_acc: str = "per_hop"        # "per_hop" | "fp32_partials"
+    dma_stripe: int = 0              # SDMA engines per staging copy; 0 = half of them
+    dma_chunk_bytes: int = 0         # SDMA all-to-all chunk; 0 = automatic
+    dma_sync: str = "host_func"      # "host_func" | "stream_flags"
 
     def to_c(self) -> ccr_config_t:
         return ccr_config_t(CCR_COPY_SDMA if self.copy_mode == "sdma" else CCR_COPY_KERNEL,
                             self.cu_budget, self.slices, int(self.overlap),
                             self.staging_chunk_bytes, self.staging_slots,
                             CCR_BF16_ACC_FP32_PARTIALS if self.bf16_acc == "fp32_partials"
-                            else CCR_BF16_ACC_PER_HOP)
+                            else CCR_BF16_ACC_PER_HOP, self.dma_stripe, self.dma_chunk_bytes,
+                            1 if self.dma_sync == "stream_flags" else 0)
 
     @staticmethod
     def from_c(c: ccr_config_t) -> "Config":
         return Config("sdma" if c.copy_mode == CCR_COPY_SDMA else "kernel", c.cu_budget,
                       c.slices, bool(c.overlap), c.staging_chunk_bytes, c.staging_slots,
-                      "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop")
+                      "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop",
+                      c.dma_stripe, c.dma_chunk_bytes,
+                      "stream_flags" if c.dma_sync == 1 else "host_func")
 
 
 def ccr_config_default() -> Config:
@@ -335,3 +346,33 @@ def ccr_profile_read(ctx: Context, kind: str) -> dict:
     st = ccr_kernel_stats_t()
     _check(_lib.ccr_profile_read(ctx.handle, PROFILE_KINDS[kind], ctypes.byref(st)))
     return {"launches": st.launches, "bytes": st.bytes, "ms": st.ms}
+
+
+def ccr_dma_info(ctx: Context) -> list:
+    """HSA indices of the SDMA engines the context's DMA proxy uses."""
+    n = ctypes.c_int32()
+    ids = (ctypes.c_int32 * 16)()
+    _check(_lib.ccr_dma_info(ctx.handle, ctypes.byref(n), ids))
+    return list(ids[:n.value])
+
+
+def ccr_sendrecv_slot_log(ctx: Context) -> np.ndarray:
+    """(n, 3) int32 array of (chunk, slot, new state) of the last SDMA staged transfer."""
+    n = ctypes.c_int64()
+    _check(_lib.ccr_sendrecv_slot_log(ctx.handle, None, 0, ctypes.byref(n)))
+    out = np.zeros((n.value, 3), np.int32)
+    if n.value:
+        _check(_lib.ccr_sendrecv_slot_log(ctx.handle, out.ctypes.data, n.value, ctypes.byref(n)))
+    return out
+
+
+def ccr_stream_wait(ctx: Context, timeout_ms: int, stream=None) -> int:
+    """Returns CCR_OK or CCR_ERR_TIMEOUT; raises on other errors."""
+    st = _lib.ccr_stream_wait(ctx.handle, _stream(stream), timeout_ms)
+    if st not in (CCR_OK, CCR_ERR_TIMEOUT):
+        _check(st)
+    return st
+
+
+def ccr_dma_hold_finish(ctx: Context, us: int):
+    _check(_lib.ccr_dma_hold_finish(ctx.handle, us))

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libccr.so")
-SOURCES = ["ccr_api.cpp", "ccr_kernels.hip"]
+SOURCES = ["ccr_api.cpp", "ccr_dma.cpp", "ccr_kernels.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 arithmetic;
@@ -58,7 +58,10 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    r = subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+    # libhsa-runtime64 (SDMA engine copies): resolved at load time to the HSA
+    # runtime already in the process (torch's), like libamdhip64.
+    r = subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+                        "-L/opt/rocm/lib", "-lhsa-runtime64"],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of libccr.so failed:\n{r.stdout}{r.stderr}")

@@ -19,14 +19,19 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
+#include <numeric>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/ccr.h"
+#include "ccr_dma.h"
 #include "ccr_internal.h"
 
 using namespace ccr;
@@ -82,8 +87,8 @@ struct ccr_ctx {
   ccr_config_t cfg{};
   bool masked = false;          // s_a / s_b carry a CU mask
   hipStream_t s_a = nullptr;    // reduce / fill / exchange side stream
-  hipStream_t s_b = nullptr;    // all-gather (overlap) / drain side stream
-  std::vector<hipStream_t> s_dma;  // SDMA copy lanes (no CU mask: SDMA uses no CUs)
+  hipStream_t s_b = nullptr;    // all-gather (overlap, SDMA handshake) / drain side stream
+  std::unique_ptr<DmaProxy> dma;  // SDMA engines + CPU proxy, started on first SDMA use
   std::vector<hipEvent_t> ev;   // event pool, grown on demand
   char* staging = nullptr;      // staging_slots x staging_chunk_bytes
   int64_t staging_bytes = 0;
@@ -119,6 +124,14 @@ ccr_status_t check_config(const ccr_config_t* c) {
   if (c->bf16_acc != CCR_BF16_ACC_PER_HOP && c->bf16_acc != CCR_BF16_ACC_FP32_PARTIALS)
     return fail(CCR_ERR_INVALID_ARG, "bf16_acc %d is not per_hop (0) or fp32_partials (1)",
                 c->bf16_acc);
+  if (c->dma_stripe < 0 || c->dma_stripe > 16)
+    return fail(CCR_ERR_INVALID_ARG, "dma_stripe %d outside [0, 16]", c->dma_stripe);
+  if (c->dma_chunk_bytes < 0 || c->dma_chunk_bytes % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "dma_chunk_bytes %lld is not a non-negative multiple of 16",
+                (long long)c->dma_chunk_bytes);
+  if (c->dma_sync != CCR_DMA_SYNC_HOST_FUNC && c->dma_sync != CCR_DMA_SYNC_STREAM_FLAGS)
+    return fail(CCR_ERR_INVALID_ARG, "dma_sync %d is not host_func (0) or stream_flags (1)",
+                c->dma_sync);
   return CCR_OK;
 }
 
@@ -132,7 +145,6 @@ std::vector<uint32_t> cu_mask_for_budget(int budget, int num_cus) {
 }
 
 ccr_status_t destroy_streams(ccr_ctx* ctx) {
-  for (hipStream_t st : ctx->s_dma) HIP_TRY(hipStreamSynchronize(st));
   if (ctx->s_a) HIP_TRY(hipStreamSynchronize(ctx->s_a));
   if (ctx->s_b) HIP_TRY(hipStreamSynchronize(ctx->s_b));
   if (ctx->s_a) HIP_TRY(hipStreamDestroy(ctx->s_a));
@@ -142,31 +154,19 @@ ccr_status_t destroy_streams(ccr_ctx* ctx) {
   return CCR_OK;
 }
 
+// The side streams are always created with a CU mask (all CUs when there is
+// no budget): a CU-masked stream gets a hardware queue of its own.  Plain
+// streams share the runtime's few hardware queues round-robin, and a
+// handshake wait or a join parked in a shared in-order queue would stall
+// unrelated work (a concurrent GEMM) queued behind it.
 ccr_status_t make_streams(ccr_ctx* ctx) {
   CCR_TRY(destroy_streams(ctx));
   const int budget = ctx->cfg.cu_budget;
-  if (budget > 0 && budget < ctx->num_cus) {
-    std::vector<uint32_t> mask = cu_mask_for_budget(budget, ctx->num_cus);
-    HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_a, (uint32_t)mask.size(), mask.data()));
-    HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_b, (uint32_t)mask.size(), mask.data()));
-    ctx->masked = true;
-  } else {
-    HIP_TRY(hipStreamCreateWithFlags(&ctx->s_a, hipStreamNonBlocking));
-    HIP_TRY(hipStreamCreateWithFlags(&ctx->s_b, hipStreamNonBlocking));
-  }
-  return CCR_OK;
-}
-
-// Number of streams SDMA copies are spread over.  Independent copies on
-// different lanes overlap their (large, fixed) per-copy start-up cost.
-constexpr int kDmaLanes = 8;
-
-ccr_status_t dma_lanes(ccr_ctx* ctx) {
-  while ((int)ctx->s_dma.size() < kDmaLanes) {
-    hipStream_t st;
-    HIP_TRY(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
-    ctx->s_dma.push_back(st);
-  }
+  const bool limited = budget > 0 && budget < ctx->num_cus;
+  std::vector<uint32_t> mask = cu_mask_for_budget(limited ? budget : ctx->num_cus, ctx->num_cus);
+  HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_a, (uint32_t)mask.size(), mask.data()));
+  HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_b, (uint32_t)mask.size(), mask.data()));
+  ctx->masked = limited;
   return CCR_OK;
 }
 
@@ -358,45 +358,108 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
   return CCR_OK;
 }
 
-ccr_status_t sdma_copy(ccr_ctx* ctx, const Piece& p, hipStream_t s) {
-  if (p.nbytes <= 0) return CCR_OK;
-  TimedScope t{ctx, s, kProfSdma, 2 * p.nbytes};
-  CCR_TRY(t.begin());
-  HIP_TRY(hipMemcpyAsync(p.dst, p.src, (size_t)p.nbytes, hipMemcpyDeviceToDeviceNoCU, s));
-  return t.end();
-}
-
-// Fork the SDMA lanes off `from` (they wait for all work enqueued on it).
-ccr_status_t lanes_after(ccr_ctx* ctx, size_t ev_index, hipStream_t from) {
-  CCR_TRY(dma_lanes(ctx));
-  CCR_TRY(events(ctx, ev_index + 1));
-  HIP_TRY(hipEventRecord(ctx->ev[ev_index], from));
-  for (hipStream_t st : ctx->s_dma) HIP_TRY(hipStreamWaitEvent(st, ctx->ev[ev_index], 0));
+// ------------------------------------------------------------- SDMA path
+ccr_status_t ensure_dma(ccr_ctx* ctx) {
+  if (ctx->dma) return CCR_OK;
+  auto d = std::make_unique<DmaProxy>();
+  std::string err;
+  if (!d->start(ctx->device, &err)) return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
+  ctx->dma = std::move(d);
   return CCR_OK;
 }
 
-// Make `to` wait for every SDMA lane.
-ccr_status_t join_lanes(ccr_ctx* ctx, size_t ev_first, hipStream_t to) {
-  CCR_TRY(events(ctx, ev_first + ctx->s_dma.size()));
-  for (size_t i = 0; i < ctx->s_dma.size(); i++) {
-    HIP_TRY(hipEventRecord(ctx->ev[ev_first + i], ctx->s_dma[i]));
-    HIP_TRY(hipStreamWaitEvent(to, ctx->ev[ev_first + i], 0));
+ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s) {
+  std::string err;
+  if (!ctx->dma->submit_copies(std::move(copies), s, (DmaSync)ctx->cfg.dma_sync, &err))
+    return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
+  return CCR_OK;
+}
+
+// Flow-size-aware chunk schedule (HOCCL §3.4): every flow is cut into
+// chunks of at most C bytes and the chunks of all flows are interleaved so
+// that each flow's share of engine service follows its size -- chunk j of a
+// flow of n chunks gets the key (j + 0.5) / n and chunks are issued in key
+// order, round-robin over the engines.  All flows progress together and
+// finish together instead of a large flow holding an engine to the end.
+std::vector<DmaCopy> flow_chunks(const std::vector<Piece>& flows, int64_t C, int engines) {
+  struct Key {
+    double key;
+    size_t flow;
+    int64_t j;
+  };
+  std::vector<Key> keys;
+  for (size_t f = 0; f < flows.size(); f++) {
+    const int64_t n = (flows[f].nbytes + C - 1) / C;
+    for (int64_t j = 0; j < n; j++) keys.push_back(Key{(j + 0.5) / (double)n, f, j});
   }
-  return CCR_OK;
+  std::stable_sort(keys.begin(), keys.end(),
+                   [](const Key& a, const Key& b) { return a.key < b.key; });
+  std::vector<DmaCopy> out;
+  out.reserve(keys.size());
+  for (size_t i = 0; i < keys.size(); i++) {
+    const Piece& f = flows[keys[i].flow];
+    const int64_t lo = keys[i].j * C, hi = std::min<int64_t>(f.nbytes, lo + C);
+    out.push_back(DmaCopy{f.dst + lo, f.src + lo, hi - lo, -1, (int32_t)(i % (size_t)engines)});
+  }
+  return out;
 }
 
-// Copy `n` pieces on `s`: one kernel launch per kMaxPieces pieces, or one
-// SDMA transfer per piece.
+// Automatic chunk size for a DMA job: about 8 chunks per engine, kept
+// within [256 KiB, 16 MiB].
+int64_t auto_chunk(int64_t total, int engines) {
+  int64_t c = total / std::max(1, 8 * engines);
+  c = std::max<int64_t>(256 << 10, std::min<int64_t>(16 << 20, c));
+  return (c + 15) & ~int64_t(15);
+}
+
+// Copy `n` pieces on `s` with the copy kernel, kMaxPieces per launch.
 ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) {
-  if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
-    for (size_t i = 0; i < n; i++) CCR_TRY(sdma_copy(ctx, p[i], s));
-    return CCR_OK;
-  }
   for (size_t i = 0; i < n; i += kMaxPieces) {
     const int m = (int)std::min<size_t>(kMaxPieces, n - i);
     CCR_TRY(launch_timed(ctx, HopKind::kCopy, p + i, m, s));
   }
   return CCR_OK;
+}
+
+// The all-gather of slice s as DMA copies.  Chunk c's copies form a chain
+// (rank c -> c+1 -> ... -> c-1, one hop each).  Each chain is cut into m
+// sub-chains over equal byte ranges, m = E / gcd(R, E) (fewer if pieces
+// would drop below 256 KiB), so the R*m chains spread evenly over the E
+// engines; chain i runs on engine i mod E.  Copies are issued hop by hop, so
+// every engine receives its chains' copies in dependency order.
+std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, int s, int V,
+                               int esize, int engines) {
+  const int E = std::max(1, engines);
+  int m = E / std::gcd(R, E);
+  if (const char* e = getenv("CCR_DMA_SPLIT"); e && atoi(e) > 0) m = atoi(e);
+  std::vector<int64_t> lo((size_t)R), hi((size_t)R);
+  int64_t widest = 0;
+  for (int c = 0; c < R; c++) {
+    int64_t clo, chi;
+    chunk_range(count, R, V, c, &clo, &chi);
+    slice_range(clo, chi, S, V, s, &lo[(size_t)c], &hi[(size_t)c]);
+    widest = std::max(widest, (hi[(size_t)c] - lo[(size_t)c]) * esize);
+  }
+  while (m > 1 && widest / m < (256 << 10)) m--;
+  std::vector<DmaCopy> out;
+  std::vector<int32_t> prev((size_t)R * m, -1);
+  for (int k = 0; k + 1 < R; k++) {
+    for (int c = 0; c < R; c++) {
+      const int q = (c + 1 + k) % R, p = (q + R - 1) % R;
+      const int64_t b0 = lo[(size_t)c] * esize, nb = (hi[(size_t)c] - lo[(size_t)c]) * esize;
+      const int64_t part = ((nb + m - 1) / m + 15) & ~int64_t(15);
+      for (int j = 0; j < m; j++) {
+        const int64_t a = std::min(nb, j * part), z = std::min(nb, (j + 1) * part);
+        if (z <= a) continue;
+        const size_t chain = (size_t)c * m + j;
+        out.push_back(DmaCopy{static_cast<char*>(bufs[q]) + b0 + a,
+                              static_cast<const char*>(bufs[p]) + b0 + a, z - a, prev[chain],
+                              (int32_t)(chain % (size_t)E)});
+        prev[chain] = (int32_t)(out.size() - 1);
+      }
+    }
+  }
+  return out;
 }
 
 ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
@@ -430,16 +493,16 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   const bool fuse = which == kWhichAllreduce && ctx->cfg.copy_mode == CCR_COPY_KERNEL;
   // Reduce-scatter runs on the CU-masked stream when a budget is set, else
   // directly on the caller's stream.  All-gather follows it on the same
-  // stream, or on the second side stream when overlap is on.
-  // In SDMA mode the all-gather copies of chunk c form a chain (rank c ->
-  // c+1 -> ...) that runs in order on SDMA lane c mod kDmaLanes; copies are
-  // enqueued hop by hop so that the lanes interleave.
+  // stream, or on the second side stream when overlap is on.  With SDMA
+  // copies the all-gather of each slice is one DMA job whose handshake sits
+  // on the second side stream, so the reduce-scatter of the next slice keeps
+  // going while the engines copy.
   const bool sdma = ctx->cfg.copy_mode == CCR_COPY_SDMA && which != kWhichRS;
+  if (sdma) CCR_TRY(ensure_dma(ctx));
   hipStream_t rs = ctx->masked ? ctx->s_a : caller;
-  hipStream_t ag = (ctx->cfg.overlap && !sdma) ? ctx->s_b : rs;
+  hipStream_t ag = (ctx->cfg.overlap || sdma) ? ctx->s_b : rs;
   const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
-  const size_t ev_lanes = ev_slice0 + (size_t)S;
-  CCR_TRY(events(ctx, ev_lanes));
+  CCR_TRY(events(ctx, ev_slice0 + (size_t)S));
   if (rs != caller || ag != caller) {
     HIP_TRY(hipEventRecord(ctx->ev[ev_fork], caller));
     if (rs != caller) HIP_TRY(hipStreamWaitEvent(rs, ctx->ev[ev_fork], 0));
@@ -471,17 +534,9 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
       }
     }
     if (which != kWhichRS && sdma) {
-      CCR_TRY(lanes_after(ctx, ev_slice0 + (size_t)s, rs));
-      for (int k = 0; k + 1 < R; k++) {
-        ops.clear();
-        hop_ops(kAG, k, s, R, count, S, V, &ops);
-        for (const ccr_ring_op_t& o : ops) {
-          if (o.hi <= o.lo) continue;
-          Piece pc{static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize,
-                   static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize, (o.hi - o.lo) * esize};
-          CCR_TRY(sdma_copy(ctx, pc, ctx->s_dma[(size_t)(o.chunk % kDmaLanes)]));
-        }
-      }
+      CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
+      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, ctx->dma->engine_count()),
+                         ag));
     } else if (which != kWhichRS) {
       if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
       for (int k = fuse ? 1 : 0; k + 1 < R; k++) {
@@ -495,7 +550,6 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   }
   CCR_TRY(order_after(ctx, ev_join_rs, rs, caller));
   if (ag != rs) CCR_TRY(order_after(ctx, ev_join_ag, ag, caller));
-  if (sdma) CCR_TRY(join_lanes(ctx, ev_lanes, caller));
   return CCR_OK;
 }
 
@@ -529,11 +583,14 @@ ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* re
     }
   }
   if (ctx->cfg.copy_mode != CCR_COPY_SDMA) return copy_pieces(ctx, p.data(), p.size(), s);
-  // SDMA: the segment copies are independent; spread them over the lanes.
-  const size_t ev_fork = 8, ev_join = 9;
-  CCR_TRY(lanes_after(ctx, ev_fork, s));
-  for (size_t i = 0; i < p.size(); i++) CCR_TRY(sdma_copy(ctx, p[i], ctx->s_dma[i % kDmaLanes]));
-  return join_lanes(ctx, ev_join, s);
+  // SDMA: one DMA job; the segments are independent flows, chunked and
+  // interleaved by size over the engines.
+  CCR_TRY(ensure_dma(ctx));
+  int64_t total = 0;
+  for (const Piece& x : p) total += x.nbytes;
+  const int E = ctx->dma->engine_count();
+  const int64_t C = ctx->cfg.dma_chunk_bytes > 0 ? ctx->cfg.dma_chunk_bytes : auto_chunk(total, E);
+  return dma_submit(ctx, flow_chunks(p, C, E), s);
 }
 
 int64_t env_int(const char* name, int64_t dflt) {
@@ -559,6 +616,12 @@ ccr_status_t ccr_config_default(ccr_config_t* cfg) {
   cfg->staging_chunk_bytes = 4 << 20;
   cfg->staging_slots = 2;
   cfg->bf16_acc = CCR_BF16_ACC_PER_HOP;
+  cfg->dma_stripe = 0;
+  cfg->dma_chunk_bytes = 0;
+  cfg->dma_sync = CCR_DMA_SYNC_HOST_FUNC;
+  if (const char* e = getenv("CCR_DMA_SYNC"); e && *e)
+    cfg->dma_sync = strcmp(e, "stream_flags") == 0 ? CCR_DMA_SYNC_STREAM_FLAGS
+                                                   : CCR_DMA_SYNC_HOST_FUNC;
   if (const char* e = getenv("CCR_COPY_MODE"); e && *e)
     cfg->copy_mode = strcmp(e, "sdma") == 0 ? CCR_COPY_SDMA : CCR_COPY_KERNEL;
   if (const char* e = getenv("CCR_BF16_ACC"); e && *e)
@@ -569,6 +632,8 @@ ccr_status_t ccr_config_default(ccr_config_t* cfg) {
   cfg->overlap = (int32_t)env_int("CCR_OVERLAP", cfg->overlap);
   cfg->staging_chunk_bytes = env_int("CCR_STAGING_CHUNK", cfg->staging_chunk_bytes);
   cfg->staging_slots = (int32_t)env_int("CCR_STAGING_SLOTS", cfg->staging_slots);
+  cfg->dma_stripe = (int32_t)env_int("CCR_DMA_STRIPE", cfg->dma_stripe);
+  cfg->dma_chunk_bytes = env_int("CCR_DMA_CHUNK", cfg->dma_chunk_bytes);
   return check_config(cfg);
 }
 
@@ -606,8 +671,8 @@ ccr_status_t ccr_ctx_create(int device, const ccr_config_t* cfg, ccr_ctx_t* out)
 ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   if (!ctx) return CCR_OK;
   (void)hipSetDevice(ctx->device);
+  ctx->dma.reset();  // drains outstanding DMA operations, stops the proxy
   ccr_status_t st = destroy_streams(ctx);
-  for (hipStream_t x : ctx->s_dma) (void)hipStreamDestroy(x);
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   for (auto& t : ctx->timed) {
     (void)hipEventDestroy(t.start);
@@ -688,7 +753,28 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
   CCR_TRY(check_disjoint(ranges, "send/recv"));
   CCR_TRY(ensure_staging(ctx));
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
+    // One DMA job: the proxy runs the slot state machine itself, each fill
+    // and drain striped over several engines.
+    CCR_TRY(ensure_dma(ctx));
+    StagedPlan plan;
+    for (int m = 0; m < n; m++) {
+      plan.src.push_back(static_cast<const char*>(send[m]));
+      plan.dst.push_back(static_cast<char*>(recv[m]));
+    }
+    plan.nbytes = nbytes;
+    plan.chunk = ctx->cfg.staging_chunk_bytes;
+    plan.slots = ctx->cfg.staging_slots;
+    plan.slot_mem = ctx->staging;
+    plan.stripe = ctx->cfg.dma_stripe > 0 ? ctx->cfg.dma_stripe
+                                          : std::max(1, ctx->dma->engine_count() / 2);
+    std::string err;
+    if (!ctx->dma->submit_staged(plan, caller, (DmaSync)ctx->cfg.dma_sync, &err))
+      return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
+    return CCR_OK;
+  }
   hipStream_t fill = ctx->s_a, drain = ctx->s_b;
+
   const int P = ctx->cfg.staging_slots;
   const int64_t C = ctx->cfg.staging_chunk_bytes;
   // events: 0 fork, 1-2 joins, then filled[p] = 3 + p, drained[p] = 3 + P + p
@@ -979,15 +1065,86 @@ ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on) {
     ctx->timing_pool.push_back(t.stop);
   }
   ctx->timed.clear();
+  if (ctx->dma) {
+    ctx->dma->drain(30.0);
+    ctx->dma->reset_stats();
+  }
   ctx->prof_on = on != 0;
   return CCR_OK;
 }
+
+ccr_status_t ccr_dma_info(ccr_ctx_t ctx, int32_t* n, int32_t* ids) {
+  CCR_TRY(check_ctx(ctx));
+  if (!n) return fail(CCR_ERR_INVALID_ARG, "n is NULL");
+  CCR_TRY(ensure_dma(ctx));
+  *n = ctx->dma->engine_count();
+  if (ids)
+    for (int i = 0; i < *n; i++) ids[i] = ctx->dma->engine_id(i);
+  return CCR_OK;
+}
+
+ccr_status_t ccr_sendrecv_slot_log(ccr_ctx_t ctx, int32_t* out, int64_t max_events, int64_t* n) {
+  CCR_TRY(check_ctx(ctx));
+  if (!n || max_events < 0) return fail(CCR_ERR_INVALID_ARG, "n is NULL or max_events < 0");
+  *n = 0;
+  if (!ctx->dma) return CCR_OK;
+  if (!ctx->dma->drain(30.0)) return fail(CCR_ERR_TIMEOUT, "SDMA operations still running after 30 s");
+  const std::vector<SlotEvent> log = ctx->dma->last_slot_log();
+  *n = (int64_t)log.size();
+  for (int64_t i = 0; out && i < std::min<int64_t>(max_events, *n); i++) {
+    out[3 * i] = log[(size_t)i].chunk;
+    out[3 * i + 1] = log[(size_t)i].slot;
+    out[3 * i + 2] = log[(size_t)i].state;
+  }
+  return CCR_OK;
+}
+
+ccr_status_t ccr_stream_wait(ccr_ctx_t ctx, void* stream, int timeout_ms) {
+  CCR_TRY(check_ctx(ctx));
+  if (timeout_ms < 0) return fail(CCR_ERR_INVALID_ARG, "timeout_ms < 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    const hipError_t e = hipStreamQuery(s);
+    if (e == hipSuccess) break;
+    if (e != hipErrorNotReady) return hip_fail(e, "hipStreamQuery");
+    const double ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (ms > timeout_ms)
+      return fail(CCR_ERR_TIMEOUT, "stream work not complete after %d ms", timeout_ms);
+    std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+  if (ctx->dma) {
+    const std::string e = ctx->dma->take_error();
+    if (!e.empty()) return fail(CCR_ERR_HIP, "SDMA proxy: %s", e.c_str());
+  }
+  return CCR_OK;
+}
+
+ccr_status_t ccr_dma_hold_finish(ccr_ctx_t ctx, int us) {
+  CCR_TRY(check_ctx(ctx));
+  if (us < 0 || us > 10000000) return fail(CCR_ERR_INVALID_ARG, "us outside [0, 10 s]");
+  CCR_TRY(ensure_dma(ctx));
+  ctx->dma->set_finish_delay_us(us);
+  return CCR_OK;
+}
+
 
 ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t* out) {
   CCR_TRY(check_ctx(ctx));
   if (!out || kind < 0 || kind > 3) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 3]");
   HIP_TRY(hipDeviceSynchronize());
   ccr_kernel_stats_t st{0, 0, 0.0};
+  if (kind == kProfSdma) {
+    if (ctx->dma) {
+      ctx->dma->drain(30.0);
+      const DmaStats d = ctx->dma->stats();
+      *out = ccr_kernel_stats_t{d.jobs, d.bytes, d.ms};
+    } else {
+      *out = st;
+    }
+    return CCR_OK;
+  }
   for (const auto& t : ctx->timed) {
     if (t.kind != kind) continue;
     float ms = 0.f;

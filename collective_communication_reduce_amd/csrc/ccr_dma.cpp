@@ -1,0 +1,550 @@
+// SDMA engines driven by a CPU proxy thread; see ccr_dma.h.
+
+#include "ccr_dma.h"
+
+#include <immintrin.h>
+
+#include <atomic>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace ccr {
+namespace {
+
+constexpr int kFlags = 64;                 // flag pairs: operations in flight at once
+constexpr int kFlagStride = 32;            // words between flags (one 128-byte line each)
+constexpr uint32_t kStartValue = 0x53544152u;
+constexpr uint32_t kFinishValue = 0x46494e49u;
+// Engines gfx950 offers for device-to-device copies when the runtime cannot
+// report them itself (engines 0 and 1 serve host transfers).
+constexpr uint32_t kFallbackEngineMask = 0xfffcu;
+
+using clk = std::chrono::steady_clock;
+
+uint32_t load_flag(const uint32_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
+void store_flag(uint32_t* p, uint32_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+
+double seconds_since(clk::time_point t) {
+  return std::chrono::duration<double>(clk::now() - t).count();
+}
+
+struct AgentSearch {
+  uint32_t bus_dev;  // (bus << 5) | device
+  uint32_t domain;
+  int want_index;    // fallback: the n-th GPU agent
+  int seen = 0;
+  hsa_agent_t by_bdf{}, by_index{};
+  bool bdf_ok = false, index_ok = false;
+};
+
+hsa_status_t match_agent(hsa_agent_t a, void* data) {
+  auto* s = static_cast<AgentSearch*>(data);
+  hsa_device_type_t t;
+  if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS ||
+      t != HSA_DEVICE_TYPE_GPU)
+    return HSA_STATUS_SUCCESS;
+  if (s->seen++ == s->want_index) {
+    s->by_index = a;
+    s->index_ok = true;
+  }
+  uint32_t bdf = 0, dom = 0;
+  if (hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_BDFID, &bdf) ==
+          HSA_STATUS_SUCCESS &&
+      hsa_agent_get_info(a, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_DOMAIN, &dom) ==
+          HSA_STATUS_SUCCESS &&
+      (bdf >> 3) == s->bus_dev && dom == s->domain && !s->bdf_ok) {
+    s->by_bdf = a;
+    s->bdf_ok = true;
+  }
+  return HSA_STATUS_SUCCESS;
+}
+
+int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+}  // namespace
+
+struct DmaProxy::Job {
+  enum Kind { kCopies, kStaged } kind = kCopies;
+  enum State { kQueued, kRunning, kFinishing } state = kQueued;
+  DmaSync sync = DmaSync::kHostFunc;
+  DmaProxy* owner = nullptr;
+  // kHostFunc gate: 0 not reached, 1 stream at the gate (start request),
+  // 2 copies done (finish), 3 gate returned (final acknowledgement)
+  std::atomic<int> gate{0};
+  int flag = -1;  // kStreamFlags: flag pair
+  bool aborted = false;  // handshake only partly enqueued: release without copying
+  bool failed = false;   // an issue call failed: stop issuing, drain what was issued
+  clk::time_point t0;
+  int64_t bytes = 0, ncopies = 0;
+  // kCopies
+  std::vector<DmaCopy> copies;
+  std::vector<hsa_signal_t> sig;  // one per issued copy
+  size_t first_pending = 0;
+  // kStaged
+  StagedPlan plan;
+  struct Slot {
+    int state = 0;
+    int64_t chunk = -1;
+    std::vector<hsa_signal_t> sigs;
+  };
+  std::vector<Slot> slots;
+  int64_t next_chunk = 0, done_chunks = 0, total_chunks = 0, chunks_per_transfer = 0;
+  std::vector<SlotEvent> log;
+};
+
+DmaProxy::~DmaProxy() {
+  if (!started_) return;
+  const bool clean = drain(10.0);
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    stop_ = true;
+  }
+  cv_.notify_all();
+  if (thread_.joinable()) thread_.join();
+  for (hsa_signal_t s : signal_pool_) hsa_signal_destroy(s);
+  // A stream may still be waiting on an unreleased flag: keep the memory then.
+  if (clean && flags_) (void)hipHostFree(flags_);
+}
+
+void DmaProxy::note_error(const std::string& e) {
+  std::lock_guard<std::mutex> lk(mu_);
+  if (error_.empty()) error_ = e;
+}
+
+std::string DmaProxy::take_error() {
+  std::lock_guard<std::mutex> lk(mu_);
+  std::string e;
+  e.swap(error_);
+  return e;
+}
+
+bool DmaProxy::start(int device, std::string* err) {
+  if (started_) return true;
+  if (hsa_init() != HSA_STATUS_SUCCESS) {
+    *err = "hsa_init failed";
+    return false;
+  }
+  int bus = 0, dev = 0, dom = 0;
+  if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, device) != hipSuccess ||
+      hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, device) != hipSuccess ||
+      hipDeviceGetAttribute(&dom, hipDeviceAttributePciDomainId, device) != hipSuccess) {
+    (void)hipGetLastError();
+    *err = "cannot read the device's PCI location";
+    return false;
+  }
+  AgentSearch s;
+  s.bus_dev = ((uint32_t)bus << 5) | (uint32_t)dev;
+  s.domain = (uint32_t)dom;
+  s.want_index = device;
+  hsa_iterate_agents(match_agent, &s);
+  if (!s.bdf_ok && !s.index_ok) {
+    *err = "no HSA GPU agent for the device";
+    return false;
+  }
+  agent_ = s.bdf_ok ? s.by_bdf : s.by_index;
+
+  uint32_t mask = 0;
+  if (hsa_amd_memory_copy_engine_status(agent_, agent_, &mask) != HSA_STATUS_SUCCESS || mask == 0)
+    mask = kFallbackEngineMask;
+
+  // Warm every engine: the first copy on an engine sets up its queue and is
+  // slow (milliseconds); keep only engines whose warm-up copy completes.
+  char* scratch = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&scratch), 8192) != hipSuccess) {
+    (void)hipGetLastError();
+    *err = "hipMalloc of the engine warm-up buffer failed";
+    return false;
+  }
+  (void)hipMemset(scratch, 0, 8192);
+  (void)hipDeviceSynchronize();
+  bool any_stuck = false;
+  for (int e = 0; e < 16; e++) {
+    if (!(mask & (1u << e))) continue;
+    hsa_signal_t sg;
+    if (hsa_signal_create(1, 0, nullptr, &sg) != HSA_STATUS_SUCCESS) continue;
+    const hsa_status_t st = hsa_amd_memory_async_copy_on_engine(
+        scratch + 4096, agent_, scratch, agent_, 4096, 0, nullptr, sg,
+        (hsa_amd_sdma_engine_id_t)(1u << e), true);
+    bool ok = st == HSA_STATUS_SUCCESS;
+    if (ok) {
+      const auto t = clk::now();
+      while (hsa_signal_load_scacquire(sg) > 0) {
+        if (seconds_since(t) > 20.0) {
+          ok = false;
+          any_stuck = true;
+          break;
+        }
+        std::this_thread::yield();
+      }
+    }
+    if (ok) engines_.push_back(e);
+    if (!any_stuck) hsa_signal_destroy(sg);
+  }
+  if (!any_stuck) (void)hipFree(scratch);  // else an engine may still write it
+  if (engines_.empty()) {
+    *err = "no usable SDMA engine for device-to-device copies";
+    return false;
+  }
+  if (const char* cap = getenv("CCR_DMA_ENGINES"); cap && atoi(cap) > 0 &&
+      (size_t)atoi(cap) < engines_.size())
+    engines_.resize((size_t)atoi(cap));
+
+  if (hipHostMalloc(reinterpret_cast<void**>(&flags_), sizeof(uint32_t) * kFlagStride * 2 * kFlags,
+                    hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
+    (void)hipGetLastError();
+    *err = "hipHostMalloc of the flag pool failed";
+    return false;
+  }
+  memset(flags_, 0, sizeof(uint32_t) * kFlagStride * 2 * kFlags);
+  for (int f = kFlags - 1; f >= 0; f--) free_flags_.push_back(f);
+  thread_ = std::thread(&DmaProxy::loop, this);
+  started_ = true;
+  return true;
+}
+
+bool DmaProxy::take_flag(int* f, std::string* err) {
+  std::unique_lock<std::mutex> lk(mu_);
+  if (!freed_.wait_for(lk, std::chrono::seconds(30), [&] { return !free_flags_.empty(); })) {
+    *err = "no free start/finish flag pair within 30 s (DMA operations are not completing)";
+    return false;
+  }
+  *f = free_flags_.back();
+  free_flags_.pop_back();
+  return true;
+}
+
+// The stream side of the handshake: raise start, wait for the proxy's
+// acknowledgement (start back to 0), wait for finish, acknowledge it.
+bool DmaProxy::enqueue_handshake(int f, hipStream_t s, std::string* err) {
+  uint32_t* st = flags_ + (size_t)(2 * f) * kFlagStride;
+  uint32_t* fi = flags_ + (size_t)(2 * f + 1) * kFlagStride;
+  hipError_t e = hipStreamWriteValue32(s, st, kStartValue, 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *err = std::string("hipStreamWriteValue32 failed: ") + hipGetErrorString(e);
+    return false;
+  }
+  e = hipStreamWaitValue32(s, st, 0, hipStreamWaitValueEq, 0xffffffffu);
+  if (e == hipSuccess) e = hipStreamWaitValue32(s, fi, kFinishValue, hipStreamWaitValueEq, 0xffffffffu);
+  if (e == hipSuccess) e = hipStreamWriteValue32(s, fi, 0, 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *err = std::string("stream flag operation failed: ") + hipGetErrorString(e);
+    return false;  // start was enqueued: caller still hands the job over, marked aborted
+  }
+  return true;
+}
+
+// The host-function gate: runs on the runtime's callback thread when the
+// stream reaches it, and holds the stream until the proxy is done.
+void DmaProxy::gate(void* p) {
+  Job* j = static_cast<Job*>(p);
+  DmaProxy* self = j->owner;
+  std::unique_lock<std::mutex> lk(self->gate_mu_);
+  j->gate.store(1);
+  self->cv_.notify_one();
+  self->gate_cv_.wait(lk, [&] { return j->gate.load() == 2; });
+  j->gate.store(3);
+}
+
+bool DmaProxy::submit(Job* j, hipStream_t stream, std::string* err) {
+  j->owner = this;
+  if (j->sync == DmaSync::kHostFunc) {
+    const hipError_t e = hipLaunchHostFunc(stream, &DmaProxy::gate, j);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      *err = std::string("hipLaunchHostFunc failed: ") + hipGetErrorString(e);
+      delete j;
+      return false;
+    }
+  } else {
+    int f;
+    if (!take_flag(&f, err)) {
+      delete j;
+      return false;
+    }
+    j->flag = f;
+    std::string e2;
+    if (!enqueue_handshake(f, stream, &e2)) {
+      if (e2.rfind("hipStreamWriteValue32", 0) == 0) {  // nothing enqueued
+        delete j;
+        std::lock_guard<std::mutex> lk(mu_);
+        free_flags_.push_back(f);
+        *err = e2;
+        return false;
+      }
+      j->aborted = true;  // the stream will raise start: release it without copying
+      note_error(e2);
+      *err = e2;
+    }
+  }
+  const bool aborted = j->aborted;
+  {
+    std::lock_guard<std::mutex> lk(mu_);
+    incoming_.push_back(j);
+    pending_++;
+  }
+  cv_.notify_one();
+  return !aborted;
+}
+
+bool DmaProxy::submit_copies(std::vector<DmaCopy> copies, hipStream_t stream, DmaSync sync,
+                             std::string* err) {
+  if (copies.empty()) return true;
+  Job* j = new Job();
+  j->kind = Job::kCopies;
+  j->sync = sync;
+  for (const DmaCopy& c : copies) j->bytes += c.bytes;
+  j->ncopies = (int64_t)copies.size();
+  j->copies = std::move(copies);
+  return submit(j, stream, err);
+}
+
+bool DmaProxy::submit_staged(const StagedPlan& plan, hipStream_t stream, DmaSync sync,
+                             std::string* err) {
+  if (plan.src.empty() || plan.nbytes == 0) return true;
+  Job* j = new Job();
+  j->kind = Job::kStaged;
+  j->sync = sync;
+  j->plan = plan;
+  j->chunks_per_transfer = (plan.nbytes + plan.chunk - 1) / plan.chunk;
+  j->total_chunks = j->chunks_per_transfer * (int64_t)plan.src.size();
+  j->bytes = 2 * plan.nbytes * (int64_t)plan.src.size();
+  return submit(j, stream, err);
+}
+
+bool DmaProxy::drain(double timeout_s) {
+  std::unique_lock<std::mutex> lk(mu_);
+  return freed_.wait_for(lk, std::chrono::duration<double>(timeout_s), [&] { return pending_ == 0; });
+}
+
+DmaStats DmaProxy::stats() {
+  std::lock_guard<std::mutex> lk(mu_);
+  return stats_;
+}
+
+void DmaProxy::reset_stats() {
+  std::lock_guard<std::mutex> lk(mu_);
+  stats_ = DmaStats();
+}
+
+std::vector<SlotEvent> DmaProxy::last_slot_log() {
+  std::lock_guard<std::mutex> lk(mu_);
+  return slot_log_;
+}
+
+hsa_signal_t DmaProxy::get_signal() {
+  hsa_signal_t s;
+  if (!signal_pool_.empty()) {
+    s = signal_pool_.back();
+    signal_pool_.pop_back();
+  } else if (hsa_signal_create(1, 0, nullptr, &s) != HSA_STATUS_SUCCESS) {
+    s.handle = 0;
+    return s;
+  }
+  hsa_signal_store_relaxed(s, 1);
+  return s;
+}
+
+void DmaProxy::put_signal(hsa_signal_t s) {
+  if (s.handle) signal_pool_.push_back(s);
+}
+
+bool DmaProxy::issue(char* dst, const char* src, int64_t bytes, const hsa_signal_t* dep,
+                     hsa_signal_t done, int engine) {
+  if (!done.handle) return false;
+  const int e = engines_[(size_t)engine % engines_.size()];
+  return hsa_amd_memory_async_copy_on_engine(dst, agent_, src, agent_, (size_t)bytes, dep ? 1 : 0,
+                                             dep, done, (hsa_amd_sdma_engine_id_t)(1u << e),
+                                             true) == HSA_STATUS_SUCCESS;
+}
+
+// Issue every copy of a copy job at once; chains are expressed as HSA
+// dependencies, so the engines run them without CPU round trips.
+bool DmaProxy::begin(Job& j) {
+  if (j.kind == Job::kCopies) {
+    j.sig.reserve(j.copies.size());
+    for (size_t i = 0; i < j.copies.size(); i++) {
+      const DmaCopy& c = j.copies[i];
+      const hsa_signal_t* dep = nullptr;
+      if (c.after >= 0 && (size_t)c.after < j.sig.size()) dep = &j.sig[(size_t)c.after];
+      hsa_signal_t s = get_signal();
+      if (!issue(c.dst, c.src, c.bytes, dep, s, c.engine)) {
+        put_signal(s);
+        j.failed = true;
+        note_error("an SDMA copy could not be issued");
+        return true;
+      }
+      j.sig.push_back(s);
+    }
+    return true;
+  }
+  j.slots.assign((size_t)j.plan.slots, Job::Slot());
+  return true;
+}
+
+// Progress a running job; true once every issued copy has completed and
+// nothing is left to issue.
+bool DmaProxy::advance(Job& j) {
+  if (j.kind == Job::kCopies) {
+    while (j.first_pending < j.sig.size() &&
+           hsa_signal_load_scacquire(j.sig[j.first_pending]) <= 0)
+      j.first_pending++;
+    return j.first_pending == j.sig.size();
+  }
+  // Staged transfer: the per-slot state machine (idle -> filling ->
+  // draining -> idle); chunk i always uses slot i mod slots.
+  const StagedPlan& p = j.plan;
+  const int n_eng = (int)engines_.size();
+  const int stripe = std::max(1, std::min(p.stripe, n_eng));
+  const int drain_base = n_eng >= 2 * stripe ? n_eng / 2 : 0;
+  auto all_done = [](const std::vector<hsa_signal_t>& v) {
+    for (hsa_signal_t s : v)
+      if (hsa_signal_load_scacquire(s) > 0) return false;
+    return true;
+  };
+  auto striped = [&](Job::Slot& sl, char* dst, const char* src, int64_t len, int base) {
+    const int64_t part = align16((len + stripe - 1) / stripe);
+    for (int k = 0; k < stripe && !j.failed; k++) {
+      const int64_t lo = std::min<int64_t>(len, k * part), hi = std::min<int64_t>(len, (k + 1) * part);
+      if (hi <= lo) break;
+      hsa_signal_t s = get_signal();
+      if (!issue(dst + lo, src + lo, hi - lo, nullptr, s, base + k)) {
+        put_signal(s);
+        j.failed = true;
+        note_error("an SDMA staging copy could not be issued");
+        break;
+      }
+      sl.sigs.push_back(s);
+      j.ncopies++;
+    }
+  };
+  auto chunk_io = [&](int64_t c, int64_t* m, int64_t* off, int64_t* len) {
+    *m = c / j.chunks_per_transfer;
+    *off = (c % j.chunks_per_transfer) * p.chunk;
+    *len = std::min<int64_t>(p.chunk, p.nbytes - *off);
+  };
+  for (int s = 0; s < p.slots; s++) {
+    Job::Slot& sl = j.slots[(size_t)s];
+    if (sl.state == 0 || !all_done(sl.sigs)) continue;
+    for (hsa_signal_t x : sl.sigs) put_signal(x);
+    sl.sigs.clear();
+    if (sl.state == 1) {  // filled -> draining
+      sl.state = 2;
+      j.log.push_back(SlotEvent{(int32_t)sl.chunk, s, 2});
+      if (!j.failed) {
+        int64_t m, off, len;
+        chunk_io(sl.chunk, &m, &off, &len);
+        striped(sl, p.dst[(size_t)m] + off, p.slot_mem + (int64_t)s * p.chunk, len, drain_base);
+      }
+    } else {  // drained -> idle
+      sl.state = 0;
+      j.log.push_back(SlotEvent{(int32_t)sl.chunk, s, 0});
+      j.done_chunks++;
+    }
+  }
+  while (!j.failed && j.next_chunk < j.total_chunks) {
+    const int s = (int)(j.next_chunk % p.slots);
+    Job::Slot& sl = j.slots[(size_t)s];
+    if (sl.state != 0) break;  // chunks fill in order; wait for this slot
+    sl.state = 1;
+    sl.chunk = j.next_chunk++;
+    j.log.push_back(SlotEvent{(int32_t)sl.chunk, s, 1});
+    int64_t m, off, len;
+    chunk_io(sl.chunk, &m, &off, &len);
+    striped(sl, p.slot_mem + (int64_t)s * p.chunk, p.src[(size_t)m] + off, len, 0);
+  }
+  if (j.failed) {  // finish once nothing issued is still running
+    for (const Job::Slot& sl : j.slots)
+      if (!all_done(sl.sigs)) return false;
+    return true;
+  }
+  return j.done_chunks == j.total_chunks;
+}
+
+void DmaProxy::loop() {
+  for (;;) {
+    {
+      std::unique_lock<std::mutex> lk(mu_);
+      while (!incoming_.empty()) {
+        active_.push_back(incoming_.front());
+        incoming_.pop_front();
+      }
+      if (active_.empty()) {
+        if (stop_) return;
+        cv_.wait_for(lk, std::chrono::milliseconds(20));
+        continue;
+      }
+      if (stop_ && pending_ > 0) {
+        // Shutting down with operations whose streams never arrived: stop
+        // polling (their flags stay allocated) rather than spin forever.
+        bool any_started = false;
+        for (Job* j : active_) any_started |= j->state != Job::kQueued;
+        if (!any_started) return;
+      }
+    }
+    bool progress = false;
+    for (auto it = active_.begin(); it != active_.end();) {
+      Job& j = **it;
+      const bool flags = j.sync == DmaSync::kStreamFlags;
+      uint32_t* st = flags ? flags_ + (size_t)(2 * j.flag) * kFlagStride : nullptr;
+      uint32_t* fi = flags ? flags_ + (size_t)(2 * j.flag + 1) * kFlagStride : nullptr;
+      if (j.state == Job::kQueued) {
+        if (flags ? load_flag(st) == kStartValue : j.gate.load() == 1) {
+          if (flags) store_flag(st, 0);  // acknowledge the start request
+          j.t0 = clk::now();
+          if (!j.aborted) begin(j);
+          j.state = Job::kRunning;
+          progress = true;
+        }
+      } else if (j.state == Job::kRunning) {
+        if (j.aborted || advance(j)) {
+          if (const int d = finish_delay_us_.load(); d > 0)
+            std::this_thread::sleep_for(std::chrono::microseconds(d));
+          {
+            std::lock_guard<std::mutex> lk(mu_);
+            if (!j.aborted && !j.failed) {
+              stats_.jobs++;
+              stats_.copies += j.kind == Job::kCopies ? (int64_t)j.sig.size() : j.ncopies;
+              stats_.bytes += 2 * j.bytes;
+              stats_.ms += 1e3 * seconds_since(j.t0);
+            }
+            if (j.kind == Job::kStaged) slot_log_ = j.log;
+          }
+          for (hsa_signal_t s : j.sig) put_signal(s);
+          j.sig.clear();
+          if (flags) {
+            store_flag(fi, kFinishValue);  // release the stream
+          } else {
+            {
+              std::lock_guard<std::mutex> lk(gate_mu_);
+              j.gate.store(2);
+            }
+            gate_cv_.notify_all();
+          }
+          j.state = Job::kFinishing;
+          progress = true;
+        }
+      } else if (flags ? load_flag(fi) == 0 : j.gate.load() == 3) {
+        // the stream acknowledged the finish: the job (and its flag pair) is free
+        {
+          std::lock_guard<std::mutex> lk(mu_);
+          if (flags) free_flags_.push_back(j.flag);
+          pending_--;
+        }
+        freed_.notify_all();
+        delete &j;
+        it = active_.erase(it);
+        progress = true;
+        continue;
+      }
+      ++it;
+    }
+    if (!progress) _mm_pause();
+  }
+}
+
+}  // namespace ccr

@@ -55,10 +55,26 @@ typedef enum {
 typedef enum { CCR_F32 = 0, CCR_BF16 = 1 } ccr_dtype_t;
 
 /* How copy hops (all-gather, staging, exchange) move bytes.
- * KERNEL: a compute-unit copy kernel.  SDMA: hipMemcpyAsync with
- * hipMemcpyDeviceToDeviceNoCU, i.e. the SDMA engines and no compute unit
- * (HOCCL Fig. 1c: DMA engine instead of SMs). */
+ * KERNEL: a compute-unit copy kernel on the caller's (or the CU-masked)
+ * stream.  SDMA: the SDMA engines, no compute unit touches the data (HOCCL
+ * Fig. 1c: DMA engine instead of SMs).  The copies are issued on the
+ * device's SDMA engines by a CPU proxy thread that the stream hands each
+ * operation to when it reaches it (HOCCL §3.2: the CPU takes over the
+ * stream's coordination, with an explicit start request, finish and
+ * acknowledgement); see ccr_dma_sync_t. */
 typedef enum { CCR_COPY_KERNEL = 0, CCR_COPY_SDMA = 1 } ccr_copy_mode_t;
+
+/* How an SDMA operation is tied to the stream.
+ * HOST_FUNC (default): a hipLaunchHostFunc gate; the gate hands the
+ *   operation to the proxy and returns when the copies are done, and the
+ *   stream waits on the gate's completion without any GPU-side polling.
+ * STREAM_FLAGS: the flag handshake of HOCCL Listing 1 on host flags with
+ *   hipStreamWriteValue32 / hipStreamWaitValue32 (the stream raises start,
+ *   waits for the proxy to reset it, waits for finish, resets it).  This
+ *   HIP runtime executes those as kernels, and a stream waiting in
+ *   hipStreamWaitValue32 for the length of a DMA slows concurrent compute
+ *   by tens of percent, so it is kept for comparison only. */
+typedef enum { CCR_DMA_SYNC_HOST_FUNC = 0, CCR_DMA_SYNC_STREAM_FLAGS = 1 } ccr_dma_sync_t;
 
 /* bf16 reduce-scatter accumulation.  PER_HOP: every hop computes
  * bf16_rne(float(a) + float(b)); bf16 travels between ranks.
@@ -75,22 +91,30 @@ typedef struct {
     int64_t staging_chunk_bytes; /* P2P staging chunk (multiple of 16)              */
     int32_t staging_slots;       /* number of staging slots (>= 1)                  */
     int32_t bf16_acc;            /* ccr_bf16_acc_t                                  */
+    int32_t dma_stripe;          /* SDMA: engines each staging fill/drain is striped
+                                    over; 0 = half the engines                      */
+    int64_t dma_chunk_bytes;     /* SDMA: all-to-all flows are cut into chunks of at
+                                    most this size (multiple of 16); 0 = automatic  */
+    int32_t dma_sync;            /* ccr_dma_sync_t                                  */
 } ccr_config_t;
 
 typedef struct ccr_ctx *ccr_ctx_t;
 
 /* Fill *cfg with the defaults (kernel copies, all CUs, S = 1, no overlap,
- * 4 MiB x 2 staging slots, per-hop bf16), then apply the environment
- * overrides CCR_COPY_MODE (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES,
- * CCR_OVERLAP, CCR_STAGING_CHUNK, CCR_STAGING_SLOTS, CCR_BF16_ACC
- * (per_hop|fp32_partials).  HOCCL §4 switches backends by an environment
- * variable; this mirrors that. */
+ * 4 MiB x 2 staging slots, per-hop bf16, automatic SDMA striping and
+ * chunking), then apply the environment overrides CCR_COPY_MODE
+ * (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES, CCR_OVERLAP, CCR_STAGING_CHUNK,
+ * CCR_STAGING_SLOTS, CCR_BF16_ACC (per_hop|fp32_partials), CCR_DMA_STRIPE,
+ * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags).  HOCCL §4 switches backends by an environment variable;
+ * this mirrors that. */
 ccr_status_t ccr_config_default(ccr_config_t *cfg);
 
 /* Create a context on HIP device `device`.  cfg NULL = ccr_config_default().
- * The context owns its side streams (one of them CU-masked when cu_budget is
- * set), events, staging slots and small device scratch.  Makes `device`
- * current on the calling thread. */
+ * The context owns its side streams (CU-masked when cu_budget is set),
+ * events, staging slots, small device scratch and -- from the first SDMA
+ * use on -- the DMA proxy thread, its flag pool and its engine list (every
+ * engine is warmed with a small copy when the proxy starts).  Makes
+ * `device` current on the calling thread. */
 ccr_status_t ccr_ctx_create(int device, const ccr_config_t *cfg, ccr_ctx_t *out);
 /* Waits for the context's streams, then frees everything it owns. */
 ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx);
@@ -211,6 +235,28 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void *const *exp, const int32_
 /* ----------------------------------------------------------------------
  * Diagnostics.
  * ---------------------------------------------------------------------- */
+/* SDMA engines the context's DMA proxy uses (starts the proxy if needed):
+ * *n = engine count, ids[0..*n) = HSA engine indices (ids may be NULL;
+ * room for 16). */
+ccr_status_t ccr_dma_info(ccr_ctx_t ctx, int32_t *n, int32_t *ids);
+
+/* Slot transitions of the context's most recent SDMA staged transfer
+ * (ccr_sendrecv with copy_mode SDMA), in the order the proxy made them:
+ * out[3*i] = chunk, out[3*i+1] = slot, out[3*i+2] = new state (0 idle,
+ * 1 filling, 2 draining).  Synchronises with the proxy first.  Writes at
+ * most max_events records; *n receives the full count. */
+ccr_status_t ccr_sendrecv_slot_log(ccr_ctx_t ctx, int32_t *out, int64_t max_events, int64_t *n);
+
+/* Wait up to timeout_ms for all work enqueued on `stream` to complete.
+ * Returns CCR_ERR_TIMEOUT if it has not (the work keeps running), or
+ * CCR_ERR_HIP with the proxy's message if the DMA proxy reported an error. */
+ccr_status_t ccr_stream_wait(ccr_ctx_t ctx, void *stream, int timeout_ms);
+
+/* Fault injection for watchdog tests: the DMA proxy holds every
+ * operation's finish flag for `us` microseconds after its copies complete
+ * (0 = off).  The stream is always released in the end. */
+ccr_status_t ccr_dma_hold_finish(ccr_ctx_t ctx, int us);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char *ccr_last_error(void);
 /* Library version string. */

@@ -103,3 +103,65 @@ def test_permute_rows_skips_out_of_range_index(ccr_mod):
     np.testing.assert_array_equal(out[0], src[3])
     np.testing.assert_array_equal(out[3], src[0])
     assert np.all(out[1] == 7) and np.all(out[2] == 7)
+
+
+# ------------------------------------------------- SDMA engines + CPU proxy
+def test_dma_engines_available(ccr_mod):
+    say("dma engines")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma")) as c:
+        ids = ccr_mod.ccr_dma_info(c)
+    assert len(ids) >= 1 and len(set(ids)) == len(ids) and all(0 <= i < 16 for i in ids)
+
+
+@pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
+@pytest.mark.parametrize("m,nbytes,chunk,slots,stripe", [(4, 1 << 20, 1 << 18, 2, 0), (3, 100000 // 16 * 16, 16384, 3, 2),
+                                                         (1, 4096, 4096, 1, 1)])
+def test_sdma_staged_slot_state_machine(ccr_mod, m, nbytes, chunk, slots, stripe, sync):
+    """The proxy's staging slots follow idle -> filling -> draining -> idle,
+    chunk i uses slot i mod slots, chunks fill in order, every chunk once,
+    and the bytes arrive intact."""
+    import torch
+    rng = np.random.default_rng(nbytes)
+    srcs = [rng.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(m)]
+    say(f"sdma staged m={m} nbytes={nbytes} chunk={chunk} slots={slots} stripe={stripe} sync={sync}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma", staging_chunk_bytes=chunk,
+                                           staging_slots=slots, dma_stripe=stripe, dma_sync=sync)) as c:
+        s = [raw_to_dev(x) for x in srcs]
+        r = [torch.zeros_like(x) for x in s]
+        ccr_mod.ccr_sendrecv(c, s, r)
+        torch.cuda.synchronize()
+        for a, b in zip(r, srcs):
+            assert to_host(a).tobytes() == b.tobytes()
+        log = ccr_mod.ccr_sendrecv_slot_log(c)
+    nchunks = m * (-(-nbytes // chunk))
+    assert len(log) == 3 * nchunks
+    state = [0] * slots
+    fills = []
+    for ch, sl, st in log.tolist():
+        assert sl == ch % slots
+        assert (state[sl], st) in ((0, 1), (1, 2), (2, 0)), (state[sl], st)
+        state[sl] = st
+        if st == 1:
+            fills.append(ch)
+    assert fills == list(range(nchunks)) and state == [0] * slots
+
+
+@pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
+def test_sdma_watchdog_reports_a_slow_operation(ccr_mod, sync):
+    """With the proxy holding the finish flag, a bounded wait on the stream
+    times out; the stream is released afterwards and the result is exact."""
+    import torch
+    R, n = 4, 40000
+    xs = workloads.random_buffers(R, n, "f32", seed=8, dist="normal")
+    say(f"sdma watchdog sync={sync}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma", dma_sync=sync)) as c:
+        ts = [to_dev(x) for x in xs]
+        torch.cuda.synchronize()
+        ccr_mod.ccr_dma_hold_finish(c, 300_000)
+        ccr_mod.ccr_allreduce(c, ts)
+        assert ccr_mod.ccr_stream_wait(c, 30) == ccr_mod.CCR_ERR_TIMEOUT
+        assert ccr_mod.ccr_stream_wait(c, 20_000) == ccr_mod.CCR_OK
+        ccr_mod.ccr_dma_hold_finish(c, 0)
+        ref = oracle.ring_allreduce(xs)
+        for q, t in enumerate(ts):
+            np.testing.assert_array_equal(to_host(t), ref[q])

@@ -69,7 +69,8 @@ def test_reduce_scatter_and_all_gather_bitwise(ccr_mod, ctx, dt, R, n):
 
 MODES = [dict(overlap=True, slices=4), dict(copy_mode="sdma", slices=2),
          dict(copy_mode="sdma", overlap=True, slices=3), dict(cu_budget=64, slices=2),
-         dict(cu_budget=16, overlap=True, slices=2, copy_mode="sdma")]
+         dict(cu_budget=16, overlap=True, slices=2, copy_mode="sdma"),
+         dict(copy_mode="sdma", slices=2, dma_sync="stream_flags")]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=lambda m: "-".join(f"{k}={v}" for k, v in m.items()))
