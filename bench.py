@@ -25,6 +25,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -153,6 +155,72 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
     return out
 
 
+def median_ms(fn, reps=10, warm=3):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sorted(ts)[len(ts) // 2]
+
+
+def workload_timings(ccr, workloads):
+    """The other workloads, for context (each is also a full-size parity
+    test): median time per call and the figures of merit of each."""
+    import torch
+    out = {}
+    for w, how in ((workloads.RING_SMALL_F32, "allreduce"), (workloads.RS_AG_R32_F32, "rs_then_ag")):
+        bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
+        b, R, N = 4, w.R, w.count
+        with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
+            if how == "allreduce":
+                ms = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 20)
+                algo = b * N * (3 * (R - 1) + 1 + 2 * (R - 2))
+            else:
+                ms = median_ms(lambda: (ccr.ccr_reduce_scatter(ctx, bufs),
+                                        ccr.ccr_all_gather(ctx, bufs)), 10)
+                algo = b * N * 5 * (R - 1)
+        out[w.name] = {"ms": round(ms, 4), "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
+                       "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "slices": w.slices}
+        del bufs
+    m = workloads.MOE_DISPATCH_BF16
+    R, T, H, E, K = m.R, m.tokens, m.hidden, m.experts, m.topk
+    xs = [torch.randn(T, H, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    logits = [torch.randn(T, E, device="cuda") for _ in range(R)]
+    with ccr.Context(0) as ctx:
+        topk = [torch.empty(T, K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        src_tok = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        slot = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        route_ms = median_ms(lambda: [ccr.ccr_moe_topk(ctx, logits[r], topk[r]) for r in range(R)], 10)
+        ecnt = np.stack([ccr.ccr_moe_plan(ctx, topk[r], E, R, src_tok[r], slot[r]) for r in range(R)])
+    rows = [int(ecnt[:, (E // R) * d:(E // R) * (d + 1)].sum()) for d in range(R)]
+    send = [torch.empty(T * K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    recv = [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows]
+    exp = [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows]
+    outb = [torch.empty(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    moved = R * T * K * H * 2  # bytes of rows each stage moves over all ranks
+    res = {"route_topk_ms_all_ranks": round(route_ms, 4), "rows_per_rank": T * K,
+           "exchange_bytes": moved}
+    for mode in ("kernel", "sdma"):
+        with ccr.Context(0, ccr.Config(copy_mode=mode)) as ctx:
+            d_ms = median_ms(lambda: ccr.ccr_moe_dispatch(ctx, xs, src_tok, ecnt, K, send, recv, exp), 10)
+            c_ms = median_ms(lambda: ccr.ccr_moe_combine(ctx, exp, slot, ecnt, T, K, recv, send, outb), 10)
+        # three stages (pack, exchange, unpack), each reading and writing `moved` bytes
+        res[mode] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
+                     "dispatch_algorithmic_gbs": round(3 * 2 * moved / (d_ms * 1e-3) / 1e9, 1),
+                     "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
+    out[m.name] = res
+    return out
+
+
 def host_call_us(ccr, call, reps=50):
     """Host time per enqueue (HOCCL Fig. 9 measures CPU launch time per op)."""
     import torch
@@ -244,7 +312,6 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import collective_communication_reduce_amd as ccr
@@ -312,6 +379,11 @@ def main():
                 launch[f"sendrecv_16MiB_{m}"] = host_call_us(
                     ccr, lambda: ccr.ccr_sendrecv(c2, mbs[:1], outs[:1]), 20)
 
+    others = None
+    if not args.no_gemm:
+        log("bench: the other workloads (context)")
+        others = workload_timings(ccr, workloads)
+
     cpu = None
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
@@ -346,6 +418,7 @@ def main():
         "pp_staging_gemm_slowdown": pp,
         "cu_occupancy": occ,
         "host_us_per_call": launch,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     ctx.close()

@@ -95,6 +95,8 @@ struct ccr_ctx {
   int64_t* d_ecnt = nullptr;    // MoE plan counts scratch
   int64_t d_ecnt_len = 0;
   int64_t* h_pinned = nullptr;  // pinned mirror of d_ecnt
+  float* partials = nullptr;    // fp32 partials: 2 (hop parity) x R x chunk
+  int64_t partials_bytes = 0;
   // per-launch timing (ccr_profile_enable): event pairs and payload bytes
   bool prof_on = false;
   struct Timed {
@@ -412,6 +414,40 @@ int64_t auto_chunk(int64_t total, int engines) {
   return (c + 15) & ~int64_t(15);
 }
 
+// fp32-partials hop; algorithmic bytes per element: read local bf16 (2) and
+// incoming (2 bf16 / 4 fp32), write the partial (4 fp32) or the result
+// (2 bf16, twice when forwarding).
+ccr_status_t launch_partials_timed(ccr_ctx* ctx, PartialKind kind, const PartialPiece* p, int n,
+                                   hipStream_t s) {
+  if (!ctx->prof_on) {
+    HIP_TRY(launch_partials(kind, p, n, s));
+    return CCR_OK;
+  }
+  int64_t elems = 0;
+  for (int i = 0; i < n; i++) elems += p[i].n;
+  const int per = kind == PartialKind::kFirst ? 8 : kind == PartialKind::kMid ? 10
+                  : kind == PartialKind::kLast ? 8 : 10;
+  hipEvent_t start, stop;
+  CCR_TRY(timing_event(ctx, &start));
+  CCR_TRY(timing_event(ctx, &stop));
+  HIP_TRY(launch_partials(kind, p, n, s, start, stop));
+  ctx->timed.push_back(ccr_ctx::Timed{kProfReduce, start, stop, elems * per});
+  return CCR_OK;
+}
+
+ccr_status_t ensure_partials(ccr_ctx* ctx, int64_t bytes) {
+  if (ctx->partials && ctx->partials_bytes >= bytes) return CCR_OK;
+  if (ctx->partials) {
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipFree(ctx->partials));
+    ctx->partials = nullptr;
+    ctx->partials_bytes = 0;
+  }
+  HIP_TRY(hipMalloc(reinterpret_cast<void**>(&ctx->partials), (size_t)bytes));
+  ctx->partials_bytes = bytes;
+  return CCR_OK;
+}
+
 // Copy `n` pieces on `s` with the copy kernel, kMaxPieces per launch.
 ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) {
   for (size_t i = 0; i < n; i += kMaxPieces) {
@@ -470,8 +506,6 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   if (count < 0) return fail(CCR_ERR_INVALID_ARG, "count %lld < 0", (long long)count);
   const int esize = dtype_size(dtype);
   if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
-  if (dtype == CCR_BF16 && which != kWhichAG && ctx->cfg.bf16_acc != CCR_BF16_ACC_PER_HOP)
-    return fail(CCR_ERR_UNSUPPORTED, "bf16 fp32-partials accumulation is not built");
   if (count == 0) return CCR_OK;
   std::vector<Range> ranges;
   for (int q = 0; q < R; q++) {
@@ -491,6 +525,13 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   // that hop each forwarded element is written only by the thread that read
   // the same element, and no other operation of the hop touches it.
   const bool fuse = which == kWhichAllreduce && ctx->cfg.copy_mode == CCR_COPY_KERNEL;
+  // bf16 with the running partial carried in fp32 between ranks (R = 2 has a
+  // single hop, identical to per-hop rounding).  Partials live in context
+  // scratch, double-buffered by hop parity, indexed by offset in the chunk.
+  const bool partials = dtype == CCR_BF16 && which != kWhichAG && R > 2 &&
+                        ctx->cfg.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS;
+  const int64_t Lc = align_up(ceil_div(count, R), V);
+  if (partials) CCR_TRY(ensure_partials(ctx, 2 * (int64_t)R * Lc * 4));
   // Reduce-scatter runs on the CU-masked stream when a budget is set, else
   // directly on the caller's stream.  All-gather follows it on the same
   // stream, or on the second side stream when overlap is on.  With SDMA
@@ -522,12 +563,39 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
       pieces[(size_t)(*n)++] = pc;
     }
   };
+  std::vector<PartialPiece> pp((size_t)R);
   for (int s = 0; s < S; s++) {
     if (which != kWhichAG) {
       for (int k = 0; k + 1 < R; k++) {
         ops.clear();
         hop_ops(kRS, k, s, R, count, S, V, &ops);
         const bool forward = fuse && k == R - 2;
+        if (partials) {
+          int n = 0;
+          for (const ccr_ring_op_t& o : ops) {
+            if (o.hi <= o.lo) continue;
+            int64_t clo, chi;
+            chunk_range(count, R, V, o.chunk, &clo, &chi);
+            const int64_t off = o.lo - clo;
+            char* mine = static_cast<char*>(bufs[o.dst_rank]) + o.lo * esize;
+            PartialPiece pc;
+            pc.loc = mine;
+            pc.in = k == 0 ? static_cast<const char*>(bufs[o.src_rank]) + o.lo * esize
+                           : reinterpret_cast<const char*>(
+                                 ctx->partials + ((int64_t)((k - 1) % 2) * R + o.src_rank) * Lc + off);
+            pc.out = k == R - 2 ? mine
+                                : reinterpret_cast<char*>(
+                                      ctx->partials + ((int64_t)(k % 2) * R + o.dst_rank) * Lc + off);
+            pc.out2 = forward ? static_cast<char*>(bufs[(o.dst_rank + 1) % R]) + o.lo * esize : nullptr;
+            pc.n = o.hi - o.lo;
+            pp[(size_t)n++] = pc;
+          }
+          const PartialKind pk = k == 0 ? PartialKind::kFirst
+                                 : k < R - 2 ? PartialKind::kMid
+                                 : forward ? PartialKind::kLastFwd : PartialKind::kLast;
+          CCR_TRY(launch_partials_timed(ctx, pk, pp.data(), n, rs));
+          continue;
+        }
         int n;
         to_pieces(&n, forward);
         CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs));
@@ -681,6 +749,7 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   for (hipEvent_t e : ctx->timing_pool) (void)hipEventDestroy(e);
   if (ctx->staging) (void)hipFree(ctx->staging);
   if (ctx->d_ecnt) (void)hipFree(ctx->d_ecnt);
+  if (ctx->partials) (void)hipFree(ctx->partials);
   if (ctx->h_pinned) (void)hipHostFree(ctx->h_pinned);
   delete ctx;
   return st;

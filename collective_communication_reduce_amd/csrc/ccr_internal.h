@@ -45,6 +45,24 @@ struct LaunchTuning {
                     // looping over the tiles
 };
 
+// bf16 reduce-scatter with the running partial carried in fp32.  Per
+// piece: out = in + float(loc) over n elements, where `in` is bf16 (the
+// first hop) or fp32 (a partial), and `out` is fp32 (a partial) or bf16
+// (the last hop, rounded to nearest even; also written to out2 when
+// forwarding).  Pointers are 16-byte aligned; element groups of 8.
+struct PartialPiece {
+  char* out;
+  const char* in;
+  const char* loc;
+  char* out2;
+  int64_t n;
+};
+
+enum class PartialKind : int { kFirst = 0, kMid = 1, kLast = 2, kLastFwd = 3 };
+
+hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
 // Enqueue one batched launch over `n` pieces (n <= kMaxPieces).  With
 // start/stop events, the launch goes through hipExtLaunchKernelGGL so that
 // the events carry the kernel's own start and end timestamps.

@@ -209,6 +209,99 @@ hipError_t launch_unroll(const PieceArgs& a, int unroll, bool nt, hipStream_t s,
   }
 }
 
+// ---------------------------------------------------------- fp32 partials
+struct PartialArgs {
+  PartialPiece p[kMaxPieces];
+  int32_t tile_start[kMaxPieces + 1];
+  int32_t n;
+};
+
+constexpr int kPartialUnroll = 2;  // 8-element groups per thread per tile
+
+__device__ __forceinline__ void unpack_bf16x8(u32x4 w, float* f) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f[2 * j] = bf16_lo(w[j]);
+    f[2 * j + 1] = bf16_hi(w[j]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f32x2 v = {f[2 * j], f[2 * j + 1]};
+    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  return r;
+}
+
+// One group of 8 elements: out = in + float(loc).
+template <PartialKind K>
+__device__ __forceinline__ void partial_group(const PartialPiece& pc, int64_t g) {
+  float loc[8], in[8], acc[8];
+  unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.loc)[g], loc);
+  if constexpr (K == PartialKind::kFirst) {
+    unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.in)[g], in);
+  } else {
+    const f32x4 a = reinterpret_cast<const f32x4*>(pc.in)[2 * g];
+    const f32x4 b = reinterpret_cast<const f32x4*>(pc.in)[2 * g + 1];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      in[j] = a[j];
+      in[4 + j] = b[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = in[j] + loc[j];
+  if constexpr (K == PartialKind::kFirst || K == PartialKind::kMid) {
+    reinterpret_cast<f32x4*>(pc.out)[2 * g] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    reinterpret_cast<f32x4*>(pc.out)[2 * g + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    const u32x4 r = pack_bf16x8(acc);
+    reinterpret_cast<u32x4*>(pc.out)[g] = r;
+    if constexpr (K == PartialKind::kLastFwd) reinterpret_cast<u32x4*>(pc.out2)[g] = r;
+  }
+}
+
+template <PartialKind K>
+__device__ __forceinline__ void partial_one(const PartialPiece& pc, int64_t i) {
+  const float loc = bf16_lo(reinterpret_cast<const uint16_t*>(pc.loc)[i]);
+  const float in = K == PartialKind::kFirst ? bf16_lo(reinterpret_cast<const uint16_t*>(pc.in)[i])
+                                            : reinterpret_cast<const float*>(pc.in)[i];
+  const float acc = in + loc;
+  if constexpr (K == PartialKind::kFirst || K == PartialKind::kMid) {
+    reinterpret_cast<float*>(pc.out)[i] = acc;
+  } else {
+    const uint16_t r = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc));
+    reinterpret_cast<uint16_t*>(pc.out)[i] = r;
+    if constexpr (K == PartialKind::kLastFwd) reinterpret_cast<uint16_t*>(pc.out2)[i] = r;
+  }
+}
+
+template <PartialKind K>
+__global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs a) {
+  const int b = blockIdx.x;
+  int lo = 0, hi = a.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_start[mid] <= b) lo = mid;
+    else hi = mid;
+  }
+  const PartialPiece pc = a.p[lo];
+  const int64_t ngroups = pc.n >> 3;
+  const int64_t tile = b - a.tile_start[lo];
+  const int64_t first = tile * (int64_t)(kBlock * kPartialUnroll);
+#pragma unroll
+  for (int u = 0; u < kPartialUnroll; u++) {
+    const int64_t g = first + u * kBlock + threadIdx.x;
+    if (g < ngroups) partial_group<K>(pc, g);
+  }
+  const int tail = (int)(pc.n & 7);
+  if (tail > 0 && tile == ngroups / (kBlock * kPartialUnroll) && (int)threadIdx.x < tail)
+    partial_one<K>(pc, (ngroups << 3) + threadIdx.x);
+}
+
 // ---------------------------------------------------------------- permute
 // dst row i = src row idx[i].  One workgroup moves RPB rows; thread t moves
 // 16-byte column t (and t + kBlock, ...) of each, with the RPB loads of a
@@ -392,6 +485,37 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
       return launch_unroll<HopKind::kReduceFwdBf16>(a, unroll, nt, stream, t, g);
     default: return launch_unroll<HopKind::kCopy>(a, unroll, nt, stream, t, g);
   }
+}
+
+hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
+                           hipEvent_t start, hipEvent_t stop) {
+  if (n <= 0) return hipSuccess;
+  if (n > kMaxPieces) return hipErrorInvalidValue;
+  PartialArgs a;
+  const int64_t per_tile = (int64_t)kBlock * kPartialUnroll;
+  int64_t tiles = 0;
+  a.n = n;
+  for (int i = 0; i < n; i++) {
+    a.p[i] = pieces[i];
+    a.tile_start[i] = (int32_t)tiles;
+    const int64_t units = (pieces[i].n >> 3) + ((pieces[i].n & 7) ? 1 : 0);
+    tiles += (units + per_tile - 1) / per_tile;
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  }
+  for (int i = n; i <= kMaxPieces; i++) a.tile_start[i] = (int32_t)tiles;
+  if (tiles == 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles), block(kBlock);
+  auto go = [&](auto kernel) {
+    if (start && stop) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, a);
+    else kernel<<<grid, block, 0, stream>>>(a);
+  };
+  switch (kind) {
+    case PartialKind::kFirst: go(partial_kernel<PartialKind::kFirst>); break;
+    case PartialKind::kMid: go(partial_kernel<PartialKind::kMid>); break;
+    case PartialKind::kLast: go(partial_kernel<PartialKind::kLast>); break;
+    default: go(partial_kernel<PartialKind::kLastFwd>); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,

@@ -79,7 +79,9 @@ typedef enum { CCR_DMA_SYNC_HOST_FUNC = 0, CCR_DMA_SYNC_STREAM_FLAGS = 1 } ccr_d
 /* bf16 reduce-scatter accumulation.  PER_HOP: every hop computes
  * bf16_rne(float(a) + float(b)); bf16 travels between ranks.
  * FP32_PARTIALS: the running partial travels in fp32 and is rounded to
- * bf16 once, at the last hop. */
+ * bf16 once, at the last hop (R > 2; R = 2 has one hop, the same as
+ * PER_HOP).  The context keeps 2 x R x chunk fp32 of scratch for the
+ * partials; a hop then moves 8-10 bytes per element instead of 6. */
 typedef enum { CCR_BF16_ACC_PER_HOP = 0, CCR_BF16_ACC_FP32_PARTIALS = 1 } ccr_bf16_acc_t;
 
 typedef struct {

@@ -67,6 +67,25 @@ def test_reduce_scatter_and_all_gather_bitwise(ccr_mod, ctx, dt, R, n):
     _assert_bitwise(ag, oracle.ring_all_gather(xs, S=2), "all_gather")
 
 
+@pytest.mark.parametrize("R,n", [(2, 1000), (3, 8), (3, 1001), (5, 4099), (8, 65536 + 13), (17, 30011)])
+@pytest.mark.parametrize("S", [1, 3])
+@pytest.mark.parametrize("mode", [dict(), dict(overlap=True), dict(copy_mode="sdma")],
+                         ids=["kernel", "overlap", "sdma"])
+def test_bf16_fp32_partials_bitwise(ccr_mod, ctx, R, n, S, mode):
+    """bf16 with the running partial carried in fp32 and rounded once."""
+    ctx.set_config(ccr_mod.Config(slices=S, bf16_acc="fp32_partials", **mode))
+    xs = workloads.random_buffers(R, n, "bf16", seed=R * 7 + n, dist="normal", scale=1.0)
+    say(f"allreduce bf16 fp32-partials R={R} n={n} S={S} {mode}")
+    got = _run(ccr_mod, ctx, xs)
+    _assert_bitwise(got, oracle.ring_allreduce(xs, S=S, bf16_acc="fp32_partials"), "fp32 partials")
+    rs = _run(ccr_mod, ctx, xs, "reduce_scatter")
+    ref = oracle.ring_reduce_scatter(xs, S=S, bf16_acc="fp32_partials")
+    for c in range(R):  # the owned chunks (the others hold per-hop scratch state)
+        lo, hi = oracle.chunk_bounds(n, R, 8, c)
+        np.testing.assert_array_equal(rs[c][lo:hi], ref[c][lo:hi])
+    ctx.set_config(ccr_mod.Config())
+
+
 MODES = [dict(overlap=True, slices=4), dict(copy_mode="sdma", slices=2),
          dict(copy_mode="sdma", overlap=True, slices=3), dict(cu_budget=64, slices=2),
          dict(cu_budget=16, overlap=True, slices=2, copy_mode="sdma"),
@@ -128,12 +147,10 @@ def test_invalid_arguments(ccr_mod, ctx):
     st = ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 1000, 5, None)
     assert st == ccr_mod.CCR_ERR_INVALID_ARG
     assert ccr_mod._lib.ccr_allreduce(ctx.handle, ptrs, 2, 0, 0, None) == ccr_mod.CCR_OK
-    ctx.set_config(ccr_mod.Config(bf16_acc="fp32_partials"))
-    h = [torch.zeros(64, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-    with pytest.raises(ccr_mod.CcrError) as e:
-        ccr_mod.ccr_allreduce(ctx, h)
-    assert e.value.status == ccr_mod.CCR_ERR_UNSUPPORTED
-    ctx.set_config(ccr_mod.Config())
+    bad = ccr_mod.Config().to_c()
+    bad.slices = 0
+    import ctypes as ct
+    assert ccr_mod._lib.ccr_ctx_set_config(ctx.handle, ct.byref(bad)) == ccr_mod.CCR_ERR_INVALID_ARG
 
 
 # ------------------------------------------------ full-size workloads
@@ -144,7 +161,8 @@ FULL = [(workloads.RING_SMALL_F32, "allreduce"), (workloads.DP_BUCKET_BF16, "all
 @pytest.mark.parametrize("w,how", FULL, ids=[w.name for w, _ in FULL])
 def test_full_size_workloads(ccr_mod, w, how):
     """The benchmark's sizes and launch configuration, compared bit for bit
-    with the oracle's closed-form fold on every element."""
+    with the oracle's closed-form fold on every element (the bf16 bucket also
+    with fp32 partials)."""
     import torch
     say(f"full-size {w.name}: generating inputs")
     xs = workloads.ring_inputs(w)
@@ -170,3 +188,13 @@ def test_full_size_workloads(ccr_mod, w, how):
         err = np.max(np.abs(oracle.bf16_to_f32(ref) - exact)) / np.max(np.abs(exact))
         say(f"{w.name}: normalised max error vs fp64 = {err:.4f}")
         assert err <= 1e-2
+        ref32 = oracle.fold(xs, bf16_acc="fp32_partials")
+        with ccr_mod.Context(0, ccr_mod.Config(slices=w.slices, bf16_acc="fp32_partials")) as c:
+            ts = [to_dev(x) for x in xs]
+            ccr_mod.ccr_allreduce(c, ts)
+            torch.cuda.synchronize()
+            for q, t in enumerate(ts):
+                assert to_host(t).tobytes() == ref32.tobytes(), f"fp32 partials, rank {q}"
+        err32 = np.max(np.abs(oracle.bf16_to_f32(ref32) - exact)) / np.max(np.abs(exact))
+        say(f"{w.name}: fp32 partials normalised max error vs fp64 = {err32:.4f}")
+        assert err32 <= err
