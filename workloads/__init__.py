@@ -148,3 +148,79 @@ def moe_inputs(w: MoeWorkload, tokens: int | None = None, R: int | None = None):
     logits = [draw([w.seed, 1000 + r], T * w.experts, "normal", 1.0).reshape(T, w.experts)
               for r in range(R)]
     return xs, logits
+
+
+# ------------------------------------------------------------- stage schedule
+@dataclass(frozen=True)
+class Topology:
+    """A modelled cluster: `nodes` scale-up domains of `gpus_per_node` GPUs.
+    Bandwidths are integers in bytes per nanosecond (GB/s): one scale-up
+    link, one NIC.  With `paired`, GPUs 2i and 2i+1 of a node are symmetric
+    peers that stage each other's inter-node traffic; otherwise no GPU
+    forwards."""
+    name: str
+    nodes: int
+    gpus_per_node: int
+    bw_scaleup: int
+    bw_rdma: int
+    paired: bool = True
+
+    @property
+    def G(self) -> int:
+        return self.nodes * self.gpus_per_node
+
+    def node(self) -> list[int]:
+        return [u // self.gpus_per_node for u in range(self.G)]
+
+    def peer(self) -> list[int]:
+        return [u ^ 1 for u in range(self.G)] if self.paired else [-1] * self.G
+
+
+# Figure 6 of the HOCCL paper: two nodes of two GPUs, peers 0<->1, 2<->3.
+FIG6_TOPOLOGY = Topology("fig6_2x2", 2, 2, 3, 1)
+# Two nodes of eight MI355X: one xGMI link carries about 153 GB/s per
+# direction, one 400 Gb/s NIC about 50 GB/s.
+MI355X_2X8 = Topology("mi355x_2x8_xgmi153_nic50", 2, 8, 153, 50)
+
+
+@dataclass(frozen=True)
+class ScheduleWorkload:
+    name: str
+    topology: Topology
+    tokens: int
+    hidden: int
+    topk: int
+    skew: float        # Zipf exponent of destination popularity
+    seed: int
+
+
+# Expert-parallel dispatch traffic across 16 GPUs: each GPU sends
+# tokens x topk rows of `hidden` bf16 values, spread over destinations with
+# Zipf-skewed popularity (the long-tail flows of an MoE all-to-all).
+SCHED_MOE_2X8 = ScheduleWorkload("stage_schedule_moe_dispatch_2x8_4096x2048_bf16_top6",
+                                 MI355X_2X8, 4096, 2048, 6, 1.2, 7)
+
+
+def random_traffic(G: int, seed, max_bytes: int, density: float = 0.7) -> list[list[int]]:
+    """A G x G origin traffic matrix of integers in [1, max_bytes] on about
+    `density` of the off-diagonal pairs, zero elsewhere."""
+    rng = np.random.default_rng(seed)
+    vals = rng.integers(1, max_bytes + 1, size=(G, G))
+    keep = rng.random((G, G)) < density
+    return [[int(vals[u, v]) if (keep[u, v] and u != v) else 0 for v in range(G)] for u in range(G)]
+
+
+def moe_traffic(w: ScheduleWorkload) -> list[list[int]]:
+    """Origin traffic matrix (bytes) of one skewed dispatch: source u sends
+    counts[u][v] rows of hidden bf16 values to v, counts multinomial over a
+    Zipf popularity that each source permutes with its own draw."""
+    G = w.topology.G
+    rng = np.random.default_rng([w.seed, 0])
+    base = 1.0 / np.arange(1, G + 1) ** w.skew
+    C = []
+    for u in range(G):
+        p = rng.permutation(base)
+        p = p / p.sum()
+        counts = rng.multinomial(w.tokens * w.topk, p)
+        C.append([int(counts[v]) * w.hidden * 2 if v != u else 0 for v in range(G)])
+    return C
