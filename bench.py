@@ -221,6 +221,38 @@ def workload_timings(ccr, workloads):
     return out
 
 
+def schedule_timings(ccr, workloads):
+    """Stage decomposition (host only) of a skewed expert-parallel dispatch
+    over a modelled two-node, 16-GPU MI355X cluster: the stage count, the
+    modelled time of the schedule (sum of stage times, HOCCL Eq. 11) beside
+    a lower bound that no schedule beats, and the host time per call."""
+    w = workloads.SCHED_MOE_2X8
+    t = w.topology
+    C = np.ascontiguousarray(workloads.moe_traffic(w), np.int64)
+    node = np.array(t.node(), np.int32)
+    peer = np.array(t.peer(), np.int32)
+    entries, times = ccr.ccr_schedule_stages(C, node, peer, t.bw_scaleup, t.bw_rdma)
+    reps = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        ccr.ccr_schedule_stages(C, node, peer, t.bw_scaleup, t.bw_rdma)
+        reps.append(time.perf_counter() - t0)
+    T = ccr.ccr_traffic_matrix(C, node, peer)
+    cross = node[:, None] != node[None, :]
+    # bytes / (GB/s) = ns.  Each GPU moves its inter-node bytes at most one
+    # flow at a time per direction, and a scale-up cell's bytes over one link.
+    rdma_ns = max(np.where(cross, C, 0).sum(axis=1).max(), np.where(cross, C, 0).sum(axis=0).max()) / t.bw_rdma
+    up_ns = np.where(cross, 0, T).max() / t.bw_scaleup
+    model_ns = float(sum(int(l) / int(b) for l, b in times.tolist()))
+    bound_ns = float(max(rdma_ns, up_ns))
+    return {"workload": w.name, "topology": t.name, "gpus": t.G,
+            "flows": int((C > 0).sum()), "stages": int(len(times)),
+            "rdma_stages": int(len(set(entries["stage"][entries["kind"] == 0].tolist()))),
+            "modelled_ms": round(model_ns / 1e6, 4), "lower_bound_ms": round(bound_ns / 1e6, 4),
+            "modelled_over_bound": round(model_ns / bound_ns, 4) if bound_ns else None,
+            "host_us_per_call": round(float(np.median(reps)) * 1e6, 1)}
+
+
 def host_call_us(ccr, call, reps=50):
     """Host time per enqueue (HOCCL Fig. 9 measures CPU launch time per op)."""
     import torch
@@ -383,6 +415,7 @@ def main():
     if not args.no_gemm:
         log("bench: the other workloads (context)")
         others = workload_timings(ccr, workloads)
+        others["stage_schedule"] = schedule_timings(ccr, workloads)
 
     cpu = None
     if not args.no_cpu:

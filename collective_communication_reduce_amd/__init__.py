@@ -51,6 +51,10 @@ class ccr_ring_op_t(ctypes.Structure):
 RING_OP_DTYPE = np.dtype([("phase", np.int32), ("slice", np.int32), ("step", np.int32),
                           ("dst_rank", np.int32), ("src_rank", np.int32), ("chunk", np.int32),
                           ("lo", np.int64), ("hi", np.int64)])
+STAGE_ENTRY_DTYPE = np.dtype([("stage", np.int32), ("kind", np.int32), ("src", np.int32),
+                              ("dst", np.int32), ("bytes", np.int64)])
+STAGE_TIME_DTYPE = np.dtype([("load", np.int64), ("bw", np.int64)])
+STAGE_KINDS = ("rdma", "forward", "native")
 
 # Every exported entry point and its argument types.
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
@@ -61,6 +65,9 @@ _SIGNATURES = {
     "ccr_ctx_set_config": [_vp, ctypes.POINTER(ccr_config_t)],
     "ccr_ctx_get_config": [_vp, ctypes.POINTER(ccr_config_t)],
     "ccr_ring_schedule": [_i32, _i64, _i32, _i32, _i32, _vp, _i64, ctypes.POINTER(_i64)],
+    "ccr_traffic_matrix": [_vp, _i32, _vp, _vp, _vp],
+    "ccr_schedule_stages": [_vp, _i32, _vp, _vp, _i64, _i64, _vp, _i64, ctypes.POINTER(_i64), _vp,
+                            _i64, ctypes.POINTER(_i64)],
     "ccr_allreduce": [_vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_reduce_scatter": [_vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_all_gather": [_vp, _vp, _i32, _i64, _i32, _vp],
@@ -243,6 +250,47 @@ def ccr_ring_schedule(R: int, count: int, slices: int, dtype: int, which: int = 
     _check(_lib.ccr_ring_schedule(R, count, slices, dtype, which,
                                   out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
     return out
+
+
+def _schedule_args(C, node, peer):
+    C = np.ascontiguousarray(C, dtype=np.int64)
+    G = C.shape[0]
+    if C.ndim != 2 or C.shape[1] != G:
+        raise ValueError("C must be a square G x G matrix")
+    node = np.ascontiguousarray(node, dtype=np.int32)
+    peer = np.ascontiguousarray(peer, dtype=np.int32)
+    if node.shape != (G,) or peer.shape != (G,):
+        raise ValueError("node and peer need one entry per GPU")
+    return C, G, node, peer
+
+
+def ccr_traffic_matrix(C, node, peer) -> np.ndarray:
+    """T (G x G int64) from the origin traffic matrix C."""
+    C, G, node, peer = _schedule_args(C, node, peer)
+    T = np.zeros((G, G), np.int64)
+    _check(_lib.ccr_traffic_matrix(C.ctypes.data, G, node.ctypes.data, peer.ctypes.data,
+                                   T.ctypes.data))
+    return T
+
+
+def ccr_schedule_stages(C, node, peer, bw_scaleup: int, bw_rdma: int):
+    """(entries, times): the stage records (STAGE_ENTRY_DTYPE) and each
+    stage's time as load / bw (STAGE_TIME_DTYPE)."""
+    C, G, node, peer = _schedule_args(C, node, peer)
+    ne, ns = ctypes.c_int64(), ctypes.c_int64()
+    args = (C.ctypes.data, G, node.ctypes.data, peer.ctypes.data, bw_scaleup, bw_rdma)
+    # Room for a typical schedule, so that one call usually suffices; call
+    # again with the exact sizes when it does not.
+    cap_s = G * G + 16
+    cap_e = min(cap_s * (3 * G + 8), 1 << 20)
+    while True:
+        entries = np.empty(cap_e, STAGE_ENTRY_DTYPE)
+        times = np.empty(cap_s, STAGE_TIME_DTYPE)
+        _check(_lib.ccr_schedule_stages(*args, entries.ctypes.data, cap_e, ctypes.byref(ne),
+                                        times.ctypes.data, cap_s, ctypes.byref(ns)))
+        if ne.value <= cap_e and ns.value <= cap_s:
+            return entries[:ne.value].copy(), times[:ns.value].copy()
+        cap_e, cap_s = ne.value, ns.value
 
 
 def ccr_allreduce(ctx: Context, bufs: Sequence, stream=None):

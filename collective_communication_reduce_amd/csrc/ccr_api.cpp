@@ -33,6 +33,7 @@
 #include "../../include/ccr.h"
 #include "ccr_dma.h"
 #include "ccr_internal.h"
+#include "ccr_schedule.h"
 
 using namespace ccr;
 
@@ -786,6 +787,53 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
   ring_schedule(R, count, slices, 16 / esize, which, &v);
   *n_ops = (int64_t)v.size();
   if (ops) std::copy(v.begin(), v.begin() + std::min<int64_t>(max_ops, (int64_t)v.size()), ops);
+  return CCR_OK;
+}
+
+ccr_status_t ccr_traffic_matrix(const int64_t* C, int G, const int32_t* node, const int32_t* peer,
+                                int64_t* T) {
+  ScheduleProblem p;
+  p.G = G;
+  p.C = C;
+  p.node = node;
+  p.peer = peer;
+  const std::string bad = check_schedule_problem(p, false);
+  if (!bad.empty()) return fail(CCR_ERR_INVALID_ARG, "%s", bad.c_str());
+  if (!T) return fail(CCR_ERR_INVALID_ARG, "T is NULL");
+  build_traffic_matrix(p, T);
+  return CCR_OK;
+}
+
+ccr_status_t ccr_schedule_stages(const int64_t* C, int G, const int32_t* node, const int32_t* peer,
+                                 int64_t bw_scaleup, int64_t bw_rdma, ccr_stage_entry_t* entries,
+                                 int64_t max_entries, int64_t* n_entries, ccr_stage_time_t* times,
+                                 int64_t max_stages, int64_t* n_stages) {
+  ScheduleProblem p;
+  p.G = G;
+  p.C = C;
+  p.node = node;
+  p.peer = peer;
+  p.bw_scaleup = bw_scaleup;
+  p.bw_rdma = bw_rdma;
+  const std::string bad = check_schedule_problem(p, true);
+  if (!bad.empty()) return fail(CCR_ERR_INVALID_ARG, "%s", bad.c_str());
+  if (!n_entries || !n_stages) return fail(CCR_ERR_INVALID_ARG, "n_entries or n_stages is NULL");
+  if (max_entries < 0 || max_stages < 0) return fail(CCR_ERR_INVALID_ARG, "negative maximum");
+  std::vector<StageEntry> e;
+  std::vector<StageTime> t;
+  decompose_stages(p, &e, &t);
+  *n_entries = (int64_t)e.size();
+  *n_stages = (int64_t)t.size();
+  if (entries) {
+    const int64_t n = std::min<int64_t>(max_entries, (int64_t)e.size());
+    for (int64_t i = 0; i < n; i++)
+      entries[i] = {e[(size_t)i].stage, e[(size_t)i].kind, e[(size_t)i].src, e[(size_t)i].dst,
+                    e[(size_t)i].bytes};
+  }
+  if (times) {
+    const int64_t n = std::min<int64_t>(max_stages, (int64_t)t.size());
+    for (int64_t i = 0; i < n; i++) times[i] = {t[(size_t)i].load, t[(size_t)i].bw};
+  }
   return CCR_OK;
 }
 

@@ -148,6 +148,59 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
                                ccr_ring_op_t *ops, int64_t max_ops, int64_t *n_ops);
 
 /* ----------------------------------------------------------------------
+ * Stage schedule of a collective's traffic (host only, no device work).
+ *
+ * HOCCL §3.4 (Collective Scheduler, Figure 6).  A collective over G GPUs is
+ * an origin traffic matrix C: C[u*G + v] = bytes GPU u sends to GPU v
+ * (int64, >= 0, at most 2^40; the diagonal is ignored).  node[u] (>= 0)
+ * names u's scale-up domain; flows between nodes go over RDMA.  peer[u] is
+ * u's symmetric peer in the same node (Figure 6 pairs 0-1 and 2-3), or -1
+ * for none: an inter-node flow u -> v is sent as a forwarding copy on the
+ * scale-up edge (u, peer[u]), the RDMA transfer, and a forwarding copy on
+ * (peer[v], v) (Eq. 2).  1 <= G <= 256.  All arrays are host memory, read
+ * during the call only.
+ *
+ * ccr_traffic_matrix: T = C with the forwarding copies added, T[u][peer u]
+ *   = C[u][peer u] + (u's inter-node bytes) + (peer u's incoming inter-node
+ *   bytes), T = C elsewhere, diagonal 0 (Eq. 3-5).  T: G*G int64.
+ * ccr_schedule_stages: Algorithm 1 (Birkhoff-like decomposition).  Each
+ *   stage takes a greedy matching of the inter-node flows with bytes left
+ *   (by decreasing remainder, ties by (src, dst); at most one outgoing and
+ *   one incoming per GPU, Eq. 8), moves the least remainder x on every
+ *   matched flow, adds its forwarding copies, and fills the scale-up edges
+ *   up to max(floor(x * bw_scaleup / bw_rdma), the largest forwarding load)
+ *   with native components, which are greedy matchings peeled off each
+ *   node's native traffic beforehand.  Native traffic left over forms
+ *   further stages.  The stages sum to T (Eq. 7).  Bandwidths are integers
+ *   in [1, 2^20] (any common unit, e.g. GB/s).
+ *   entries: one record per (stage, kind, src, dst) with bytes > 0, sorted
+ *   by those keys; kind 0 = RDMA flow, 1 = forwarding copy, 2 = native
+ *   scale-up flow.  times[s]: the stage time of Eq. 9-10 as the exact ratio
+ *   load / bw of the slowest domain.  At most max_entries / max_stages
+ *   records are written; *n_entries and *n_stages receive the full counts
+ *   (query them with NULL arrays and zero maxima).
+ * Errors: CCR_ERR_INVALID_ARG for NULL arrays, G out of range, negative or
+ * oversized bytes, a node id < 0, or a peer that is not -1 or another GPU of
+ * the same node.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t stage, kind, src, dst;
+    int64_t bytes;
+} ccr_stage_entry_t;
+
+typedef struct {
+    int64_t load, bw;
+} ccr_stage_time_t;
+
+ccr_status_t ccr_traffic_matrix(const int64_t *C, int G, const int32_t *node,
+                                const int32_t *peer, int64_t *T);
+ccr_status_t ccr_schedule_stages(const int64_t *C, int G, const int32_t *node,
+                                 const int32_t *peer, int64_t bw_scaleup, int64_t bw_rdma,
+                                 ccr_stage_entry_t *entries, int64_t max_entries,
+                                 int64_t *n_entries, ccr_stage_time_t *times,
+                                 int64_t max_stages, int64_t *n_stages);
+
+/* ----------------------------------------------------------------------
  * Ring collectives, in place over R virtual ranks.
  * bufs: host array of R device pointers, each to `count` elements of dtype;
  * the R buffers must not overlap.  1 <= R <= 64.

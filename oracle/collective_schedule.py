@@ -22,16 +22,17 @@ GPU Cores to Accelerate Distributed Training", §3.4 Collective Scheduler
   tau^s    max_d L^s_d / B_d (Eq. 10); the schedule's cost is sum_s tau^s (Eq. 11)
 
 Where Algorithm 1 leaves a step open, these readings are taken:
-  (a) a "matching" (lines 2 and 5) is built greedily: entries with traffic
+  (a) a matching (of the native components, and the contention-free RDMA
+      set of each stage) is built greedily: entries with traffic
       left, by decreasing residual, ties by (u, v); an entry joins when its
       sender has no outgoing and its receiver no incoming entry yet.  Native
       scale-up traffic is decomposed node by node.
-  (b) "the largest removable portion" (line 6) is the smallest residual over
+  (b) the largest portion a stage can remove is the smallest residual over
       the matching, the Birkhoff-von Neumann coefficient: every matched entry
       moves that much, so at least one of them empties.
-  (c) forwarding copies (line 7): a moved portion x of u -> v adds x on (u, ū)
+  (c) forwarding copies: a moved portion x of u -> v adds x on (u, ū)
       and x on (v̄, v).
-  (d) "NVLink slack" (line 8): with the stage lasting at least x / B_rdma,
+  (d) scale-up slack: with the stage lasting at least x / B_rdma,
       every scale-up edge may carry cap = max(floor(x * B_nv / B_rdma), the
       largest forwarding load of the stage); native components, node by node
       and in decomposition order, each move min(what is left, the least room
@@ -79,7 +80,7 @@ def greedy_matching(resid):
 
 
 def native_components(C, node):
-    """Algorithm 1, line 2: per node, matchings peeled off the native traffic.
+    """Algorithm 1, first step: per node, matchings peeled off the native traffic.
     Returns {node: [[pairs, bytes], ...]} in decomposition order."""
     G = len(C)
     comps = {}
@@ -106,19 +107,19 @@ def decompose(C, node, peer, bw_nv, bw_rdma):
     (kind, u, v, bytes), "tau": (bytes, bandwidth)} where tau^s equals
     bytes / bandwidth of the stage's slowest domain (Eq. 9, 10)."""
     G = len(C)
-    comps = native_components(C, node)                       # line 2
+    comps = native_components(C, node)
     resid = {(u, v): C[u][v] for u in range(G) for v in range(G)
-             if node[u] != node[v] and C[u][v] > 0}          # line 1 (RDMA part of R)
+             if node[u] != node[v] and C[u][v] > 0}          # RDMA part of the residual
     stages = []
-    while any(resid.values()):                               # line 3
-        st = {}                                              # line 4
-        m = greedy_matching(resid)                           # line 5
-        x = min(resid[p] for p in m)                         # line 6
+    while any(resid.values()):
+        st = {}
+        m = greedy_matching(resid)                           # reading (a)
+        x = min(resid[p] for p in m)                         # reading (b)
         load = {}
         for u, v in m:
             resid[(u, v)] -= x
             _add(st, RDMA, u, v, x)
-        for u, v in m:                                       # line 7
+        for u, v in m:                                       # reading (c)
             if peer[u] >= 0:
                 _add(st, FWD, u, peer[u], x)
                 load[(u, peer[u])] = load.get((u, peer[u]), 0) + x
@@ -126,7 +127,7 @@ def decompose(C, node, peer, bw_nv, bw_rdma):
                 _add(st, FWD, peer[v], v, x)
                 load[(peer[v], v)] = load.get((peer[v], v), 0) + x
         cap = max(x * bw_nv // bw_rdma, max(load.values(), default=0))
-        for n in sorted(comps):                              # line 8
+        for n in sorted(comps):                              # reading (d)
             for comp in comps[n]:
                 pairs, left = comp
                 if left == 0:
@@ -137,7 +138,7 @@ def decompose(C, node, peer, bw_nv, bw_rdma):
                         _add(st, NATIVE, u, v, amount)
                         load[(u, v)] = load.get((u, v), 0) + amount
                     comp[1] -= amount
-        stages.append(st)                                    # line 9
+        stages.append(st)
     while True:                                              # reading (e)
         st = {}
         for n in sorted(comps):
