@@ -217,6 +217,18 @@ def workload_timings(ccr, workloads):
         res[mode] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
                      "dispatch_algorithmic_gbs": round(3 * 2 * moved / (d_ms * 1e-3) / 1e9, 1),
                      "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
+    with ccr.Context(0) as ctx:
+        d_ms = median_ms(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp), 10)
+        c_ms = median_ms(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb), 10)
+        ccr.ccr_profile_enable(ctx, True)
+        ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp)
+        g = ccr.ccr_profile_read(ctx, "moe_gather")
+        ccr.ccr_profile_enable(ctx, False)
+    # one gather: every row read once and written once
+    res["fused"] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
+                    "dispatch_algorithmic_gbs": round(2 * moved / (d_ms * 1e-3) / 1e9, 1),
+                    "gather_kernel_gbs": round(g["bytes"] / (g["ms"] * 1e-3) / 1e9, 1) if g["ms"] else None,
+                    "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
     out[m.name] = res
     return out
 

@@ -78,6 +78,8 @@ _SIGNATURES = {
     "ccr_moe_plan": [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp],
     "ccr_moe_dispatch": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp],
     "ccr_moe_combine": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp],
+    "ccr_moe_dispatch_fused": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp],
+    "ccr_moe_combine_fused": [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _vp, _vp],
     "ccr_last_error": [],
     "ccr_version": [],
     "ccr_probe_cu_ids": [_vp, _vp, _i32, _vp],
@@ -354,7 +356,7 @@ def ccr_moe_dispatch(ctx: Context, x: Sequence, src_tok: Sequence, ecnt, K: int,
                      send: Sequence, recv: Sequence, exp: Sequence, stream=None):
     R = len(x)
     T = x[0].shape[0]
-    row_bytes = x[0][0].numel() * x[0].element_size()
+    row_bytes = x[0].shape[-1] * x[0].element_size()
     ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
     _check(_lib.ccr_moe_dispatch(ctx.handle, _ptrs(x), _ptrs(src_tok), ecnt.ctypes.data, R, T,
                                  ecnt.shape[1], K, row_bytes, _ptrs(send), _ptrs(recv),
@@ -364,11 +366,30 @@ def ccr_moe_dispatch(ctx: Context, x: Sequence, src_tok: Sequence, ecnt, K: int,
 def ccr_moe_combine(ctx: Context, exp: Sequence, slot: Sequence, ecnt, T: int, K: int,
                     recv: Sequence, send: Sequence, out: Sequence, stream=None):
     R = len(exp)
-    row_bytes = exp[0][0].numel() * exp[0].element_size()
+    row_bytes = exp[0].shape[-1] * exp[0].element_size()
     ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
     _check(_lib.ccr_moe_combine(ctx.handle, _ptrs(exp), _ptrs(slot), ecnt.ctypes.data, R, T,
                                 ecnt.shape[1], K, row_bytes, _ptrs(recv), _ptrs(send),
                                 _ptrs(out), _stream(stream)))
+
+
+def ccr_moe_dispatch_fused(ctx: Context, x: Sequence, src_tok: Sequence, ecnt, K: int,
+                           exp: Sequence, stream=None):
+    R = len(x)
+    T = x[0].shape[0]
+    row_bytes = x[0].shape[-1] * x[0].element_size()
+    ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
+    _check(_lib.ccr_moe_dispatch_fused(ctx.handle, _ptrs(x), _ptrs(src_tok), ecnt.ctypes.data, R,
+                                       T, ecnt.shape[1], K, row_bytes, _ptrs(exp), _stream(stream)))
+
+
+def ccr_moe_combine_fused(ctx: Context, exp: Sequence, slot: Sequence, ecnt, T: int, K: int,
+                          out: Sequence, stream=None):
+    R = len(exp)
+    row_bytes = out[0].shape[-1] * out[0].element_size()
+    ecnt = np.ascontiguousarray(ecnt, dtype=np.int64)
+    _check(_lib.ccr_moe_combine_fused(ctx.handle, _ptrs(exp), _ptrs(slot), ecnt.ctypes.data, R, T,
+                                      ecnt.shape[1], K, row_bytes, _ptrs(out), _stream(stream)))
 
 
 def ccr_probe_cu_ids(ctx: Context, nblocks: int, stream=None):
@@ -383,7 +404,7 @@ class ccr_kernel_stats_t(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("bytes", ctypes.c_int64), ("ms", ctypes.c_double)]
 
 
-PROFILE_KINDS = {"reduce": 0, "copy_kernel": 1, "sdma": 2, "reduce_forward": 3}
+PROFILE_KINDS = {"reduce": 0, "copy_kernel": 1, "sdma": 2, "reduce_forward": 3, "moe_gather": 4}
 
 
 def ccr_profile_enable(ctx: Context, on: bool = True):

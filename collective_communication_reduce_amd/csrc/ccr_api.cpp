@@ -98,6 +98,18 @@ struct ccr_ctx {
   int64_t* h_pinned = nullptr;  // pinned mirror of d_ecnt
   float* partials = nullptr;    // fp32 partials: 2 (hop parity) x R x chunk
   int64_t partials_bytes = 0;
+  // Small per-call tables (fused MoE segment tables) go to the device
+  // through a ring of pinned host / device buffer pairs; a slot is reused
+  // only after the work of its previous call has completed.
+  struct TableSlot {
+    char* dev = nullptr;
+    char* host = nullptr;
+    int64_t cap = 0;
+    hipEvent_t done = nullptr;
+  };
+  static constexpr int kTableSlots = 4;
+  TableSlot tables[kTableSlots];
+  int next_table = 0;
   // per-launch timing (ccr_profile_enable): event pairs and payload bytes
   bool prof_on = false;
   struct Timed {
@@ -300,7 +312,7 @@ LaunchTuning tuning() {
   return t;
 }
 
-enum { kProfReduce = 0, kProfCopyKernel = 1, kProfSdma = 2, kProfReduceFwd = 3 };
+enum { kProfReduce = 0, kProfCopyKernel = 1, kProfSdma = 2, kProfReduceFwd = 3, kProfGather = 4 };
 
 ccr_status_t timing_event(ccr_ctx* ctx, hipEvent_t* e) {
   if (!ctx->timing_pool.empty()) {
@@ -517,7 +529,7 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   CCR_TRY(check_disjoint(ranges, "bufs"));
   if (R == 1) return CCR_OK;
 
-  const int V = 16 / esize, S = ctx->cfg.slices;
+  const int V = 16 / esize;
   const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
   const HopKind reduce_fwd = dtype == CCR_F32 ? HopKind::kReduceFwdF32 : HopKind::kReduceFwdBf16;
   // With compute-unit copies, an all-reduce's last reduce-scatter hop also
@@ -541,6 +553,13 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   // going while the engines copy.
   const bool sdma = ctx->cfg.copy_mode == CCR_COPY_SDMA && which != kWhichRS;
   if (sdma) CCR_TRY(ensure_dma(ctx));
+  // Slices exist so that one slice's all-gather can run while the next
+  // slice's reduce-scatter does.  When nothing runs beside them (a single
+  // phase, or both phases on one stream), the slices of a hop are adjacent
+  // ranges of each chunk and run as one launch over whole chunks: every
+  // element sees the same operations in the same order.
+  const bool pipelined = which == kWhichAllreduce && (ctx->cfg.overlap || sdma);
+  const int S = pipelined ? ctx->cfg.slices : 1;
   hipStream_t rs = ctx->masked ? ctx->s_a : caller;
   hipStream_t ag = (ctx->cfg.overlap || sdma) ? ctx->s_b : rs;
   const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
@@ -752,6 +771,12 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   if (ctx->d_ecnt) (void)hipFree(ctx->d_ecnt);
   if (ctx->partials) (void)hipFree(ctx->partials);
   if (ctx->h_pinned) (void)hipHostFree(ctx->h_pinned);
+  for (auto& t : ctx->tables) {
+    if (t.done) (void)hipEventSynchronize(t.done);
+    if (t.dev) (void)hipFree(t.dev);
+    if (t.host) (void)hipHostFree(t.host);
+    if (t.done) (void)hipEventDestroy(t.done);
+  }
   delete ctx;
   return st;
 }
@@ -1174,6 +1199,147 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   return CCR_OK;
 }
 
+namespace {
+
+// Copy `bytes` of host data to a device table for work about to be enqueued
+// on `s`; the caller records the slot's `done` event on `s` after that work.
+ccr_status_t upload_table(ccr_ctx* ctx, const void* data, int64_t bytes, hipStream_t s,
+                          ccr_ctx::TableSlot** slot) {
+  ccr_ctx::TableSlot& t = ctx->tables[ctx->next_table];
+  ctx->next_table = (ctx->next_table + 1) % ccr_ctx::kTableSlots;
+  if (!t.done) HIP_TRY(hipEventCreateWithFlags(&t.done, hipEventDisableTiming));
+  HIP_TRY(hipEventSynchronize(t.done));  // the slot's previous call is done with it
+  if (t.cap < bytes) {
+    if (t.dev) HIP_TRY(hipFree(t.dev));
+    if (t.host) HIP_TRY(hipHostFree(t.host));
+    t.dev = t.host = nullptr;
+    t.cap = 0;
+    const int64_t cap = std::max<int64_t>(bytes, 64 << 10);
+    HIP_TRY(hipMalloc(reinterpret_cast<void**>(&t.dev), (size_t)cap));
+    HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&t.host), (size_t)cap, hipHostMallocDefault));
+    t.cap = cap;
+  }
+  memcpy(t.host, data, (size_t)bytes);
+  HIP_TRY(hipMemcpyAsync(t.dev, t.host, (size_t)bytes, hipMemcpyHostToDevice, s));
+  *slot = &t;
+  return CCR_OK;
+}
+
+// One gather per row between each source rank's rows and the expert-major
+// buffers, with the placement of the three-stage path: for destination d,
+// local expert l, source r, r's rows for expert d*eloc + l, in pack order.
+ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int64_t* h_ecnt,
+                        void* const* own, const int32_t* const* idx, void* const* exp,
+                        hipStream_t caller) {
+  const int R = m.R, E = m.E, eloc = m.eloc;
+  const int64_t rows = m.T * m.K;
+  // table: R MoeRank records, then R*E MoeSeg records
+  std::vector<char> tab(sizeof(MoeRank) * (size_t)R + sizeof(MoeSeg) * (size_t)R * E);
+  MoeRank* rk = reinterpret_cast<MoeRank*>(tab.data());
+  MoeSeg* sg = reinterpret_cast<MoeSeg*>(tab.data() + sizeof(MoeRank) * (size_t)R);
+  for (int r = 0; r < R; r++) {
+    rk[r] = MoeRank{static_cast<char*>(own[r]), idx[r]};
+    int64_t start = 0;  // pack position of r's first row for expert e
+    for (int e = 0; e < E; e++) {
+      sg[(size_t)r * E + e] = MoeSeg{start, 0, static_cast<char*>(exp[e / eloc])};
+      start += h_ecnt[(size_t)r * E + e];
+    }
+  }
+  for (int d = 0; d < R; d++) {  // exp[d] holds (local expert, source rank) blocks in order
+    int64_t row = 0;
+    for (int l = 0; l < eloc; l++)
+      for (int r = 0; r < R; r++) {
+        const int e = d * eloc + l;
+        sg[(size_t)r * E + e].exp_row = row;
+        row += h_ecnt[(size_t)r * E + e];
+      }
+  }
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  ccr_ctx::TableSlot* slot = nullptr;
+  CCR_TRY(upload_table(ctx, tab.data(), (int64_t)tab.size(), s, &slot));
+  const MoeRank* d_rk = reinterpret_cast<const MoeRank*>(slot->dev);
+  const MoeSeg* d_sg = reinterpret_cast<const MoeSeg*>(slot->dev + sizeof(MoeRank) * (size_t)R);
+  const int64_t limit = combine ? rows : m.T;
+  if (ctx->prof_on) {
+    hipEvent_t start, stop;
+    CCR_TRY(timing_event(ctx, &start));
+    CCR_TRY(timing_event(ctx, &stop));
+    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s, start, stop));
+    ctx->timed.push_back(ccr_ctx::Timed{kProfGather, start, stop, 2 * R * rows * m.row_bytes});
+  } else {
+    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s));
+  }
+  HIP_TRY(hipEventRecord(slot->done, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
+  return CCR_OK;
+}
+
+// No buffer the gather writes may overlap any other buffer of the call
+// (read-only buffers may overlap each other).  written_exp: the expert-major
+// buffers are the ones written (dispatch), else the per-rank rows are.
+ccr_status_t check_moe_disjoint(const MoeShape& m, void* const* own, int64_t own_bytes,
+                                void* const* exp, const int64_t* exp_bytes, bool written_exp) {
+  struct B {
+    uintptr_t lo, hi;
+    bool written;
+    const char* what;
+    int rank;
+  };
+  std::vector<B> b;
+  for (int i = 0; i < m.R; i++) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(own[i]);
+    b.push_back(B{a, a + (uintptr_t)own_bytes, !written_exp, written_exp ? "x" : "out", i});
+    const uintptr_t e = reinterpret_cast<uintptr_t>(exp[i]);
+    if (exp_bytes[i] > 0) b.push_back(B{e, e + (uintptr_t)exp_bytes[i], written_exp, "exp", i});
+  }
+  for (size_t i = 0; i < b.size(); i++)
+    for (size_t j = i + 1; j < b.size(); j++)
+      if ((b[i].written || b[j].written) && b[i].lo < b[j].hi && b[j].lo < b[i].hi)
+        return fail(CCR_ERR_INVALID_ARG, "%s[%d] and %s[%d] overlap", b[i].what, b[i].rank,
+                    b[j].what, b[j].rank);
+  return CCR_OK;
+}
+
+}  // namespace
+
+ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void* const* x,
+                                    const int32_t* const* src_tok, const int64_t* h_ecnt, int R,
+                                    int64_t T, int E, int K, int64_t row_bytes, void* const* exp,
+                                    void* stream) {
+  MoeShape m;
+  CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
+  if (T == 0) return CCR_OK;
+  const int64_t xb = T * row_bytes, ib = T * K * 4;
+  std::vector<int64_t> rb((size_t)R, 0);
+  for (int d = 0; d < R; d++)
+    for (int r = 0; r < R; r++) rb[(size_t)d] += m.cnt[(size_t)r * R + d] * row_bytes;
+  CCR_TRY(check_rank_ptrs(ctx, x, R, &xb, false, "x"));
+  CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(src_tok), R, &ib, false, "src_tok"));
+  CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
+  CCR_TRY(check_moe_disjoint(m, const_cast<void* const*>(x), xb, exp, rb.data(), true));
+  return moe_gather(ctx, 0, m, h_ecnt, const_cast<void* const*>(x), src_tok, exp,
+                    static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_moe_combine_fused(ccr_ctx_t ctx, const void* const* exp, const int32_t* const* slot,
+                                   const int64_t* h_ecnt, int R, int64_t T, int E, int K,
+                                   int64_t row_bytes, void* const* out, void* stream) {
+  MoeShape m;
+  CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
+  if (T == 0) return CCR_OK;
+  const int64_t ob = T * K * row_bytes, ib = T * K * 4;
+  std::vector<int64_t> rb((size_t)R, 0);
+  for (int d = 0; d < R; d++)
+    for (int r = 0; r < R; r++) rb[(size_t)d] += m.cnt[(size_t)r * R + d] * row_bytes;
+  CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
+  CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(slot), R, &ib, false, "slot"));
+  CCR_TRY(check_rank_ptrs(ctx, out, R, &ob, false, "out"));
+  CCR_TRY(check_moe_disjoint(m, out, ob, const_cast<void* const*>(exp), rb.data(), false));
+  return moe_gather(ctx, 1, m, h_ecnt, out, slot, const_cast<void* const*>(exp),
+                    static_cast<hipStream_t>(stream));
+}
+
 ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on) {
   CCR_TRY(check_ctx(ctx));
   HIP_TRY(hipDeviceSynchronize());
@@ -1249,7 +1415,7 @@ ccr_status_t ccr_dma_hold_finish(ccr_ctx_t ctx, int us) {
 
 ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t* out) {
   CCR_TRY(check_ctx(ctx));
-  if (!out || kind < 0 || kind > 3) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 3]");
+  if (!out || kind < 0 || kind > 4) return fail(CCR_ERR_INVALID_ARG, "out is NULL or kind outside [0, 4]");
   HIP_TRY(hipDeviceSynchronize());
   ccr_kernel_stats_t st{0, 0, 0.0};
   if (kind == kProfSdma) {

@@ -72,6 +72,29 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
 
 // dst row i = src row idx[i] for i < nrows; rows of row_bytes (multiple of
 // 16); entries outside [0, nsrc) are skipped.
+// Fused MoE dispatch / combine (one gather per row).  Per source rank r:
+// `rows` is x[r] (dispatch) or out[r] (combine) and `idx` is src_tok[r]
+// (pack position -> token) or slot[r] ((t, k) -> pack position).  Per
+// (r, expert e): the pack position where e's rows start, and where they sit
+// in the destination's expert-major buffer `exp` (row exp_row onwards).
+struct MoeRank {
+  char* rows;
+  const int32_t* idx;
+};
+struct MoeSeg {
+  int64_t pack_start;
+  int64_t exp_row;
+  char* exp;
+};
+// ranks: device [R]; segs: device [R * E], pack_start increasing in e with
+// pack_start[r][0] = 0.  rows_per_rank = T * K.  combine = 0: exp row of
+// pack position p <- x row idx[p] (idx < T); combine = 1: out row q <- exp
+// row of pack position idx[q] (idx < T * K).  Out-of-range indices skip the
+// row.
+hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
+                             int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
+                             hipStream_t stream, hipEvent_t start = nullptr,
+                             hipEvent_t stop = nullptr);
 hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,
                                int64_t nsrc, int64_t row_bytes, hipStream_t stream);
 

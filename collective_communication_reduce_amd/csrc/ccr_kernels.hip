@@ -15,6 +15,8 @@
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <cstdlib>
 #include <stdint.h>
 
 #include "ccr_internal.h"
@@ -329,6 +331,69 @@ __global__ __launch_bounds__(kBlock) void permute_rows_kernel(u32x4* dst, const 
   }
 }
 
+// ------------------------------------------------------- fused MoE gather
+// One workgroup moves RPB consecutive rows of one source rank's T*K rows.
+// Lane j of the first wave resolves row j (its index, then the expert whose
+// segment holds the pack position, by binary search over the segment
+// starts) and leaves the row's source and destination in LDS, so the RPB
+// lookups run side by side; then every thread moves 16-byte column c of
+// all RPB rows, loads first.  The expert of a pack position is the last
+// expert whose segment starts at or before it (an empty segment shares its
+// start with the next one, so the search lands on the segment that holds
+// the position).
+template <int RPB>
+__global__ __launch_bounds__(kBlock) void moe_gather_kernel(const MoeRank* ranks,
+                                                            const MoeSeg* segs, int E,
+                                                            int64_t rows, int64_t idx_limit,
+                                                            int64_t vpr, int64_t blocks_per_rank,
+                                                            int combine) {
+  static_assert(RPB <= 64, "one lane per row of the first wave");
+  __shared__ const u32x4* s_from[RPB];
+  __shared__ u32x4* s_to[RPB];
+  const int64_t r = blockIdx.x / blocks_per_rank;
+  const int64_t q0 = (int64_t)(blockIdx.x % blocks_per_rank) * RPB;
+  if (threadIdx.x < RPB) {
+    const MoeRank rk = ranks[r];
+    const MoeSeg* sg = segs + r * E;
+    const int64_t q = q0 + threadIdx.x;
+    const u32x4* from = nullptr;
+    u32x4* to = nullptr;
+    const int64_t i = q < rows ? (int64_t)rk.idx[q] : -1;
+    if (i >= 0 && i < idx_limit) {
+      const int64_t pos = combine ? i : q;  // pack position
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sg[mid].pack_start <= pos) lo = mid; else hi = mid - 1;
+      }
+      const MoeSeg g = sg[lo];
+      u32x4* e = reinterpret_cast<u32x4*>(g.exp) + (g.exp_row + (pos - g.pack_start)) * vpr;
+      u32x4* own = reinterpret_cast<u32x4*>(rk.rows) + (combine ? q : i) * vpr;
+      from = combine ? e : own;
+      to = combine ? own : e;
+    }
+    s_from[threadIdx.x] = from;
+    s_to[threadIdx.x] = to;
+  }
+  __syncthreads();
+  const u32x4* from[RPB];
+  u32x4* to[RPB];
+#pragma unroll
+  for (int j = 0; j < RPB; j++) {
+    from[j] = s_from[j];
+    to[j] = s_to[j];
+  }
+  for (int64_t c = threadIdx.x; c < vpr; c += kBlock) {
+    u32x4 v[RPB];
+#pragma unroll
+    for (int j = 0; j < RPB; j++)
+      if (from[j]) v[j] = from[j][c];
+#pragma unroll
+    for (int j = 0; j < RPB; j++)
+      if (to[j]) to[j][c] = v[j];
+  }
+}
+
 // ------------------------------------------------------------------- topk
 // One wave per token: lane l holds the logits of experts l, l+64, ...
 // Each of the K rounds takes the largest remaining logit (lowest expert id
@@ -528,6 +593,46 @@ hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, i
       reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), idx, nrows, nsrc,
       row_bytes >> 4);
   return hipGetLastError();
+}
+
+template <int RPB>
+hipError_t launch_gather_rpb(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
+                             int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int64_t per_rank = (rows_per_rank + RPB - 1) / RPB;
+  const int64_t grid = per_rank * R;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (start && stop)
+    hipExtLaunchKernelGGL(moe_gather_kernel<RPB>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                          start, stop, 0, ranks, segs, E, rows_per_rank, idx_limit, row_bytes >> 4,
+                          per_rank, combine);
+  else
+    moe_gather_kernel<RPB><<<(unsigned)grid, kBlock, 0, stream>>>(
+        ranks, segs, E, rows_per_rank, idx_limit, row_bytes >> 4, per_rank, combine);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
+                             int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
+                             hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (R <= 0 || E <= 0 || rows_per_rank <= 0 || row_bytes <= 0) return hipSuccess;
+  // rows per workgroup: overridable for tuning sweeps
+  static const int rpb = [] {
+    const char* e = getenv("CCR_GATHER_RPB");
+    const int v = e ? atoi(e) : 8;
+    return (v == 4 || v == 16) ? v : 8;
+  }();
+  switch (rpb) {
+    case 4:
+      return launch_gather_rpb<4>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
+                                  stream, start, stop);
+    case 16:
+      return launch_gather_rpb<16>(combine, ranks, segs, R, E, rows_per_rank, idx_limit,
+                                   row_bytes, stream, start, stop);
+    default:
+      return launch_gather_rpb<8>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
+                                  stream, start, stop);
+  }
 }
 
 hipError_t launch_moe_topk(const float* logits, int32_t* topk, int64_t T, int E, int K,

@@ -87,7 +87,11 @@ typedef enum { CCR_BF16_ACC_PER_HOP = 0, CCR_BF16_ACC_FP32_PARTIALS = 1 } ccr_bf
 typedef struct {
     int32_t copy_mode;           /* ccr_copy_mode_t                                 */
     int32_t cu_budget;           /* compute units the collective may use; 0 = all   */
-    int32_t slices;              /* S >= 1 pipeline slices per ring chunk           */
+    int32_t slices;              /* S >= 1 pipeline slices per ring chunk; they
+                                    run separately only in an all-reduce whose
+                                    all-gather overlaps (overlap = 1 or SDMA
+                                    copies); otherwise a hop's slices run as one
+                                    launch, with the same per-element order     */
     int32_t overlap;             /* 1: all-gather of slice s runs on a second stream
                                     while reduce-scatter continues with slice s+1   */
     int64_t staging_chunk_bytes; /* P2P staging chunk (multiple of 16)              */
@@ -246,7 +250,7 @@ ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void *const *send, void *const *r
 
 /* dst row i = src row d_idx[i], for i < nrows.  d_idx: device int32, each
  * entry in [0, nsrc); an out-of-range entry leaves that dst row unwritten
- * and is reported by the next ccr_permute_rows_check() call. */
+ * (the indices live on the device, so no error is returned for it). */
 ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void *dst, const void *src, const int32_t *d_idx,
                               int64_t nrows, int64_t nsrc, int64_t row_bytes, void *stream);
 
@@ -286,6 +290,29 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void *const *exp, const int32_
                              const int64_t *h_ecnt, int R, int64_t T, int E, int K,
                              int64_t row_bytes, void *const *recv, void *const *send,
                              void *const *out, void *stream);
+
+/* Fused variants: the same results without the packed send or receive
+ * buffers.  Each row moves once, directly between x[r] (or out[r]) and its
+ * place in the destination's expert-major buffer exp[d] -- the pack, the
+ * exchange and the unpack in one gather on the compute units (a one-GPU
+ * stand-in for writing each row straight into the peer's receive buffer,
+ * HOCCL §3.3.2's direct path).  2 bytes of traffic per payload byte instead
+ * of 6.  exp[d] holds the same rows in the same order as ccr_moe_dispatch
+ * gives; ccr_moe_combine_fused's out equals ccr_moe_combine's.  The copy mode
+ * does not apply (row gathers run on compute units).  A buffer the call
+ * writes (exp for dispatch, out for combine) must not overlap any other
+ * buffer of the call.  The segment table (R records of 16 bytes and R*E of
+ * 24) is copied to the device on `stream`.  Arguments and errors as for
+ * ccr_moe_dispatch / ccr_moe_combine; indices out of range leave their row
+ * unwritten. */
+ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void *const *x,
+                                    const int32_t *const *src_tok, const int64_t *h_ecnt, int R,
+                                    int64_t T, int E, int K, int64_t row_bytes, void *const *exp,
+                                    void *stream);
+ccr_status_t ccr_moe_combine_fused(ccr_ctx_t ctx, const void *const *exp,
+                                   const int32_t *const *slot, const int64_t *h_ecnt, int R,
+                                   int64_t T, int E, int K, int64_t row_bytes, void *const *out,
+                                   void *stream);
 
 /* ----------------------------------------------------------------------
  * Diagnostics.
@@ -331,7 +358,8 @@ ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *st
  * synchronises the context's streams and the device, then reports, for
  * `kind` (0 = reduce kernels, 1 = copy kernels, 2 = SDMA copies,
  * 3 = reduce-and-forward kernels, the last reduce-scatter hop of an
- * all-reduce with kernel copies), the number of launches since the last
+ * all-reduce with kernel copies, 4 = fused MoE gathers, 2 bytes per byte of
+ * payload), the number of launches since the last
  * enable, the sum of their durations in milliseconds, and their algorithmic
  * bytes (a reduce moves 3 bytes per byte of payload: read local, read
  * incoming, write local; reduce-and-forward 4; a copy 2).  Kernel launches

@@ -89,3 +89,106 @@ def test_dispatch_combine_full_size(ccr_mod, mode):
     """8 ranks x 4096 tokens x 2048 hidden bf16, 64 experts, top-6."""
     w = workloads.MOE_DISPATCH_BF16
     _dispatch_case(ccr_mod, w.R, w.tokens, w.experts, w.topk, w.hidden, mode)
+
+
+def _plan(ccr_mod, c, logits, E, K, R):
+    import torch
+    T = logits[0].shape[0]
+    topk = [torch.zeros(T, K, dtype=torch.int32, device="cuda") for _ in range(R)]
+    src_tok = [torch.zeros(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+    slot = [torch.zeros(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+    ecnt = []
+    for r in range(R):
+        ccr_mod.ccr_moe_topk(c, to_dev(logits[r]), topk[r])
+        ecnt.append(ccr_mod.ccr_moe_plan(c, topk[r], E, R, src_tok[r], slot[r]))
+    return src_tok, slot, np.stack(ecnt)
+
+
+def _fused_case(ccr_mod, R, T, E, K, H, skew=None, reps=1):
+    """Fused dispatch: exp byte-exact against the oracle's three-stage
+    dispatch; fused combine: every token back in all K of its slots."""
+    import torch
+    w = workloads.MOE_DISPATCH_BF16
+    xs, logits = workloads.moe_inputs(w, tokens=T, R=R)
+    xs = [x[:, :H].copy() for x in xs]
+    logits = [np.tile(l, (1, -(-E // l.shape[1])))[:, :E].copy() for l in logits]
+    if skew is not None:  # route every token of the first ranks to the lowest experts
+        for r in range(min(skew, R)):
+            logits[r][:, :K] += 100.0
+    ref_topk = [oracle.moe_topk(l, K) for l in logits]
+    ref = oracle.moe_dispatch(xs, ref_topk, E)
+    say(f"moe fused dispatch/combine R={R} T={T} E={E} K={K} H={H} skew={skew} reps={reps}")
+    with ccr_mod.Context(0) as c:
+        src_tok, slot, ecnt = _plan(ccr_mod, c, logits, E, K, R)
+        np.testing.assert_array_equal(ecnt, ref["ecnt"])
+        rows = [int(ref["counts"][:, d].sum()) for d in range(R)]
+        d_x = [to_dev(x) for x in xs]
+        for rep in range(reps):
+            exp = [torch.full((max(1, n), H), -7.0, dtype=torch.bfloat16, device="cuda") for n in rows]
+            ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, ecnt, K, exp)
+            out = [torch.zeros(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+            ccr_mod.ccr_moe_combine_fused(c, exp, slot, ecnt, T, K, out)
+            torch.cuda.synchronize()
+            for d in range(R):
+                got = to_host(exp[d])
+                np.testing.assert_array_equal(got[:rows[d]], ref["exp"][d])
+                if rows[d] == 0:  # nothing may be written to an empty destination
+                    assert (got == to_host(torch.full((1, H), -7.0, dtype=torch.bfloat16))).all()
+            for r in range(R):
+                np.testing.assert_array_equal(to_host(out[r]), np.repeat(xs[r][:, None, :], K, axis=1))
+
+
+@pytest.mark.parametrize("R,T,E,K,H", [(1, 5, 4, 2, 8), (2, 4, 4, 2, 8), (2, 50, 8, 2, 64),
+                                       (4, 257, 16, 3, 136), (8, 512, 64, 6, 256),
+                                       (3, 1, 6, 6, 8), (5, 77, 1000, 16, 24)])
+def test_fused_dispatch_combine_small(ccr_mod, R, T, E, K, H):
+    _fused_case(ccr_mod, R, T, E, K, H)
+
+
+def test_fused_dispatch_empty_destinations(ccr_mod):
+    # ranks 0..3 send every row to experts 0..K-1, which live on rank 0
+    _fused_case(ccr_mod, 4, 100, 8, 2, 64, skew=4)
+
+
+def test_fused_repeated_calls_reuse_tables(ccr_mod):
+    # more calls than table slots, each checked
+    _fused_case(ccr_mod, 4, 129, 16, 4, 72, reps=6)
+    _fused_case(ccr_mod, 2, 31, 4, 1, 16, reps=2)
+
+
+def test_fused_dispatch_combine_full_size(ccr_mod):
+    """8 ranks x 4096 tokens x 2048 hidden bf16, 64 experts, top-6."""
+    w = workloads.MOE_DISPATCH_BF16
+    _fused_case(ccr_mod, w.R, w.tokens, w.experts, w.topk, w.hidden)
+
+
+def test_fused_invalid_arguments(ccr_mod):
+    import torch
+    R, T, E, K, H = 2, 16, 4, 2, 8
+    w = workloads.MOE_DISPATCH_BF16
+    xs, logits = workloads.moe_inputs(w, tokens=T, R=R)
+    xs = [x[:, :H].copy() for x in xs]
+    logits = [l[:, :E].copy() for l in logits]
+    say("moe fused invalid arguments")
+    with ccr_mod.Context(0) as c:
+        src_tok, slot, ecnt = _plan(ccr_mod, c, logits, E, K, R)
+        rows = [int(ecnt[:, (E // R) * d:(E // R) * (d + 1)].sum()) for d in range(R)]
+        d_x = [to_dev(x) for x in xs]
+        exp = [torch.zeros(max(1, n), H, dtype=torch.bfloat16, device="cuda") for n in rows]
+        # an expert-major buffer that overlaps a source
+        big = torch.zeros(T + max(rows) + 1, H, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(ccr_mod.CcrError) as e:
+            ccr_mod.ccr_moe_dispatch_fused(c, [big[:T], d_x[1]], src_tok, ecnt, K, [big[1:], exp[1]])
+        assert e.value.status == ccr_mod.CCR_ERR_INVALID_ARG
+        # counts that do not add up to T*K
+        bad = ecnt.copy()
+        bad[0, 0] += 1
+        with pytest.raises(ccr_mod.CcrError):
+            ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, bad, K, exp)
+        # two outputs of the combine that overlap
+        out = torch.zeros(2 * T * K + 1, H, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(ccr_mod.CcrError):
+            ccr_mod.ccr_moe_combine_fused(c, exp, slot, ecnt, T, K, [out[:T * K], out[1:T * K + 1]])
+        # the valid call still works afterwards
+        ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, ecnt, K, exp)
+        torch.cuda.synchronize()
