@@ -171,6 +171,41 @@ def median_ms(fn, reps=10, warm=3):
     return sorted(ts)[len(ts) // 2]
 
 
+def moe_buffers(ccr, m):
+    """Inputs, routing, plan and every buffer of one expert-parallel
+    dispatch / combine of workload m, on cuda:0."""
+    import torch
+    R, T, H, E, K = m.R, m.tokens, m.hidden, m.experts, m.topk
+    xs = [torch.randn(T, H, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    logits = [torch.randn(T, E, device="cuda") for _ in range(R)]
+    with ccr.Context(0) as ctx:
+        topk = [torch.empty(T, K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        src_tok = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        slot = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        route_ms = median_ms(lambda: [ccr.ccr_moe_topk(ctx, logits[r], topk[r]) for r in range(R)], 10)
+        ecnt = np.stack([ccr.ccr_moe_plan(ctx, topk[r], E, R, src_tok[r], slot[r]) for r in range(R)])
+    rows = [int(ecnt[:, (E // R) * d:(E // R) * (d + 1)].sum()) for d in range(R)]
+    return {"xs": xs, "src_tok": src_tok, "slot": slot, "ecnt": ecnt, "route_ms": route_ms,
+            "send": [torch.empty(T * K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)],
+            "recv": [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows],
+            "exp": [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows],
+            "out": [torch.empty(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]}
+
+
+def moe_probe(ccr, workloads, steps):
+    """Only the fused dispatch and combine of the MoE dispatch workload,
+    `steps` times each (the run behind the gather kernel's profiles)."""
+    import torch
+    m = workloads.MOE_DISPATCH_BF16
+    b = moe_buffers(ccr, m)
+    with ccr.Context(0) as ctx:
+        for _ in range(steps):
+            ccr.ccr_moe_dispatch_fused(ctx, b["xs"], b["src_tok"], b["ecnt"], m.topk, b["exp"])
+            ccr.ccr_moe_combine_fused(ctx, b["exp"], b["slot"], b["ecnt"], m.tokens, m.topk, b["out"])
+        torch.cuda.synchronize()
+    log(f"moe probe: {steps} fused dispatch + combine")
+
+
 def workload_timings(ccr, workloads):
     """The other workloads, for context (each is also a full-size parity
     test): median time per call and the figures of merit of each."""
@@ -193,19 +228,9 @@ def workload_timings(ccr, workloads):
         del bufs
     m = workloads.MOE_DISPATCH_BF16
     R, T, H, E, K = m.R, m.tokens, m.hidden, m.experts, m.topk
-    xs = [torch.randn(T, H, device="cuda").to(torch.bfloat16) for _ in range(R)]
-    logits = [torch.randn(T, E, device="cuda") for _ in range(R)]
-    with ccr.Context(0) as ctx:
-        topk = [torch.empty(T, K, dtype=torch.int32, device="cuda") for _ in range(R)]
-        src_tok = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
-        slot = [torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
-        route_ms = median_ms(lambda: [ccr.ccr_moe_topk(ctx, logits[r], topk[r]) for r in range(R)], 10)
-        ecnt = np.stack([ccr.ccr_moe_plan(ctx, topk[r], E, R, src_tok[r], slot[r]) for r in range(R)])
-    rows = [int(ecnt[:, (E // R) * d:(E // R) * (d + 1)].sum()) for d in range(R)]
-    send = [torch.empty(T * K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
-    recv = [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows]
-    exp = [torch.empty(n, H, dtype=torch.bfloat16, device="cuda") for n in rows]
-    outb = [torch.empty(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    b = moe_buffers(ccr, m)
+    xs, src_tok, slot, ecnt = b["xs"], b["src_tok"], b["slot"], b["ecnt"]
+    send, recv, exp, outb, route_ms = b["send"], b["recv"], b["exp"], b["out"], b["route_ms"]
     moved = R * T * K * H * 2  # bytes of rows each stage moves over all ranks
     res = {"route_topk_ms_all_ranks": round(route_ms, 4), "rows_per_rank": T * K,
            "exchange_bytes": moved}
@@ -220,15 +245,22 @@ def workload_timings(ccr, workloads):
     with ccr.Context(0) as ctx:
         d_ms = median_ms(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp), 10)
         c_ms = median_ms(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb), 10)
-        ccr.ccr_profile_enable(ctx, True)
-        ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp)
-        g = ccr.ccr_profile_read(ctx, "moe_gather")
+        gbs = {}
+        for name, fn in (("dispatch", lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp)),
+                         ("combine", lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb))):
+            ccr.ccr_profile_enable(ctx, True)
+            for _ in range(5):
+                fn()
+            g = ccr.ccr_profile_read(ctx, "moe_gather")
+            gbs[name] = (round(g["bytes"] / (g["ms"] * 1e-3) / 1e9, 1) if g["ms"] else None,
+                         round(g["ms"] / max(1, g["launches"]) * 1e3, 2))
         ccr.ccr_profile_enable(ctx, False)
     # one gather: every row read once and written once
     res["fused"] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
                     "dispatch_algorithmic_gbs": round(2 * moved / (d_ms * 1e-3) / 1e9, 1),
-                    "gather_kernel_gbs": round(g["bytes"] / (g["ms"] * 1e-3) / 1e9, 1) if g["ms"] else None,
-                    "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
+                    "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1),
+                    "dispatch_gather_kernel": {"gbs": gbs["dispatch"][0], "us": gbs["dispatch"][1]},
+                    "combine_gather_kernel": {"gbs": gbs["combine"][0], "us": gbs["combine"][1]}}
     out[m.name] = res
     return out
 
@@ -350,6 +382,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain BYTES copy through the copy kernel (counter calibration)")
+    ap.add_argument("--moe-probe", action="store_true",
+                    help="only run --steps fused MoE dispatch + combine calls (gather kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "
@@ -363,6 +397,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(ccr, args.copy_probe, max(1, args.steps))
+        return
+    if args.moe_probe:
+        moe_probe(ccr, workloads, max(1, args.steps))
         return
 
     w = workloads.DP_BUCKET_BF16
