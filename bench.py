@@ -155,13 +155,17 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
     return out
 
 
-def median_ms(fn, reps=10, warm=3):
+def median_ms(fn, reps=10, warm=3, before=None):
+    """Median event time of fn; `before` (untimed) runs ahead of each rep,
+    e.g. a scratch write that evicts the caches."""
     import torch
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
+        if before is not None:
+            before()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -214,15 +218,22 @@ def workload_timings(ccr, workloads):
     for w, how in ((workloads.RING_SMALL_F32, "allreduce"), (workloads.RS_AG_R32_F32, "rs_then_ag")):
         bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
         b, R, N = 4, w.R, w.count
+        cold = None
         with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
             if how == "allreduce":
                 ms = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 20)
                 algo = b * N * (3 * (R - 1) + 1 + 2 * (R - 2))
+                if R * N * b <= (128 << 20):  # fits the 256 MB MALL: also time it cold
+                    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+                    cold = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 20,
+                                     before=lambda: scratch.fill_(1))
+                    del scratch
             else:
                 ms = median_ms(lambda: (ccr.ccr_reduce_scatter(ctx, bufs),
                                         ccr.ccr_all_gather(ctx, bufs)), 10)
                 algo = b * N * 5 * (R - 1)
-        out[w.name] = {"ms": round(ms, 4), "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
+        out[w.name] = {"ms": round(ms, 4), "cold_ms": None if cold is None else round(cold, 4),
+                       "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
                        "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "slices": w.slices}
         del bufs
@@ -341,6 +352,50 @@ def cu_occupancy(ccr, budgets=(0, 64, 32, 16), nblocks=4096):
     return out
 
 
+def restored_steps(fn, bufs, steps):
+    """Per-step times (ms) of `fn` with every input restored from a pristine
+    device copy before each step, outside the timed region, so each step
+    reduces the same bits.  Events on the current stream bracket each step."""
+    import torch
+    pristine = [b.clone() for b in bufs]
+    times = []
+    for _ in range(steps):
+        for b, p in zip(bufs, pristine):
+            b.copy_(p)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    for b, p in zip(bufs, pristine):
+        b.copy_(p)
+    return times
+
+
+def percentiles(ts):
+    a = np.sort(np.asarray(ts, dtype=np.float64))
+    return {"median_ms": round(float(np.median(a)), 4), "p10_ms": round(float(np.percentile(a, 10)), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+def copy_roofline(ccr, nbytes=1 << 30, reps=5):
+    """The library's copy kernel on one plain nbytes copy at full CUs: the
+    practical streaming ceiling the reduce hop is compared with."""
+    import torch
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    with ccr.Context(0) as ctx:
+        ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+        ccr.ccr_profile_enable(ctx, True)
+        for _ in range(reps):
+            ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+        st = ccr.ccr_profile_read(ctx, "copy_kernel")
+        ccr.ccr_profile_enable(ctx, False)
+    del a, b
+    return st["bytes"] / (st["ms"] * 1e6)
+
+
 def copy_probe(ccr, nbytes, reps):
     """A plain copy of nbytes through the library's copy kernel, reps times
     (the calibration run for the HBM traffic counters)."""
@@ -431,6 +486,11 @@ def main():
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
 
+    log("bench: per-step times with inputs restored before each step")
+    restored = percentiles(restored_steps(step, bufs, max(20, args.steps)))
+    log("bench: plain 1 GiB copy (copy roofline)")
+    copy_gbs = copy_roofline(ccr)
+
     gemm = pp = occ = launch = None
     if not args.no_gemm:
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
@@ -487,6 +547,13 @@ def main():
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
                      "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
+        "protocol": {"timed_region": f"{args.steps} back-to-back in-place all-reduces, host clock, "
+                                     "synchronised on both sides",
+                     "restored_inputs": dict(restored, note="inputs restored by a device copy before "
+                                             "each step, outside HIP events around the step")},
+        "copy_roofline": {"gbs": round(copy_gbs, 1), "frac_of_8tbs": round(copy_gbs / HBM_PEAK_GBS, 4),
+                          "reduce_hop_frac_of_copy": round(red_gbs / copy_gbs, 4),
+                          "what": "copy kernel, one 1 GiB copy, full CUs"},
         "reduce_forward_kernel": None if not fwd["ms"] else {
             "achieved": round(fwd["bytes"] / (fwd["ms"] * 1e6), 1), "launches": fwd["launches"],
             "mean_launch_us": round(fwd["ms"] * 1e3 / max(1, fwd["launches"]), 3)},
