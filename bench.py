@@ -105,7 +105,7 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
         for _ in range(n_gemm):
             torch.matmul(A, B, out=C)
 
-    def window(ctx=None):
+    def window(ctx=None, events=False):
         torch.cuda.synchronize()
         go = torch.cuda.Event()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -130,7 +130,30 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             return gemm, 0.0, gemm
         coll = ev[2].elapsed_time(ev[3])
         span = max(ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[3]))
-        return gemm, coll, span
+        return (gemm, coll, span, ev) if events else (gemm, coll, span)
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def contention(ctx):
+        """HOCCL Eq. 1 for the collective: the integral over the GEMMs' active
+        time of the compute units its kernels hold, over n_cu times that
+        time.  One more window, with every collective kernel bracketed by
+        events attached to its launch; the GEMMs run back to back, so
+        compute is active from the first GEMM's start to the last one's end."""
+        ccr.ccr_profile_enable(ctx, True)
+        gemm, _, _, ev = window(ctx, events=True)
+        iv = np.concatenate([ccr.ccr_profile_intervals(ctx, k, ev[0])
+                             for k in ("reduce", "copy_kernel", "reduce_forward")])
+        ccr.ccr_profile_enable(ctx, False)
+        # sweep the interval ends: CUs held at t = min(n_cu, sum over running kernels)
+        edges = sorted([(max(0.0, s), cu) for s, e, cu in iv if e > 0 and s < gemm] +
+                       [(min(gemm, e), -cu) for s, e, cu in iv if e > 0 and s < gemm])
+        held, level, last = 0.0, 0.0, 0.0
+        for t, d in edges:
+            held += min(n_cu, level) * (t - last)
+            level += d
+            last = t
+        return held / (n_cu * gemm)
 
     with torch.cuda.stream(g):
         gemms()
@@ -144,6 +167,7 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             torch.cuda.synchronize()
             t1 = time_steps(lambda: collective(ctx, c), 3)
             gemm, coll, span = sorted(window(ctx) for _ in range(3))[1]
+            i_coll = contention(ctx)
             out["runs"].append({
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
                 "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
@@ -151,7 +175,8 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
                 "collective_alone_ms": round(t1 * 1e3, 4),
                 "collectives_under_load_ms": round(coll, 3),
                 "makespan_ms": round(span, 3),
-                "makespan_over_gemm_alone_pct": round(100.0 * (span / alone - 1.0), 2)})
+                "makespan_over_gemm_alone_pct": round(100.0 * (span / alone - 1.0), 2),
+                "contention_rate": round(i_coll, 4)})
     return out
 
 

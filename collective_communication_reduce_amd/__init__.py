@@ -85,6 +85,7 @@ _SIGNATURES = {
     "ccr_probe_cu_ids": [_vp, _vp, _i32, _vp],
     "ccr_profile_enable": [_vp, _i32],
     "ccr_profile_read": [_vp, _i32, _vp],
+    "ccr_profile_intervals": [_vp, _i32, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_dma_info": [_vp, _vp, _vp],
     "ccr_sendrecv_slot_log": [_vp, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_stream_wait": [_vp, _vp, _i32],
@@ -415,6 +416,23 @@ def ccr_profile_read(ctx: Context, kind: str) -> dict:
     st = ccr_kernel_stats_t()
     _check(_lib.ccr_profile_read(ctx.handle, PROFILE_KINDS[kind], ctypes.byref(st)))
     return {"launches": st.launches, "bytes": st.bytes, "ms": st.ms}
+
+
+def ccr_profile_intervals(ctx: Context, kind: str, ref_event) -> np.ndarray:
+    """(n, 3) float64 array of (start ms, end ms, compute units held) of
+    every timed launch of `kind`, relative to the recorded torch.cuda.Event
+    `ref_event` (created with enable_timing=True)."""
+    n = ctypes.c_int64()
+    ref = ctypes.c_void_p(ref_event.cuda_event)
+    _check(_lib.ccr_profile_intervals(ctx.handle, PROFILE_KINDS[kind], ref, None, None, None, 0,
+                                      ctypes.byref(n)))
+    a = np.zeros(n.value, np.float64)
+    b = np.zeros(n.value, np.float64)
+    c = np.zeros(n.value, np.int32)
+    if n.value:
+        _check(_lib.ccr_profile_intervals(ctx.handle, PROFILE_KINDS[kind], ref, a.ctypes.data,
+                                          b.ctypes.data, c.ctypes.data, n.value, ctypes.byref(n)))
+    return np.stack([a, b, c.astype(np.float64)], axis=1) if n.value else np.zeros((0, 3))
 
 
 def ccr_dma_info(ctx: Context) -> list:

@@ -116,6 +116,7 @@ struct ccr_ctx {
     int kind;
     hipEvent_t start, stop;
     int64_t bytes;
+    int32_t cus;  // compute units the launch can hold (0 for SDMA copies)
   };
   std::vector<Timed> timed;
   std::vector<hipEvent_t> timing_pool;
@@ -342,10 +343,18 @@ struct TimedScope {
     hipEvent_t stop;
     CCR_TRY(timing_event(ctx, &stop));
     HIP_TRY(hipEventRecord(stop, s));
-    ctx->timed.push_back(ccr_ctx::Timed{kind, start, stop, bytes});
+    ctx->timed.push_back(ccr_ctx::Timed{kind, start, stop, bytes, 0});  // SDMA: no compute unit
     return CCR_OK;
   }
 };
+
+// Compute units a launch of `workgroups` workgroups can hold at once: one
+// per workgroup, at most the CUs the context's mask allows.
+int32_t cus_held(const ccr_ctx* ctx, int64_t workgroups) {
+  const int64_t allowed = ctx->cfg.cu_budget > 0 ? std::min(ctx->cfg.cu_budget, ctx->num_cus)
+                                                 : ctx->num_cus;
+  return (int32_t)std::max<int64_t>(0, std::min(allowed, workgroups));
+}
 
 int64_t payload(const Piece* p, size_t n) {
   int64_t b = 0;
@@ -368,8 +377,15 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
   HIP_TRY(launch_pieces(kind, p, n, tuning(), s, start, stop));
   // algorithmic bytes: reduce reads 2 and writes 1 (forwarding writes 2),
   // copy reads 1 and writes 1, per byte of payload
+  // workgroups: one per kBlock x unroll 16-byte vectors of each piece
+  const LaunchTuning tune = tuning();
+  const int64_t per_wg = (int64_t)kBlock * std::max(1, tune.unroll) * 16;
+  int64_t wgs = 0;
+  for (int i = 0; i < n; i++) wgs += (p[i].nbytes + per_wg - 1) / per_wg;
+  if (tune.grid > 0) wgs = std::min<int64_t>(wgs, tune.grid);
   ctx->timed.push_back(ccr_ctx::Timed{fwd ? kProfReduceFwd : reduce ? kProfReduce : kProfCopyKernel,
-                                      start, stop, payload(p, (size_t)n) * (fwd ? 4 : reduce ? 3 : 2)});
+                                      start, stop, payload(p, (size_t)n) * (fwd ? 4 : reduce ? 3 : 2),
+                                      cus_held(ctx, wgs)});
   return CCR_OK;
 }
 
@@ -444,7 +460,8 @@ ccr_status_t launch_partials_timed(ccr_ctx* ctx, PartialKind kind, const Partial
   CCR_TRY(timing_event(ctx, &start));
   CCR_TRY(timing_event(ctx, &stop));
   HIP_TRY(launch_partials(kind, p, n, s, start, stop));
-  ctx->timed.push_back(ccr_ctx::Timed{kProfReduce, start, stop, elems * per});
+  ctx->timed.push_back(ccr_ctx::Timed{kProfReduce, start, stop, elems * per,
+                                      cus_held(ctx, (elems + 8 * kBlock * 2 - 1) / (8 * kBlock * 2))});
   return CCR_OK;
 }
 
@@ -1266,7 +1283,8 @@ ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int6
     CCR_TRY(timing_event(ctx, &start));
     CCR_TRY(timing_event(ctx, &stop));
     HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s, start, stop));
-    ctx->timed.push_back(ccr_ctx::Timed{kProfGather, start, stop, 2 * R * rows * m.row_bytes});
+    ctx->timed.push_back(ccr_ctx::Timed{kProfGather, start, stop, 2 * R * rows * m.row_bytes,
+                                        cus_held(ctx, R * ((rows + 7) / 8))});
   } else {
     HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s));
   }
@@ -1353,6 +1371,32 @@ ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on) {
     ctx->dma->reset_stats();
   }
   ctx->prof_on = on != 0;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_profile_intervals(ccr_ctx_t ctx, int kind, void* ref_event, double* start_ms,
+                                  double* end_ms, int32_t* cus, int64_t max, int64_t* n) {
+  CCR_TRY(check_ctx(ctx));
+  if (!n || !ref_event) return fail(CCR_ERR_INVALID_ARG, "n or ref_event is NULL");
+  if (kind < 0 || kind > 4) return fail(CCR_ERR_INVALID_ARG, "kind %d outside [0, 4]", kind);
+  if (max < 0) return fail(CCR_ERR_INVALID_ARG, "max < 0");
+  HIP_TRY(hipDeviceSynchronize());
+  if (ctx->dma) ctx->dma->drain(30.0);
+  hipEvent_t ref = static_cast<hipEvent_t>(ref_event);
+  int64_t k = 0;
+  for (const auto& t : ctx->timed) {
+    if (t.kind != kind) continue;
+    if (k < max) {
+      float a = 0.f, b = 0.f;
+      HIP_TRY(hipEventElapsedTime(&a, ref, t.start));
+      HIP_TRY(hipEventElapsedTime(&b, ref, t.stop));
+      if (start_ms) start_ms[k] = a;
+      if (end_ms) end_ms[k] = b;
+      if (cus) cus[k] = t.cus;
+    }
+    k++;
+  }
+  *n = k;
   return CCR_OK;
 }
 

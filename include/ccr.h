@@ -375,6 +375,19 @@ typedef struct {
 ccr_status_t ccr_profile_enable(ccr_ctx_t ctx, int on);
 ccr_status_t ccr_profile_read(ccr_ctx_t ctx, int kind, ccr_kernel_stats_t *out);
 
+/* The timed launches of `kind` (as for ccr_profile_read) since profiling
+ * was enabled, one record each, in issue order: start_ms[i] and end_ms[i]
+ * relative to `ref_event` (a hipEvent_t with timing, recorded on the
+ * context's device and complete), and cus[i] = the compute units the
+ * launch can hold at once: one per workgroup, at most the CUs the context's
+ * budget allows (0 for SDMA copies).  With the intervals of the compute
+ * kernels, this gives HOCCL's contention rate (Eq. 1: compute units held by
+ * communication while compute kernels run, over all compute units).
+ * Synchronises the device first.  Any of the three arrays may be NULL;
+ * at most max records are written; *n receives the full count. */
+ccr_status_t ccr_profile_intervals(ccr_ctx_t ctx, int kind, void *ref_event, double *start_ms,
+                                  double *end_ms, int32_t *cus, int64_t max, int64_t *n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,6 +153,42 @@ def test_invalid_arguments(ccr_mod, ctx):
     assert ccr_mod._lib.ccr_ctx_set_config(ctx.handle, ct.byref(bad)) == ccr_mod.CCR_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("budget", [0, 32])
+def test_profile_intervals(ccr_mod, budget):
+    """Per-launch intervals follow the launches: ordered, inside the
+    caller's window, and never holding more CUs than the budget allows."""
+    import torch
+    R, n = 8, 1 << 20
+    xs = workloads.random_buffers(R, n, "f32", seed=9)
+    ts = [to_dev(x) for x in xs]
+    say(f"profile intervals, cu_budget={budget}")
+    with ccr_mod.Context(0, ccr_mod.Config(cu_budget=budget)) as c:
+        ccr_mod.ccr_allreduce(c, ts)
+        torch.cuda.synchronize()
+        ccr_mod.ccr_profile_enable(c, True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ccr_mod.ccr_allreduce(c, ts)
+        e1.record()
+        torch.cuda.synchronize()
+        window = e0.elapsed_time(e1)
+        red = ccr_mod.ccr_profile_intervals(c, "reduce", e0)
+        fwd = ccr_mod.ccr_profile_intervals(c, "reduce_forward", e0)
+        cpy = ccr_mod.ccr_profile_intervals(c, "copy_kernel", e0)
+        stats = ccr_mod.ccr_profile_read(c, "reduce")
+        ccr_mod.ccr_profile_enable(c, False)
+    assert (len(red), len(fwd), len(cpy)) == (R - 2, 1, R - 2) == (stats["launches"], 1, R - 2)
+    allowed = budget or torch.cuda.get_device_properties(0).multi_processor_count
+    iv = np.concatenate([red, fwd, cpy])
+    assert (iv[:, 0] >= -1e-3).all() and (iv[:, 1] >= iv[:, 0]).all() and (iv[:, 1] <= window + 1e-3).all()
+    assert (iv[:, 2] >= 1).all() and (iv[:, 2] <= allowed).all()
+    assert (iv[:, 2] == allowed).all()  # 1 Mi elements per rank: far more workgroups than CUs
+    hops = np.concatenate([red, fwd, cpy])
+    hops = hops[np.argsort(hops[:, 0])]
+    assert (np.diff(hops[:, 0]) > 0).all()  # one stream: launches run one after another
+    assert abs(np.sum(red[:, 1] - red[:, 0]) - stats["ms"]) < 1e-2
+
+
 # ------------------------------------------------ full-size workloads
 FULL = [(workloads.RING_SMALL_F32, "allreduce"), (workloads.DP_BUCKET_BF16, "allreduce"),
         (workloads.RS_AG_R32_F32, "rs_then_ag")]
