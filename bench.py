@@ -200,6 +200,29 @@ def median_ms(fn, reps=10, warm=3, before=None):
     return sorted(ts)[len(ts) // 2]
 
 
+def size_sweep(ccr, R=8, sizes_mib=(2, 4, 8, 16, 64, 256, 1024)):
+    """The pages' message-size sweep (nccl-tests style), at R = 8 bf16 ranks:
+    busBW of the all-reduce and of the all-gather alone, with kernel and
+    with SDMA copies, per-rank sizes in MiB."""
+    import torch
+    out = []
+    for mib in sizes_mib:
+        N = (mib << 20) // 2
+        bufs = [torch.randn(N, device="cuda").mul_(1e-3).to(torch.bfloat16) for _ in range(R)]
+        row = {"mib_per_rank": mib}
+        for mode in ("kernel", "sdma"):
+            with ccr.Context(0, ccr.Config(copy_mode=mode)) as ctx:
+                reps = 10 if mib <= 64 else 4
+                ar = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), reps, warm=2)
+                ag = median_ms(lambda: ccr.ccr_all_gather(ctx, bufs), reps, warm=2)
+            row[f"allreduce_{mode}_busbw"] = round(2 * N / (ar * 1e-3) * 2 * (R - 1) / R / 1e9, 1)
+            row[f"allgather_{mode}_busbw"] = round(2 * N / (ag * 1e-3) * (R - 1) / R / 1e9, 1)
+        out.append(row)
+        del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def moe_buffers(ccr, m):
     """Inputs, routing, plan and every buffer of one expert-parallel
     dispatch / combine of workload m, on cuda:0."""
@@ -550,6 +573,8 @@ def main():
         log("bench: the other workloads (context)")
         others = workload_timings(ccr, workloads)
         others["stage_schedule"] = schedule_timings(ccr, workloads)
+        log("bench: message-size sweep")
+        others["size_sweep_r8_bf16"] = size_sweep(ccr)
 
     cpu = None
     if not args.no_cpu:

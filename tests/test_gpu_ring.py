@@ -189,6 +189,29 @@ def test_profile_intervals(ccr_mod, budget):
     assert abs(np.sum(red[:, 1] - red[:, 0]) - stats["ms"]) < 1e-2
 
 
+def test_launch_blocking_does_not_change_bits(ccr_mod, tmp_path):
+    """HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one) leaves
+    the bits unchanged in every mode.  HIP reads the variable when it
+    initialises, so the case runs in one child process."""
+    import os
+    import subprocess
+    import sys
+    R, n = 5, 2 * 65536 + 7
+    xs = workloads.random_buffers(R, n, "bf16", seed=77, dist="normal", scale=1e-3)
+    src, dst = tmp_path / "in.npz", tmp_path / "out.npz"
+    np.savez(src, R=R, **{f"x{i}": x for i, x in enumerate(xs)})
+    say(f"launch-blocking child R={R} n={n}")
+    env = dict(os.environ, HIP_LAUNCH_BLOCKING="1")
+    child = os.path.join(os.path.dirname(__file__), "launch_blocking_child.py")
+    r = subprocess.run([sys.executable, child, str(src), str(dst)], env=env, timeout=150,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    got = np.load(dst)
+    ref = oracle.ring_allreduce(xs, S=1)
+    for name in ("kernel_s1", "kernel_overlap_s3", "sdma_s2"):
+        _assert_bitwise([got[f"{name}_{q}"] for q in range(R)], ref, f"launch blocking, {name}")
+
+
 # ------------------------------------------------ full-size workloads
 FULL = [(workloads.RING_SMALL_F32, "allreduce"), (workloads.DP_BUCKET_BF16, "allreduce"),
         (workloads.RS_AG_R32_F32, "rs_then_ag")]
