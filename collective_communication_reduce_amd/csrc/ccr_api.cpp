@@ -491,8 +491,9 @@ ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) 
 // (rank c -> c+1 -> ... -> c-1, one hop each).  Each chain is cut into m
 // sub-chains over equal byte ranges, m = E / gcd(R, E) (fewer if pieces
 // would drop below 256 KiB), so the R*m chains spread evenly over the E
-// engines; chain i runs on engine i mod E.  Copies are issued hop by hop, so
-// every engine receives its chains' copies in dependency order.
+// engines; chain i runs on engine i mod E.  Copies are listed hop by hop;
+// each waits for the previous link of its chain, and the DMA proxy issues it
+// when that link completes.
 std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, int s, int V,
                                int esize, int engines) {
   const int E = std::max(1, engines);

@@ -81,8 +81,11 @@ struct DmaProxy::Job {
   int64_t bytes = 0, ncopies = 0;
   // kCopies
   std::vector<DmaCopy> copies;
-  std::vector<hsa_signal_t> sig;  // one per issued copy
-  size_t first_pending = 0;
+  std::vector<hsa_signal_t> sig;   // per copy; handle 0 until issued
+  std::vector<int32_t> kid_start;  // copies that wait for copy i: kids[kid_start[i] .. kid_start[i+1])
+  std::vector<int32_t> kids;
+  std::vector<int32_t> inflight;   // issued, not yet seen complete
+  int64_t ndone = 0;
   // kStaged
   StagedPlan plan;
   struct Slot {
@@ -353,33 +356,55 @@ void DmaProxy::put_signal(hsa_signal_t s) {
   if (s.handle) signal_pool_.push_back(s);
 }
 
-bool DmaProxy::issue(char* dst, const char* src, int64_t bytes, const hsa_signal_t* dep,
-                     hsa_signal_t done, int engine) {
+bool DmaProxy::issue(char* dst, const char* src, int64_t bytes, hsa_signal_t done, int engine) {
   if (!done.handle) return false;
   const int e = engines_[(size_t)engine % engines_.size()];
-  return hsa_amd_memory_async_copy_on_engine(dst, agent_, src, agent_, (size_t)bytes, dep ? 1 : 0,
-                                             dep, done, (hsa_amd_sdma_engine_id_t)(1u << e),
+  return hsa_amd_memory_async_copy_on_engine(dst, agent_, src, agent_, (size_t)bytes, 0, nullptr,
+                                             done, (hsa_amd_sdma_engine_id_t)(1u << e),
                                              true) == HSA_STATUS_SUCCESS;
 }
 
-// Issue every copy of a copy job at once; chains are expressed as HSA
-// dependencies, so the engines run them without CPU round trips.
+bool DmaProxy::start_copy(Job& j, int32_t i) {
+  const DmaCopy& c = j.copies[(size_t)i];
+  hsa_signal_t s = get_signal();
+  if (!issue(c.dst, c.src, c.bytes, s, c.engine)) {
+    put_signal(s);
+    j.failed = true;
+    note_error("an SDMA copy could not be issued");
+    return false;
+  }
+  j.sig[(size_t)i] = s;
+  j.inflight.push_back(i);
+  return true;
+}
+
+// A copy job starts with the copies that wait for nothing; the proxy issues
+// each remaining copy once the copy it waits for has completed.  Chains are
+// kept on the host on purpose: expressed as HSA dependency signals, a chain
+// makes its engine wait on the signal itself, and with chains on many
+// engines at once that waiting slowed a concurrent GEMM by 2x and the
+// copies themselves by two orders of magnitude on gfx950.
 bool DmaProxy::begin(Job& j) {
   if (j.kind == Job::kCopies) {
-    j.sig.reserve(j.copies.size());
-    for (size_t i = 0; i < j.copies.size(); i++) {
-      const DmaCopy& c = j.copies[i];
-      const hsa_signal_t* dep = nullptr;
-      if (c.after >= 0 && (size_t)c.after < j.sig.size()) dep = &j.sig[(size_t)c.after];
-      hsa_signal_t s = get_signal();
-      if (!issue(c.dst, c.src, c.bytes, dep, s, c.engine)) {
-        put_signal(s);
+    const size_t n = j.copies.size();
+    j.sig.assign(n, hsa_signal_t{0});
+    j.kid_start.assign(n + 1, 0);
+    for (size_t i = 0; i < n; i++) {
+      const int32_t a = j.copies[i].after;
+      if (a >= (int32_t)i) {  // a copy can only wait for an earlier one
         j.failed = true;
-        note_error("an SDMA copy could not be issued");
+        note_error("an SDMA copy waits for a later copy of its job");
         return true;
       }
-      j.sig.push_back(s);
+      if (a >= 0) j.kid_start[(size_t)a + 1]++;
     }
+    for (size_t i = 0; i < n; i++) j.kid_start[i + 1] += j.kid_start[i];
+    j.kids.assign((size_t)j.kid_start[n], 0);
+    std::vector<int32_t> fill(j.kid_start.begin(), j.kid_start.end() - 1);
+    for (size_t i = 0; i < n; i++)
+      if (const int32_t a = j.copies[i].after; a >= 0) j.kids[(size_t)fill[(size_t)a]++] = (int32_t)i;
+    for (size_t i = 0; i < n && !j.failed; i++)
+      if (j.copies[i].after < 0) start_copy(j, (int32_t)i);
     return true;
   }
   j.slots.assign((size_t)j.plan.slots, Job::Slot());
@@ -390,10 +415,20 @@ bool DmaProxy::begin(Job& j) {
 // nothing is left to issue.
 bool DmaProxy::advance(Job& j) {
   if (j.kind == Job::kCopies) {
-    while (j.first_pending < j.sig.size() &&
-           hsa_signal_load_scacquire(j.sig[j.first_pending]) <= 0)
-      j.first_pending++;
-    return j.first_pending == j.sig.size();
+    std::vector<int32_t> running;
+    running.swap(j.inflight);
+    for (size_t k = 0; k < running.size(); k++) {
+      const int32_t i = running[k];
+      if (hsa_signal_load_scacquire(j.sig[(size_t)i]) > 0) {
+        j.inflight.push_back(i);
+        continue;
+      }
+      j.ndone++;
+      for (int32_t q = j.kid_start[(size_t)i]; q < j.kid_start[(size_t)i + 1] && !j.failed; q++)
+        start_copy(j, j.kids[(size_t)q]);
+    }
+    if (j.failed) return j.inflight.empty();  // finish once nothing issued is running
+    return j.ndone == (int64_t)j.copies.size();
   }
   // Staged transfer: the per-slot state machine (idle -> filling ->
   // draining -> idle); chunk i always uses slot i mod slots.
@@ -412,7 +447,7 @@ bool DmaProxy::advance(Job& j) {
       const int64_t lo = std::min<int64_t>(len, k * part), hi = std::min<int64_t>(len, (k + 1) * part);
       if (hi <= lo) break;
       hsa_signal_t s = get_signal();
-      if (!issue(dst + lo, src + lo, hi - lo, nullptr, s, base + k)) {
+      if (!issue(dst + lo, src + lo, hi - lo, s, base + k)) {
         put_signal(s);
         j.failed = true;
         note_error("an SDMA staging copy could not be issued");
@@ -514,7 +549,8 @@ void DmaProxy::loop() {
             }
             if (j.kind == Job::kStaged) slot_log_ = j.log;
           }
-          for (hsa_signal_t s : j.sig) put_signal(s);
+          for (hsa_signal_t s : j.sig)
+            if (s.handle) put_signal(s);
           j.sig.clear();
           if (flags) {
             store_flag(fi, kFinishValue);  // release the stream

@@ -45,9 +45,9 @@
 
 namespace ccr {
 
-// One copy of a job.  `after` indexes a copy of the same job that must have
-// finished before this one starts (-1: none); `engine` indexes the proxy's
-// engine list.
+// One copy of a job.  `after` indexes an earlier copy of the same job that
+// must have finished before this one starts (-1: none); the proxy issues the
+// copy when that one completes.  `engine` indexes the proxy's engine list.
 struct DmaCopy {
   char* dst;
   const char* src;
@@ -123,8 +123,8 @@ class DmaProxy {
   void loop();
   bool begin(Job& j);
   bool advance(Job& j);
-  bool issue(char* dst, const char* src, int64_t bytes, const hsa_signal_t* dep, hsa_signal_t done,
-             int engine);
+  bool issue(char* dst, const char* src, int64_t bytes, hsa_signal_t done, int engine);
+  bool start_copy(Job& j, int32_t i);
   hsa_signal_t get_signal();
   void put_signal(hsa_signal_t s);
   void note_error(const std::string& e);
