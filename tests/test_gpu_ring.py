@@ -212,6 +212,55 @@ def test_launch_blocking_does_not_change_bits(ccr_mod, tmp_path):
         _assert_bitwise([got[f"{name}_{q}"] for q in range(R)], ref, f"launch blocking, {name}")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_past_32_bit_offsets(ccr_mod, dt):
+    """3 ranks of 2^31 + 12345 elements (4 or 8 GiB each): element indices
+    past 2^31 and byte offsets past 4 GiB.  Inputs come from torch's seeded
+    generator on the device; sampled outputs (chunk edges, the 2^31
+    boundary, the ragged end, random picks) must equal the oracle's fold of
+    the same input values bit for bit, on every rank.  An element of chunk c
+    folds ranks c+1, ..., c-1 and then c, so the oracle folds each sample's
+    values rotated by c."""
+    import torch
+    R, n = 3, (1 << 31) + 12345
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    vec = 8 if dt == "bf16" else 4
+    say(f"allreduce {dt} R={R} n={n} (past 32-bit offsets)")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    bufs = []
+    for _ in range(R):
+        x = torch.empty(n, dtype=tdt, device="cuda")
+        for lo in range(0, n, 1 << 28):  # draw in float32 pieces, cast in place
+            hi = min(n, lo + (1 << 28))
+            x[lo:hi] = torch.randn(hi - lo, generator=gen, device="cuda").mul_(1e-3).to(tdt)
+        bufs.append(x)
+    rng = np.random.default_rng(5)
+    edges = [0, 1, n - 1, n - 2, (1 << 31) - 1, 1 << 31, (1 << 31) + 1]
+    for c in range(R):
+        lo, hi = oracle.chunk_bounds(n, R, vec, c)
+        edges += [lo, max(lo, hi - 1)]
+    idx = np.unique(np.concatenate([np.array(edges, np.int64), rng.integers(0, n, 2000)]))
+    d_idx = torch.from_numpy(idx).cuda()
+    before = [to_host(b[d_idx]) for b in bufs]
+    with ccr_mod.Context(0) as c:
+        ccr_mod.ccr_allreduce(c, bufs)
+        torch.cuda.synchronize()
+    after = [to_host(b[d_idx]) for b in bufs]
+    del bufs
+    torch.cuda.empty_cache()
+    chunk = np.zeros(idx.size, np.int64)
+    for c in range(R):
+        lo, hi = oracle.chunk_bounds(n, R, vec, c)
+        chunk[(idx >= lo) & (idx < hi)] = c
+    want = np.empty_like(before[0])
+    for k in range(idx.size):
+        cc = int(chunk[k])
+        rot = [before[(r + cc) % R][k:k + 1] for r in range(R)]
+        want[k] = oracle.fold(rot)[0]
+    for q in range(R):
+        assert after[q].tobytes() == want.tobytes(), f"rank {q} differs from the oracle"
+
+
 # ------------------------------------------------ full-size workloads
 FULL = [(workloads.RING_SMALL_F32, "allreduce"), (workloads.DP_BUCKET_BF16, "allreduce"),
         (workloads.RS_AG_R32_F32, "rs_then_ag")]
