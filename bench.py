@@ -481,9 +481,17 @@ def cpu_baseline(xs, R, count, esize, S, budget_s=12.0):
             break
     t = (time.perf_counter() - t0) / n
     bus = esize * count / t * 2 * (R - 1) / R / 1e9
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": bus, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the full workload, {n} all-reduce(s), single-threaded C oracle",
-            "ms_per_step": t * 1e3}
+            "ms_per_step": t * 1e3, "host_cpus": os.cpu_count(), "cpu_model": model}
 
 
 def main():
