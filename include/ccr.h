@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
     CCR_OK = 0,
     CCR_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment, dtype, aliasing */
-    CCR_ERR_UNSUPPORTED = 2, /* valid request this build cannot run          */
+    CCR_ERR_UNSUPPORTED = 2, /* valid request the library cannot run        */
     CCR_ERR_HIP = 3,         /* a HIP runtime call failed                     */
     CCR_ERR_OOM = 4,         /* device or pinned-host allocation failed       */
     CCR_ERR_TIMEOUT = 5      /* a bounded wait expired                        */
