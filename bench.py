@@ -212,6 +212,31 @@ def median_ms(fn, reps=10, warm=3, before=None):
     return sorted(ts)[len(ts) // 2]
 
 
+def bf16_modes(ccr, xs):
+    """The gradient bucket with both bf16 accumulation modes: time per
+    all-reduce, and the error against the float64 sum of the same bf16
+    inputs, max |y - ref| / max |ref| (the accuracy bar is 1e-2)."""
+    import torch
+    ref = np.zeros(xs[0].size, np.float64)
+    for x in xs:
+        ref += (x.astype(np.uint32) << 16).view(np.float32)
+    scale = np.abs(ref).max()
+    pristine = [to_dev(x) for x in xs]
+    bufs = [p.clone() for p in pristine]
+    out = {}
+    for mode in ("per_hop", "fp32_partials"):
+        with ccr.Context(0, ccr.Config(bf16_acc=mode)) as ctx:
+            ms = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 10,
+                           before=lambda: [b.copy_(p) for b, p in zip(bufs, pristine)])
+            for b, p in zip(bufs, pristine):
+                b.copy_(p)
+            ccr.ccr_allreduce(ctx, bufs)
+            torch.cuda.synchronize()
+        y = bufs[0].float().cpu().numpy().astype(np.float64)
+        out[mode] = {"ms": round(ms, 4), "max_err_over_max_ref": float(np.abs(y - ref).max() / scale)}
+    return out
+
+
 def size_sweep(ccr, R=8, sizes_mib=(2, 4, 8, 16, 64, 256, 1024)):
     """The pages' message-size sweep (nccl-tests style), at R = 8 bf16 ranks:
     busBW of the all-reduce and of the all-gather alone, with kernel and
@@ -593,6 +618,8 @@ def main():
         log("bench: the other workloads (context)")
         others = workload_timings(ccr, workloads)
         others["stage_schedule"] = schedule_timings(ccr, workloads)
+        log("bench: bf16 accumulation modes on the bucket")
+        others["dp_bucket_bf16_accumulation"] = bf16_modes(ccr, xs)
         log("bench: message-size sweep")
         others["size_sweep_r8_bf16"] = size_sweep(ccr)
 

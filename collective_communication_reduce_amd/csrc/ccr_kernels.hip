@@ -29,9 +29,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// The pieces of one launch, by value in the kernel arguments.  NP slots: a
+// launch of up to 8 or 16 pieces (one ring hop of R <= 16 ranks) uses the
+// small table, because a launch's host cost grows with its argument block
+// (on gfx950, ~2.3 us for 32 bytes, ~4.7 us for the 2.6 KB of 64 slots).
+template <int NP>
 struct PieceArgs {
-  Piece p[kMaxPieces];
-  int32_t tile_start[kMaxPieces + 1];  // first workgroup of each piece
+  Piece p[NP];
+  int32_t tile_start[NP + 1];  // first workgroup of each piece
   int32_t n;
 };
 
@@ -122,8 +127,8 @@ constexpr int tail_unit_bytes() {
 // issued before the first add, so 2U vectors per thread are in flight.
 // Workgroup b processes tiles b, b + gridDim.x, ... (one tile when the grid
 // has one workgroup per tile).
-template <HopKind K, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs a) {
+template <HopKind K, int U, bool NT, int NP>
+__global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
   const int ntiles = a.tile_start[a.n];
   for (int b = blockIdx.x; b < ntiles; b += gridDim.x) {
     int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
@@ -184,37 +189,47 @@ struct Timing {
   hipEvent_t start, stop;
 };
 
-template <HopKind K, int U, bool NT>
-hipError_t launch_one(const PieceArgs& a, hipStream_t s, Timing t, int grid_cap) {
+template <HopKind K, int U, bool NT, int NP>
+hipError_t launch_one(const PieceArgs<NP>& a, hipStream_t s, Timing t, int grid_cap) {
   int grid = a.tile_start[a.n];
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
   if (t.start && t.stop)
-    hipExtLaunchKernelGGL(pieces_kernel<K, U, NT>, dim3(grid), dim3(kBlock), 0, s, t.start, t.stop,
-                          0, a);
+    hipExtLaunchKernelGGL(pieces_kernel<K, U, NT, NP>, dim3(grid), dim3(kBlock), 0, s, t.start,
+                          t.stop, 0, a);
   else
-    pieces_kernel<K, U, NT><<<grid, kBlock, 0, s>>>(a);
+    pieces_kernel<K, U, NT, NP><<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <HopKind K, int U>
-hipError_t launch_kind(const PieceArgs& a, bool nt, hipStream_t s, Timing t, int g) {
+hipError_t launch_kind(const PieceArgs<kMaxPieces>& a, bool nt, hipStream_t s, Timing t, int g) {
   return nt ? launch_one<K, U, true>(a, s, t, g) : launch_one<K, U, false>(a, s, t, g);
 }
 
-template <HopKind K>
-hipError_t launch_unroll(const PieceArgs& a, int unroll, bool nt, hipStream_t s, Timing t, int g) {
-  switch (unroll) {
-    case 1: return launch_kind<K, 1>(a, nt, s, t, g);
-    case 2: return launch_kind<K, 2>(a, nt, s, t, g);
-    case 8: return launch_kind<K, 8>(a, nt, s, t, g);
-    default: return launch_kind<K, 4>(a, nt, s, t, g);
+// Every tuning variant exists for the full table; the small tables exist for
+// the default variant (2 vectors per operand per thread, temporal loads).
+template <HopKind K, int NP>
+hipError_t launch_unroll(const PieceArgs<NP>& a, int unroll, bool nt, hipStream_t s, Timing t,
+                         int g) {
+  if constexpr (NP != kMaxPieces) {
+    (void)unroll;
+    (void)nt;
+    return launch_one<K, 2, false>(a, s, t, g);
+  } else {
+    switch (unroll) {
+      case 1: return launch_kind<K, 1>(a, nt, s, t, g);
+      case 2: return launch_kind<K, 2>(a, nt, s, t, g);
+      case 8: return launch_kind<K, 8>(a, nt, s, t, g);
+      default: return launch_kind<K, 4>(a, nt, s, t, g);
+    }
   }
 }
 
 // ---------------------------------------------------------- fp32 partials
+template <int NP>
 struct PartialArgs {
-  PartialPiece p[kMaxPieces];
-  int32_t tile_start[kMaxPieces + 1];
+  PartialPiece p[NP];
+  int32_t tile_start[NP + 1];
   int32_t n;
 };
 
@@ -281,8 +296,8 @@ __device__ __forceinline__ void partial_one(const PartialPiece& pc, int64_t i) {
   }
 }
 
-template <PartialKind K>
-__global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs a) {
+template <PartialKind K, int NP>
+__global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
   const int b = blockIdx.x;
   int lo = 0, hi = a.n;
   while (hi - lo > 1) {
@@ -318,12 +333,12 @@ __global__ __launch_bounds__(64) void probe_cu_ids_kernel(int32_t* out) {
 
 }  // namespace
 
-hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
-                         hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (n <= 0) return hipSuccess;
-  if (n > kMaxPieces) return hipErrorInvalidValue;
-  PieceArgs a;
-  const int unroll = (tune.unroll == 1 || tune.unroll == 2 || tune.unroll == 8) ? tune.unroll : 4;
+namespace {
+
+template <int NP>
+hipError_t launch_pieces_np(HopKind kind, const Piece* pieces, int n, LaunchTuning tune, int unroll,
+                            hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  PieceArgs<NP> a;
   const int64_t per_tile = (int64_t)kBlock * unroll;
   int64_t tiles = 0;
   a.n = n;
@@ -335,8 +350,7 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
     tiles += (units + per_tile - 1) / per_tile;
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
   }
-  a.tile_start[n] = (int32_t)tiles;
-  for (int i = n + 1; i <= kMaxPieces; i++) a.tile_start[i] = (int32_t)tiles;
+  for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   const bool nt = tune.nontemporal != 0;
   const Timing t{start, stop};
@@ -352,11 +366,27 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
   }
 }
 
-hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
-                           hipEvent_t start, hipEvent_t stop) {
+}  // namespace
+
+hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning tune,
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (n <= 0) return hipSuccess;
   if (n > kMaxPieces) return hipErrorInvalidValue;
-  PartialArgs a;
+  const int unroll = (tune.unroll == 1 || tune.unroll == 2 || tune.unroll == 8) ? tune.unroll : 4;
+  const bool small_ok = unroll == 2 && tune.nontemporal == 0;
+  if (small_ok && n <= 8)
+    return launch_pieces_np<8>(kind, pieces, n, tune, unroll, stream, start, stop);
+  if (small_ok && n <= 16)
+    return launch_pieces_np<16>(kind, pieces, n, tune, unroll, stream, start, stop);
+  return launch_pieces_np<kMaxPieces>(kind, pieces, n, tune, unroll, stream, start, stop);
+}
+
+namespace {
+
+template <int NP>
+hipError_t launch_partials_np(PartialKind kind, const PartialPiece* pieces, int n,
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  PartialArgs<NP> a;
   const int64_t per_tile = (int64_t)kBlock * kPartialUnroll;
   int64_t tiles = 0;
   a.n = n;
@@ -367,7 +397,7 @@ hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, 
     tiles += (units + per_tile - 1) / per_tile;
     if (tiles > INT32_MAX) return hipErrorInvalidValue;
   }
-  for (int i = n; i <= kMaxPieces; i++) a.tile_start[i] = (int32_t)tiles;
+  for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
   const dim3 grid((unsigned)tiles), block(kBlock);
   auto go = [&](auto kernel) {
@@ -375,12 +405,22 @@ hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, 
     else kernel<<<grid, block, 0, stream>>>(a);
   };
   switch (kind) {
-    case PartialKind::kFirst: go(partial_kernel<PartialKind::kFirst>); break;
-    case PartialKind::kMid: go(partial_kernel<PartialKind::kMid>); break;
-    case PartialKind::kLast: go(partial_kernel<PartialKind::kLast>); break;
-    default: go(partial_kernel<PartialKind::kLastFwd>); break;
+    case PartialKind::kFirst: go(partial_kernel<PartialKind::kFirst, NP>); break;
+    case PartialKind::kMid: go(partial_kernel<PartialKind::kMid, NP>); break;
+    case PartialKind::kLast: go(partial_kernel<PartialKind::kLast, NP>); break;
+    default: go(partial_kernel<PartialKind::kLastFwd, NP>); break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
+                           hipEvent_t start, hipEvent_t stop) {
+  if (n <= 0) return hipSuccess;
+  if (n > kMaxPieces) return hipErrorInvalidValue;
+  if (n <= 16) return launch_partials_np<16>(kind, pieces, n, stream, start, stop);
+  return launch_partials_np<kMaxPieces>(kind, pieces, n, stream, start, stop);
 }
 
 hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream) {
