@@ -530,6 +530,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain BYTES copy through the copy kernel (counter calibration)")
+    ap.add_argument("--ring-only", action="store_true",
+                    help="only the timed all-reduce steps and the per-launch pass (for profiler runs)")
     ap.add_argument("--moe-probe", action="store_true",
                     help="only run --steps fused MoE dispatch + combine calls (gather kernel profiles)")
     args = ap.parse_args()
@@ -579,10 +581,14 @@ def main():
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
 
-    log("bench: per-step times with inputs restored before each step")
-    restored = percentiles(restored_steps(step, bufs, max(20, args.steps)))
-    log("bench: plain 1 GiB copy (copy roofline)")
-    copy_gbs = copy_roofline(ccr)
+    restored = copy_gbs = None
+    if not args.ring_only:
+        log("bench: per-step times with inputs restored before each step")
+        restored = percentiles(restored_steps(step, bufs, max(20, args.steps)))
+        log("bench: plain 1 GiB copy (copy roofline)")
+        copy_gbs = copy_roofline(ccr)
+    if args.ring_only:
+        args.no_gemm = args.no_cpu = True
 
     gemm = pp = occ = launch = None
     if not args.no_gemm:
@@ -640,17 +646,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "pieces_kernel<kReduceBf16, 2, false>: one reduce-scatter hop, all 8 ranks",
+                     "kernel": "pieces_kernel<kReduceBf16, 2, false, 8>: one reduce-scatter hop, all 8 ranks",
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
                      "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
         "protocol": {"timed_region": f"{args.steps} back-to-back in-place all-reduces, host clock, "
                                      "synchronised on both sides",
-                     "restored_inputs": dict(restored, note="inputs restored by a device copy before "
-                                             "each step, outside HIP events around the step")},
-        "copy_roofline": {"gbs": round(copy_gbs, 1), "frac_of_8tbs": round(copy_gbs / HBM_PEAK_GBS, 4),
-                          "reduce_hop_frac_of_copy": round(red_gbs / copy_gbs, 4),
-                          "what": "copy kernel, one 1 GiB copy, full CUs"},
+                     "restored_inputs": None if restored is None else dict(
+                         restored, note="inputs restored by a device copy before each step, "
+                                        "outside HIP events around the step")},
+        "copy_roofline": None if copy_gbs is None else {
+            "gbs": round(copy_gbs, 1), "frac_of_8tbs": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "reduce_hop_frac_of_copy": round(red_gbs / copy_gbs, 4),
+            "what": "copy kernel, one 1 GiB copy, full CUs"},
         "reduce_forward_kernel": None if not fwd["ms"] else {
             "achieved": round(fwd["bytes"] / (fwd["ms"] * 1e6), 1), "launches": fwd["launches"],
             "mean_launch_us": round(fwd["ms"] * 1e3 / max(1, fwd["launches"]), 3)},
