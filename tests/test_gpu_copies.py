@@ -165,3 +165,74 @@ def test_sdma_watchdog_reports_a_slow_operation(ccr_mod, sync):
         ref = oracle.ring_allreduce(xs)
         for q, t in enumerate(ts):
             np.testing.assert_array_equal(to_host(t), ref[q])
+
+
+@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+def test_sendrecv_edges(ccr_mod, mode):
+    """Nothing to send; more transfers than slots; transfers smaller than one
+    16-byte unit per striped engine; a ragged last chunk."""
+    import torch
+    say(f"sendrecv edges {mode}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, staging_chunk_bytes=4096,
+                                           staging_slots=2, dma_stripe=7)) as c:
+        ccr_mod.ccr_sendrecv(c, [], [])
+        e = torch.zeros(0, dtype=torch.uint8, device="cuda")
+        ccr_mod.ccr_sendrecv(c, [e], [torch.zeros(0, dtype=torch.uint8, device="cuda")])
+        for m, nbytes in ((9, 4096 * 2 + 16), (3, 48), (2, 16), (5, 4096 * 5 - 16)):
+            rng = np.random.default_rng(m * 1000 + nbytes)
+            srcs = [rng.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(m)]
+            s = [raw_to_dev(x) for x in srcs]
+            r = [torch.zeros_like(x) for x in s]
+            ccr_mod.ccr_sendrecv(c, s, r)
+            torch.cuda.synchronize()
+            dsts, _ = oracle.staged_copy(srcs, 4096, 2)
+            for a, b in zip(r, dsts):
+                assert to_host(a).tobytes() == b.tobytes(), f"m={m} nbytes={nbytes}"
+
+
+@pytest.mark.parametrize("mode,chunk", [("kernel", 0), ("sdma", 4096), ("sdma", 0)])
+def test_alltoall_skewed_flows(ccr_mod, mode, chunk):
+    """One flow of 10,000 rows among flows of 0-3 rows, cut into 4 KiB chunks
+    on the SDMA engines (so the large flow spans many chunks and interleaves
+    with the small ones) or with the automatic chunk size."""
+    import torch
+    R, row_bytes = 8, 64
+    rng = np.random.default_rng(77)
+    counts = rng.integers(0, 4, (R, R))
+    counts[3, 5] = 10000
+    sends = [rng.integers(0, 256, int(counts[r].sum()) * row_bytes, dtype=np.uint8) for r in range(R)]
+    ref = oracle.alltoall(sends, counts, row_bytes)
+    say(f"alltoall skewed {mode} chunk={chunk}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, dma_chunk_bytes=chunk)) as c:
+        s = [raw_to_dev(x) for x in sends]
+        r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
+        ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
+        torch.cuda.synchronize()
+        for a, b in zip(r, ref):
+            assert to_host(a)[:b.size].tobytes() == b.tobytes()
+
+
+@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+def test_alltoall_max_ranks_and_empty(ccr_mod, mode):
+    """64 ranks (4,096 flows, many of them empty), then an exchange with no
+    rows at all."""
+    import torch
+    R, row_bytes = 64, 32
+    rng = np.random.default_rng(64)
+    counts = rng.integers(0, 3, (R, R))
+    sends = [rng.integers(0, 256, int(counts[r].sum()) * row_bytes, dtype=np.uint8) for r in range(R)]
+    ref = oracle.alltoall(sends, counts, row_bytes)
+    say(f"alltoall R=64 {mode}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode)) as c:
+        s = [raw_to_dev(x) if x.size else torch.zeros(16, dtype=torch.uint8, device="cuda") for x in sends]
+        r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
+        ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
+        torch.cuda.synchronize()
+        for a, b in zip(r, ref):
+            assert to_host(a)[:b.size].tobytes() == b.tobytes()
+        zero = np.zeros((R, R), np.int64)
+        keep = [to_host(x) for x in r[:3]]
+        ccr_mod.ccr_alltoall(c, s, r, zero, row_bytes)
+        torch.cuda.synchronize()
+        for a, b in zip(r[:3], keep):
+            assert to_host(a).tobytes() == b.tobytes()
