@@ -214,6 +214,7 @@ ccr_status_t check_ctx(ccr_ctx* ctx) {
 // nbytes bytes lie inside one HIP allocation.
 ccr_status_t check_dev_ptr(ccr_ctx* ctx, const void* p, int64_t nbytes, const char* what,
                            int index) {
+  if (nbytes == 0) return CCR_OK;  // never dereferenced (an empty tensor may even be NULL)
   if (!p) return fail(CCR_ERR_INVALID_ARG, "%s[%d] is NULL", what, index);
   if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
     return fail(CCR_ERR_INVALID_ARG, "%s[%d] = %p is not 16-byte aligned", what, index, p);

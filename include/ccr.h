@@ -23,6 +23,8 @@
  *     ccr_last_error() on the same thread.  No entry point aborts or prints.
  *   - Device pointers are caller-owned, must stay valid and unmodified until
  *     the work enqueued on `stream` completes, and must be 16-byte aligned.
+ *     A buffer the call reads or writes zero bytes of is never accessed and
+ *     may be NULL (an empty tensor).
  *     Host arrays of pointers or counts are read during the call only.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     stream-ordered and asynchronous unless stated otherwise: they return

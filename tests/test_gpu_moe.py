@@ -124,16 +124,14 @@ def _fused_case(ccr_mod, R, T, E, K, H, skew=None, reps=1):
         rows = [int(ref["counts"][:, d].sum()) for d in range(R)]
         d_x = [to_dev(x) for x in xs]
         for rep in range(reps):
-            exp = [torch.full((max(1, n), H), -7.0, dtype=torch.bfloat16, device="cuda") for n in rows]
+            # a destination with no rows gets an empty tensor (its pointer may be NULL)
+            exp = [torch.full((n, H), -7.0, dtype=torch.bfloat16, device="cuda") for n in rows]
             ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, ecnt, K, exp)
             out = [torch.zeros(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
             ccr_mod.ccr_moe_combine_fused(c, exp, slot, ecnt, T, K, out)
             torch.cuda.synchronize()
             for d in range(R):
-                got = to_host(exp[d])
-                np.testing.assert_array_equal(got[:rows[d]], ref["exp"][d])
-                if rows[d] == 0:  # nothing may be written to an empty destination
-                    assert (got == to_host(torch.full((1, H), -7.0, dtype=torch.bfloat16))).all()
+                np.testing.assert_array_equal(to_host(exp[d]), ref["exp"][d].reshape(rows[d], H))
             for r in range(R):
                 np.testing.assert_array_equal(to_host(out[r]), np.repeat(xs[r][:, None, :], K, axis=1))
 
