@@ -492,11 +492,13 @@ ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) 
 // (rank c -> c+1 -> ... -> c-1, one hop each).  Each chain is cut into m
 // sub-chains over equal byte ranges, m = E / gcd(R, E) (fewer if pieces
 // would drop below 256 KiB), so the R*m chains spread evenly over the E
-// engines; chain i runs on engine i mod E.  Copies are listed hop by hop;
+// engines; chain i runs on engine i mod E.  Hops before first_hop are
+// already done (an all-reduce's last reduce-scatter hop forwards, which is
+// hop 0).  Copies are listed hop by hop;
 // each waits for the previous link of its chain, and the DMA proxy issues it
 // when that link completes.
 std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, int s, int V,
-                               int esize, int engines) {
+                               int esize, int engines, int first_hop) {
   const int E = std::max(1, engines);
   int m = E / std::gcd(R, E);
   if (const char* e = getenv("CCR_DMA_SPLIT"); e && atoi(e) > 0) m = atoi(e);
@@ -511,7 +513,7 @@ std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, i
   while (m > 1 && widest / m < (256 << 10)) m--;
   std::vector<DmaCopy> out;
   std::vector<int32_t> prev((size_t)R * m, -1);
-  for (int k = 0; k + 1 < R; k++) {
+  for (int k = first_hop; k + 1 < R; k++) {
     for (int c = 0; c < R; c++) {
       const int q = (c + 1 + k) % R, p = (q + R - 1) % R;
       const int64_t b0 = lo[(size_t)c] * esize, nb = (hi[(size_t)c] - lo[(size_t)c]) * esize;
@@ -551,12 +553,13 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   const int V = 16 / esize;
   const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
   const HopKind reduce_fwd = dtype == CCR_F32 ? HopKind::kReduceFwdF32 : HopKind::kReduceFwdBf16;
-  // With compute-unit copies, an all-reduce's last reduce-scatter hop also
-  // forwards the reduced chunk to the next rank (rank q writes chunk q into
-  // bufs[q] and bufs[q+1] in one pass), which is all-gather hop 0.  Within
-  // that hop each forwarded element is written only by the thread that read
-  // the same element, and no other operation of the hop touches it.
-  const bool fuse = which == kWhichAllreduce && ctx->cfg.copy_mode == CCR_COPY_KERNEL;
+  // An all-reduce's last reduce-scatter hop also forwards the reduced chunk
+  // to the next rank (rank q writes chunk q into bufs[q] and bufs[q+1] in
+  // one pass), which is all-gather hop 0; with either copy mode the
+  // all-gather then starts at hop 1.  Within that hop each forwarded element
+  // is written only by the thread that read the same element, and no other
+  // operation of the hop touches it.
+  const bool fuse = which == kWhichAllreduce;
   // bf16 with the running partial carried in fp32 between ranks (R = 2 has a
   // single hop, identical to per-hop rounding).  Partials live in context
   // scratch, double-buffered by hop parity, indexed by offset in the chunk.
@@ -642,7 +645,8 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
     }
     if (which != kWhichRS && sdma) {
       CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
-      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, ctx->dma->engine_count()),
+      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, ctx->dma->engine_count(),
+                                        fuse ? 1 : 0),
                          ag));
     } else if (which != kWhichRS) {
       if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));

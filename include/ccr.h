@@ -360,7 +360,7 @@ ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *st
  * synchronises the context's streams and the device, then reports, for
  * `kind` (0 = reduce kernels, 1 = copy kernels, 2 = SDMA copies,
  * 3 = reduce-and-forward kernels, the last reduce-scatter hop of an
- * all-reduce with kernel copies, 4 = fused MoE gathers, 2 bytes per byte of
+ * all-reduce, 4 = fused MoE gathers, 2 bytes per byte of
  * payload), the number of launches since the last
  * enable, the sum of their durations in milliseconds, and their algorithmic
  * bytes (a reduce moves 3 bytes per byte of payload: read local, read
