@@ -526,6 +526,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--slices", type=int, default=None)
     ap.add_argument("--overlap", type=int, default=0)
+    ap.add_argument("--copy-mode", choices=("kernel", "sdma"), default="kernel",
+                    help="all-gather copies of the timed all-reduce (default: kernel)")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -558,7 +560,7 @@ def main():
     log(f"bench: {w.name}: generating inputs")
     xs = workloads.ring_inputs(w)
     bufs = [to_dev(x) for x in xs]
-    cfg = dict(slices=S, overlap=bool(args.overlap))
+    cfg = dict(slices=S, overlap=bool(args.overlap), copy_mode=args.copy_mode)
     ctx = ccr.Context(0, ccr.Config(**cfg))
     step = lambda: ccr.ccr_allreduce(ctx, bufs)  # noqa: E731
     log(f"bench: warmup {args.warmup}")
@@ -577,6 +579,7 @@ def main():
     red = ccr.ccr_profile_read(ctx, "reduce")
     fwd = ccr.ccr_profile_read(ctx, "reduce_forward")
     cpy = ccr.ccr_profile_read(ctx, "copy_kernel")
+    dma = ccr.ccr_profile_read(ctx, "sdma")
     ccr.ccr_profile_enable(ctx, False)
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
@@ -640,7 +643,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "ranks": R, "count_per_rank": count, "slices": S,
-                   "overlap": bool(args.overlap), "copy_mode": "kernel",
+                   "overlap": bool(args.overlap), "copy_mode": args.copy_mode,
                    "values": "normal(0, 1e-3)", "accumulation": "fp32 add, bf16 per hop"},
         "hbm": {"algorithmic_gbs": round(algo, 1), "frac_of_8tbs": round(algo / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -662,6 +665,9 @@ def main():
         "reduce_forward_kernel": None if not fwd["ms"] else {
             "achieved": round(fwd["bytes"] / (fwd["ms"] * 1e6), 1), "launches": fwd["launches"],
             "mean_launch_us": round(fwd["ms"] * 1e3 / max(1, fwd["launches"]), 3)},
+        "sdma_copies": None if not dma["launches"] else {
+            "jobs": dma["launches"], "bytes": dma["bytes"], "ms": round(dma["ms"], 4),
+            "gbs": round(dma["bytes"] / (dma["ms"] * 1e6), 1) if dma["ms"] else None},
         "copy_kernel": None if cpy_gbs is None else {
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
