@@ -938,37 +938,38 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
       return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
     return CCR_OK;
   }
-  hipStream_t fill = ctx->s_a, drain = ctx->s_b;
-
+  // Compute-unit copies: rounds of P chunks on one stream.  A round fills
+  // slots 0..P-1 in one launch and drains them in the next; stream order
+  // keeps each slot idle -> filling -> draining -> idle, and a slot is
+  // refilled only after its previous chunk has drained.  Filling and
+  // draining are both compute-unit copies sharing HBM, so running them on
+  // two streams would gain nothing on one GPU -- and a cross-stream wait
+  // costs ~27 us of host time on this runtime.
+  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  CCR_TRY(order_after(ctx, 0, caller, s));
   const int P = ctx->cfg.staging_slots;
   const int64_t C = ctx->cfg.staging_chunk_bytes;
-  // events: 0 fork, 1-2 joins, then filled[p] = 3 + p, drained[p] = 3 + P + p
-  CCR_TRY(events(ctx, (size_t)(3 + 2 * P)));
-  CCR_TRY(order_after(ctx, 0, caller, fill));
-  HIP_TRY(hipStreamWaitEvent(drain, ctx->ev[0], 0));
-  std::vector<bool> used((size_t)P, false);
+  std::vector<Piece> fills, drains;
+  auto flush = [&]() -> ccr_status_t {
+    CCR_TRY(copy_pieces(ctx, fills.data(), fills.size(), s));
+    CCR_TRY(copy_pieces(ctx, drains.data(), drains.size(), s));
+    fills.clear();
+    drains.clear();
+    return CCR_OK;
+  };
   int64_t chunk = 0;
   for (int m = 0; m < n; m++) {
     for (int64_t off = 0; off < nbytes; off += C, chunk++) {
       const int p = (int)(chunk % P);
       const int64_t len = std::min<int64_t>(C, nbytes - off);
       char* slot = ctx->staging + (int64_t)p * C;
-      hipEvent_t filled = ctx->ev[(size_t)(3 + p)], drained = ctx->ev[(size_t)(3 + P + p)];
-      // idle -> filling: only once the slot's previous chunk has drained
-      if (used[(size_t)p]) HIP_TRY(hipStreamWaitEvent(fill, drained, 0));
-      Piece in{slot, static_cast<const char*>(send[m]) + off, len};
-      CCR_TRY(copy_pieces(ctx, &in, 1, fill));
-      HIP_TRY(hipEventRecord(filled, fill));
-      // filling -> draining -> idle
-      HIP_TRY(hipStreamWaitEvent(drain, filled, 0));
-      Piece out{static_cast<char*>(recv[m]) + off, slot, len};
-      CCR_TRY(copy_pieces(ctx, &out, 1, drain));
-      HIP_TRY(hipEventRecord(drained, drain));
-      used[(size_t)p] = true;
+      fills.push_back(Piece{slot, static_cast<const char*>(send[m]) + off, len});
+      drains.push_back(Piece{static_cast<char*>(recv[m]) + off, slot, len});
+      if (p == P - 1) CCR_TRY(flush());
     }
   }
-  CCR_TRY(order_after(ctx, 1, fill, caller));
-  CCR_TRY(order_after(ctx, 2, drain, caller));
+  if (!fills.empty()) CCR_TRY(flush());
+  CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
 }
 

@@ -232,8 +232,12 @@ ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void *const *bufs, int R, int64_t cou
  * Point-to-point transfers through the context's staging pool (HOCCL
  * §3.3.1 DMA-RNIC chunk pipelining; slot states of Fig. 4).  Transfer m
  * copies nbytes from send[m] to recv[m], chunk by chunk: chunk i is copied
- * into slot i mod staging_slots (filling) on one stream and out of it
- * (draining) on another, and a slot is refilled only after it has drained.
+ * into slot i mod staging_slots (filling) and out of it (draining), and a
+ * slot is refilled only after it has drained.  SDMA copies: the DMA proxy
+ * runs each slot's state machine, fills and drains on different engines, so
+ * they overlap.  Kernel copies: rounds of staging_slots chunks on one
+ * stream, one launch filling the round's slots and one draining them (both
+ * stages share the compute units and HBM, so there is nothing to overlap).
  * Transfers run in order m = 0..n-1.  send/recv: host arrays of n device
  * pointers; the 2n ranges must not overlap.  nbytes must be a multiple of 16.
  * ---------------------------------------------------------------------- */
