@@ -569,10 +569,10 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   if (partials) CCR_TRY(ensure_partials(ctx, 2 * (int64_t)R * Lc * 4));
   // Reduce-scatter runs on the CU-masked stream when a budget is set, else
   // directly on the caller's stream.  All-gather follows it on the same
-  // stream, or on the second side stream when overlap is on.  With SDMA
-  // copies the all-gather of each slice is one DMA job whose handshake sits
-  // on the second side stream, so the reduce-scatter of the next slice keeps
-  // going while the engines copy.
+  // stream, or, with several slices, on the second side stream when overlap
+  // is on.  With SDMA copies the all-gather of each slice is one DMA job;
+  // with several slices its handshake sits on the second side stream, so
+  // the reduce-scatter of the next slice keeps going while the engines copy.
   const bool sdma = ctx->cfg.copy_mode == CCR_COPY_SDMA && which != kWhichRS;
   if (sdma) CCR_TRY(ensure_dma(ctx));
   // Slices exist so that one slice's all-gather can run while the next
@@ -583,7 +583,11 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   const bool pipelined = which == kWhichAllreduce && (ctx->cfg.overlap || sdma);
   const int S = pipelined ? ctx->cfg.slices : 1;
   hipStream_t rs = ctx->masked ? ctx->s_a : caller;
-  hipStream_t ag = (ctx->cfg.overlap || sdma) ? ctx->s_b : rs;
+  // A second stream only when there is something to overlap: with a single
+  // slice the all-gather (kernel copies or the SDMA job's gate) follows the
+  // reduce-scatter on its stream, which saves two cross-stream waits (each
+  // ~27 us of host time on this runtime when the work is still running).
+  hipStream_t ag = (S > 1 && (ctx->cfg.overlap || sdma)) ? ctx->s_b : rs;
   const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
   CCR_TRY(events(ctx, ev_slice0 + (size_t)S));
   if (rs != caller || ag != caller) {
