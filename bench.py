@@ -645,6 +645,7 @@ def main():
         "config": {"workload": w.name, "ranks": R, "count_per_rank": count, "slices": S,
                    "overlap": bool(args.overlap), "copy_mode": args.copy_mode,
                    "values": "normal(0, 1e-3)", "accumulation": "fp32 add, bf16 per hop"},
+        "algbw_gbs": round(esize * count / t / 1e9, 2),
         "hbm": {"algorithmic_gbs": round(algo, 1), "frac_of_8tbs": round(algo / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
