@@ -180,6 +180,11 @@ std::string check_schedule_problem(const ScheduleProblem& p, bool need_bandwidth
       snprintf(msg, sizeof msg, "peer[%d] = %d is not -1 or another GPU of the same node", u, w);
       return msg;
     }
+    if (p.peer[w] != u) {  // Eq. 4 charges both copies of the pair to the edge (u, peer u)
+      snprintf(msg, sizeof msg, "peer[%d] = %d but peer[%d] = %d: peers must be mutual", u, w, w,
+               p.peer[w]);
+      return msg;
+    }
   }
   for (int64_t i = 0; i < (int64_t)p.G * p.G; i++) {
     if (p.C[i] < 0 || p.C[i] > kMaxFlowBytes) {

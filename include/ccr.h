@@ -160,8 +160,8 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
  * an origin traffic matrix C: C[u*G + v] = bytes GPU u sends to GPU v
  * (int64, >= 0, at most 2^40; the diagonal is ignored).  node[u] (>= 0)
  * names u's scale-up domain; flows between nodes go over RDMA.  peer[u] is
- * u's symmetric peer in the same node (Figure 6 pairs 0-1 and 2-3), or -1
- * for none: an inter-node flow u -> v is sent as a forwarding copy on the
+ * u's symmetric peer in the same node (Figure 6 pairs 0-1 and 2-3; peers are
+ * mutual: peer[peer[u]] == u), or -1 for none: an inter-node flow u -> v is sent as a forwarding copy on the
  * scale-up edge (u, peer[u]), the RDMA transfer, and a forwarding copy on
  * (peer[v], v) (Eq. 2).  1 <= G <= 256.  All arrays are host memory, read
  * during the call only.
@@ -187,7 +187,7 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
  *   (query them with NULL arrays and zero maxima).
  * Errors: CCR_ERR_INVALID_ARG for NULL arrays, G out of range, negative or
  * oversized bytes, a node id < 0, or a peer that is not -1 or another GPU of
- * the same node.
+ * the same node whose own peer is u.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t stage, kind, src, dst;

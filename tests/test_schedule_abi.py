@@ -118,6 +118,8 @@ def test_truncated_output_reports_full_counts():
     dict(peer=[1, 0, 3, 3]),                  # own peer
     dict(peer=[2, 0, 3, 2]),                  # peer in another node
     dict(peer=[1, 0, 3, 9]),                  # out of range
+    dict(peer=[1, -1, 3, 2]),                 # not mutual (0 names 1, 1 names nobody)
+    dict(node=[0, 0, 0, 1], peer=[1, 2, 0, -1]),  # not mutual (a cycle)
     dict(C_fix=(0, 1, -5)),                   # negative bytes
     dict(C_fix=(0, 1, (1 << 40) + 1)),        # above the limit
     dict(bw=(0, 1)),
