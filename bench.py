@@ -178,16 +178,27 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             collective(ctx, c)  # first use starts the SDMA proxy
             torch.cuda.synchronize()
             t1 = time_steps(lambda: collective(ctx, c), 3)
-            gemm, coll, span = sorted(window(ctx) for _ in range(3))[1]
+            # A/B interleaved: GEMM alone, then with the collectives, five times;
+            # each run is compared with its own alone windows, so slow drift of
+            # the GEMM's own time (clocks, temperature) does not count as slowdown
+            a_ms, b_runs = [], []
+            for _ in range(5):
+                a_ms.append(window()[0])
+                b_runs.append(window(ctx))
+            alone_i = sorted(a_ms)[2]
+            gemm, coll, span = sorted(b_runs)[2]
             i_coll = contention(ctx)
             out["runs"].append({
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
                 "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
-                "gemm_ms": round(gemm, 3), "slowdown_pct": round(100.0 * (gemm / alone - 1.0), 2),
+                "gemm_alone_ms": round(alone_i, 3),
+                "gemm_ms": round(gemm, 3), "slowdown_pct": round(100.0 * (gemm / alone_i - 1.0), 2),
+                "slowdown_pct_spread": [round(100.0 * (min(r[0] for r in b_runs) / alone_i - 1.0), 2),
+                                        round(100.0 * (max(r[0] for r in b_runs) / alone_i - 1.0), 2)],
                 "collective_alone_ms": round(t1 * 1e3, 4),
                 "collectives_under_load_ms": round(coll, 3),
                 "makespan_ms": round(span, 3),
-                "makespan_over_gemm_alone_pct": round(100.0 * (span / alone - 1.0), 2),
+                "makespan_over_gemm_alone_pct": round(100.0 * (span / alone_i - 1.0), 2),
                 "contention_rate": round(i_coll, 4)})
     return out
 
