@@ -537,6 +537,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--slices", type=int, default=None)
     ap.add_argument("--overlap", type=int, default=0)
+    ap.add_argument("--bf16-acc", choices=("per_hop", "fp32_partials"), default="per_hop",
+                    help="bf16 accumulation of the timed all-reduce (default: per_hop)")
     ap.add_argument("--copy-mode", choices=("kernel", "sdma"), default="kernel",
                     help="all-gather copies of the timed all-reduce (default: kernel)")
     ap.add_argument("--no-gemm", action="store_true")
@@ -571,7 +573,7 @@ def main():
     log(f"bench: {w.name}: generating inputs")
     xs = workloads.ring_inputs(w)
     bufs = [to_dev(x) for x in xs]
-    cfg = dict(slices=S, overlap=bool(args.overlap), copy_mode=args.copy_mode)
+    cfg = dict(slices=S, overlap=bool(args.overlap), copy_mode=args.copy_mode, bf16_acc=args.bf16_acc)
     ctx = ccr.Context(0, ccr.Config(**cfg))
     step = lambda: ccr.ccr_allreduce(ctx, bufs)  # noqa: E731
     log(f"bench: warmup {args.warmup}")
@@ -655,13 +657,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "ranks": R, "count_per_rank": count, "slices": S,
                    "overlap": bool(args.overlap), "copy_mode": args.copy_mode,
-                   "values": "normal(0, 1e-3)", "accumulation": "fp32 add, bf16 per hop"},
+                   "values": "normal(0, 1e-3)",
+                   "accumulation": "fp32 add, bf16 per hop" if args.bf16_acc == "per_hop"
+                   else "fp32 partials between hops, bf16 at the last hop"},
         "algbw_gbs": round(esize * count / t / 1e9, 2),
         "hbm": {"algorithmic_gbs": round(algo, 1), "frac_of_8tbs": round(algo / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "pieces_kernel<kReduceBf16, 2, false, 8>: one reduce-scatter hop, all 8 ranks",
+                     "traffic": measured_traffic() if args.bf16_acc == "per_hop" else None,
+                     "kernel": "pieces_kernel<kReduceBf16, 2, false, 8>: one reduce-scatter hop, all 8 ranks"
+                               if args.bf16_acc == "per_hop" else
+                               "partial_kernel<kFirst/kMid/kLast*, 8>: the reduce-scatter hops with fp32 partials",
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
                      "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
