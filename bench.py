@@ -667,7 +667,7 @@ def main():
                      "traffic": measured_traffic() if args.bf16_acc == "per_hop" else None,
                      "kernel": "pieces_kernel<kReduceBf16, 2, false, 8>: one reduce-scatter hop, all 8 ranks"
                                if args.bf16_acc == "per_hop" else
-                               "partial_kernel<kFirst/kMid/kLast*, 8>: the reduce-scatter hops with fp32 partials",
+                               "partial_kernel<kFirst/kMid/kLast*, 16>: the reduce-scatter hops with fp32 partials",
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
                      "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},

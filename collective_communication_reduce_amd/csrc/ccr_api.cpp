@@ -249,6 +249,8 @@ struct Range {
 };
 
 ccr_status_t check_disjoint(std::vector<Range> r, const char* what) {
+  // an empty range touches no byte and cannot conflict
+  r.erase(std::remove_if(r.begin(), r.end(), [](const Range& x) { return x.hi <= x.lo; }), r.end());
   std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
   for (size_t i = 1; i < r.size(); i++)
     if (r[i].lo < r[i - 1].hi)
@@ -1156,6 +1158,35 @@ ccr_status_t check_rank_ptrs(ccr_ctx* ctx, const void* const* p, int R, const in
   return CCR_OK;
 }
 
+// The buffers of a call, each marked written or read-only.  No written
+// buffer may overlap any other buffer of the call (read-only buffers may
+// overlap each other); empty buffers are ignored.
+struct CallBuf {
+  uintptr_t lo, hi;
+  bool written;
+  const char* what;
+  int rank;
+};
+
+void add_bufs(std::vector<CallBuf>* b, const void* const* p, int R, const int64_t* nbytes,
+              bool per_rank, bool written, const char* what) {
+  for (int r = 0; r < R; r++) {
+    const int64_t n = nbytes[per_rank ? r : 0];
+    if (n <= 0) continue;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p[r]);
+    b->push_back(CallBuf{a, a + (uintptr_t)n, written, what, r});
+  }
+}
+
+ccr_status_t check_writes_disjoint(const std::vector<CallBuf>& b) {
+  for (size_t i = 0; i < b.size(); i++)
+    for (size_t j = i + 1; j < b.size(); j++)
+      if ((b[i].written || b[j].written) && b[i].lo < b[j].hi && b[j].lo < b[i].hi)
+        return fail(CCR_ERR_INVALID_ARG, "%s[%d] and %s[%d] overlap", b[i].what, b[i].rank,
+                    b[j].what, b[j].rank);
+  return CCR_OK;
+}
+
 }  // namespace
 
 ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t* const* src_tok,
@@ -1174,6 +1205,13 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
   CCR_TRY(check_rank_ptrs(ctx, send, R, &sb, false, "send"));
   CCR_TRY(check_rank_ptrs(ctx, recv, R, rb.data(), true, "recv"));
   CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
+  std::vector<CallBuf> bufs;
+  add_bufs(&bufs, x, R, &xb, false, false, "x");
+  add_bufs(&bufs, reinterpret_cast<const void* const*>(src_tok), R, &ib, false, false, "src_tok");
+  add_bufs(&bufs, send, R, &sb, false, true, "send");
+  add_bufs(&bufs, recv, R, rb.data(), true, true, "recv");
+  add_bufs(&bufs, exp, R, rb.data(), true, true, "exp");
+  CCR_TRY(check_writes_disjoint(bufs));
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
@@ -1207,6 +1245,13 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   CCR_TRY(check_rank_ptrs(ctx, recv, R, rb.data(), true, "recv"));
   CCR_TRY(check_rank_ptrs(ctx, send, R, &sb, false, "send"));
   CCR_TRY(check_rank_ptrs(ctx, out, R, &sb, false, "out"));
+  std::vector<CallBuf> bufs;
+  add_bufs(&bufs, exp, R, rb.data(), true, false, "exp");
+  add_bufs(&bufs, reinterpret_cast<const void* const*>(slot), R, &ib, false, false, "slot");
+  add_bufs(&bufs, recv, R, rb.data(), true, true, "recv");
+  add_bufs(&bufs, send, R, &sb, false, true, "send");
+  add_bufs(&bufs, out, R, &sb, false, true, "out");
+  CCR_TRY(check_writes_disjoint(bufs));
   hipStream_t caller = static_cast<hipStream_t>(stream);
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
@@ -1304,32 +1349,6 @@ ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int6
   return CCR_OK;
 }
 
-// No buffer the gather writes may overlap any other buffer of the call
-// (read-only buffers may overlap each other).  written_exp: the expert-major
-// buffers are the ones written (dispatch), else the per-rank rows are.
-ccr_status_t check_moe_disjoint(const MoeShape& m, void* const* own, int64_t own_bytes,
-                                void* const* exp, const int64_t* exp_bytes, bool written_exp) {
-  struct B {
-    uintptr_t lo, hi;
-    bool written;
-    const char* what;
-    int rank;
-  };
-  std::vector<B> b;
-  for (int i = 0; i < m.R; i++) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(own[i]);
-    b.push_back(B{a, a + (uintptr_t)own_bytes, !written_exp, written_exp ? "x" : "out", i});
-    const uintptr_t e = reinterpret_cast<uintptr_t>(exp[i]);
-    if (exp_bytes[i] > 0) b.push_back(B{e, e + (uintptr_t)exp_bytes[i], written_exp, "exp", i});
-  }
-  for (size_t i = 0; i < b.size(); i++)
-    for (size_t j = i + 1; j < b.size(); j++)
-      if ((b[i].written || b[j].written) && b[i].lo < b[j].hi && b[j].lo < b[i].hi)
-        return fail(CCR_ERR_INVALID_ARG, "%s[%d] and %s[%d] overlap", b[i].what, b[i].rank,
-                    b[j].what, b[j].rank);
-  return CCR_OK;
-}
-
 }  // namespace
 
 ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void* const* x,
@@ -1346,7 +1365,11 @@ ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void* const* x,
   CCR_TRY(check_rank_ptrs(ctx, x, R, &xb, false, "x"));
   CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(src_tok), R, &ib, false, "src_tok"));
   CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
-  CCR_TRY(check_moe_disjoint(m, const_cast<void* const*>(x), xb, exp, rb.data(), true));
+  std::vector<CallBuf> bufs;
+  add_bufs(&bufs, x, R, &xb, false, false, "x");
+  add_bufs(&bufs, reinterpret_cast<const void* const*>(src_tok), R, &ib, false, false, "src_tok");
+  add_bufs(&bufs, exp, R, rb.data(), true, true, "exp");
+  CCR_TRY(check_writes_disjoint(bufs));
   return moe_gather(ctx, 0, m, h_ecnt, const_cast<void* const*>(x), src_tok, exp,
                     static_cast<hipStream_t>(stream));
 }
@@ -1364,7 +1387,11 @@ ccr_status_t ccr_moe_combine_fused(ccr_ctx_t ctx, const void* const* exp, const 
   CCR_TRY(check_rank_ptrs(ctx, exp, R, rb.data(), true, "exp"));
   CCR_TRY(check_rank_ptrs(ctx, reinterpret_cast<const void* const*>(slot), R, &ib, false, "slot"));
   CCR_TRY(check_rank_ptrs(ctx, out, R, &ob, false, "out"));
-  CCR_TRY(check_moe_disjoint(m, out, ob, const_cast<void* const*>(exp), rb.data(), false));
+  std::vector<CallBuf> bufs;
+  add_bufs(&bufs, exp, R, rb.data(), true, false, "exp");
+  add_bufs(&bufs, reinterpret_cast<const void* const*>(slot), R, &ib, false, false, "slot");
+  add_bufs(&bufs, out, R, &ob, false, true, "out");
+  CCR_TRY(check_writes_disjoint(bufs));
   return moe_gather(ctx, 1, m, h_ecnt, out, slot, const_cast<void* const*>(exp),
                     static_cast<hipStream_t>(stream));
 }

@@ -253,24 +253,34 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
   return r;
 }
 
-// One group of 8 elements: out = in + float(loc).
+// One group of 8 elements: out = in + float(loc).  The loads and the
+// stores are split so that a tile issues all its loads before its first
+// store (the compiler may not move a load above a store that could alias).
 template <PartialKind K>
-__device__ __forceinline__ void partial_group(const PartialPiece& pc, int64_t g) {
-  float loc[8], in[8], acc[8];
-  unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.loc)[g], loc);
+__device__ __forceinline__ void partial_load(const PartialPiece& pc, int64_t g, u32x4* loc,
+                                             f32x4* in) {
+  *loc = reinterpret_cast<const u32x4*>(pc.loc)[g];
   if constexpr (K == PartialKind::kFirst) {
-    unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.in)[g], in);
+    float f[8];
+    unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.in)[g], f);
+    in[0] = f32x4{f[0], f[1], f[2], f[3]};
+    in[1] = f32x4{f[4], f[5], f[6], f[7]};
   } else {
-    const f32x4 a = reinterpret_cast<const f32x4*>(pc.in)[2 * g];
-    const f32x4 b = reinterpret_cast<const f32x4*>(pc.in)[2 * g + 1];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      in[j] = a[j];
-      in[4 + j] = b[j];
-    }
+    in[0] = reinterpret_cast<const f32x4*>(pc.in)[2 * g];
+    in[1] = reinterpret_cast<const f32x4*>(pc.in)[2 * g + 1];
   }
+}
+
+template <PartialKind K>
+__device__ __forceinline__ void partial_store(const PartialPiece& pc, int64_t g, u32x4 locw,
+                                              const f32x4* in) {
+  float loc[8], acc[8];
+  unpack_bf16x8(locw, loc);
 #pragma unroll
-  for (int j = 0; j < 8; j++) acc[j] = in[j] + loc[j];
+  for (int j = 0; j < 4; j++) {
+    acc[j] = in[0][j] + loc[j];
+    acc[4 + j] = in[1][j] + loc[4 + j];
+  }
   if constexpr (K == PartialKind::kFirst || K == PartialKind::kMid) {
     reinterpret_cast<f32x4*>(pc.out)[2 * g] = f32x4{acc[0], acc[1], acc[2], acc[3]};
     reinterpret_cast<f32x4*>(pc.out)[2 * g + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
@@ -309,10 +319,26 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
   const int64_t ngroups = pc.n >> 3;
   const int64_t tile = b - a.tile_start[lo];
   const int64_t first = tile * (int64_t)(kBlock * kPartialUnroll);
+  if (first + kBlock * kPartialUnroll <= ngroups) {  // whole tile in range (uniform)
+    u32x4 loc[kPartialUnroll];
+    f32x4 in[kPartialUnroll][2];
 #pragma unroll
-  for (int u = 0; u < kPartialUnroll; u++) {
-    const int64_t g = first + u * kBlock + threadIdx.x;
-    if (g < ngroups) partial_group<K>(pc, g);
+    for (int u = 0; u < kPartialUnroll; u++)
+      partial_load<K>(pc, first + u * kBlock + threadIdx.x, &loc[u], in[u]);
+#pragma unroll
+    for (int u = 0; u < kPartialUnroll; u++)
+      partial_store<K>(pc, first + u * kBlock + threadIdx.x, loc[u], in[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPartialUnroll; u++) {
+      const int64_t g = first + u * kBlock + threadIdx.x;
+      if (g < ngroups) {
+        u32x4 loc;
+        f32x4 in[2];
+        partial_load<K>(pc, g, &loc, in);
+        partial_store<K>(pc, g, loc, in);
+      }
+    }
   }
   const int tail = (int)(pc.n & 7);
   if (tail > 0 && tile == ngroups / (kBlock * kPartialUnroll) && (int)threadIdx.x < tail)

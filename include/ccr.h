@@ -34,6 +34,13 @@
  *   - A count of zero is a successful no-op.
  *   - A context is bound to one device and must not be used from two host
  *     threads at once.
+ *   - Some calls work through context-owned device scratch: the bf16
+ *     all-reduce / reduce-scatter with fp32 partials, ccr_sendrecv (staging
+ *     slots) and ccr_moe_plan (count scratch).  Two such calls on one
+ *     context that are enqueued on different streams with nothing ordering
+ *     them may run at the same time and race on that scratch; keep them on
+ *     one stream or order the streams with events.  Every other call keeps
+ *     no device state between launches.
  */
 #ifndef CCR_H
 #define CCR_H
@@ -281,8 +288,12 @@ ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void *dst, const void *src, const i
  *   local expert, then source rank, then token).  h_ecnt: host int64
  *   [R*E] (row r = ccr_moe_plan's counts of rank r).  Every rank sends
  *   T*K rows of row_bytes; send/recv/exp[r] must each hold the rows it gets.
+ *   A buffer the call writes (send, recv, exp) must not overlap any other
+ *   buffer of the call, src_tok included.
  * ccr_moe_combine: the exact inverse; out[r] is [T x K x row_bytes] with
  *   out[r] row (t, k) = the expert row that carried token t's k-th choice.
+ *   Written buffers (recv, send, out) must not overlap any other buffer of
+ *   the call, slot included.
  * ---------------------------------------------------------------------- */
 ccr_status_t ccr_moe_topk(ccr_ctx_t ctx, const float *logits, int32_t *topk, int64_t T, int E,
                           int K, void *stream);
@@ -307,7 +318,7 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void *const *exp, const int32_
  * gives; ccr_moe_combine_fused's out equals ccr_moe_combine's.  The copy mode
  * does not apply (row gathers run on compute units).  A buffer the call
  * writes (exp for dispatch, out for combine) must not overlap any other
- * buffer of the call.  The segment table (R records of 16 bytes and R*E of
+ * buffer of the call, the index arrays included.  The segment table (R records of 16 bytes and R*E of
  * 24) is copied to the device on `stream`.  Arguments and errors as for
  * ccr_moe_dispatch / ccr_moe_combine; indices out of range leave their row
  * unwritten. */

@@ -190,3 +190,54 @@ def test_fused_invalid_arguments(ccr_mod):
         # the valid call still works afterwards
         ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, ecnt, K, exp)
         torch.cuda.synchronize()
+
+
+def test_overlapping_buffers_rejected(ccr_mod):
+    """A buffer a call writes may not overlap another buffer of the call,
+    index arrays included; the three-stage and the fused paths alike."""
+    import torch
+    R, T, E, K, H = 2, 16, 4, 2, 8
+    w = workloads.MOE_DISPATCH_BF16
+    xs, logits = workloads.moe_inputs(w, tokens=T, R=R)
+    xs = [x[:, :H].copy() for x in xs]
+    logits = [l[:, :E].copy() for l in logits]
+    say("moe overlapping buffers")
+    with ccr_mod.Context(0) as c:
+        src_tok, slot, ecnt = _plan(ccr_mod, c, logits, E, K, R)
+        rows = [int(ecnt[:, (E // R) * d:(E // R) * (d + 1)].sum()) for d in range(R)]
+        d_x = [to_dev(x) for x in xs]
+        send = [torch.zeros(T * K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        recv = [torch.zeros(max(1, n), H, dtype=torch.bfloat16, device="cuda") for n in rows]
+        exp = [torch.zeros(max(1, n), H, dtype=torch.bfloat16, device="cuda") for n in rows]
+
+        def rejected(fn, *a):
+            with pytest.raises(ccr_mod.CcrError) as e:
+                fn(c, *a)
+            assert e.value.status == ccr_mod.CCR_ERR_INVALID_ARG
+            assert "overlap" in ccr_mod.ccr_last_error()
+
+        # dispatch: send over x, recv over send, exp over recv
+        big = torch.zeros(T * K + T, H, dtype=torch.bfloat16, device="cuda")
+        rejected(ccr_mod.ccr_moe_dispatch, [big[:T], d_x[1]], src_tok, ecnt, K,
+                 [big[T - 1:T - 1 + T * K], send[1]], recv, exp)
+        both = torch.zeros(T * K + max(rows), H, dtype=torch.bfloat16, device="cuda")
+        rejected(ccr_mod.ccr_moe_dispatch, d_x, src_tok, ecnt, K,
+                 [both[:T * K], send[1]], [both[T * K - 1:T * K - 1 + rows[0]], recv[1]], exp)
+        # an expert-major output that runs into the index array
+        combo = torch.zeros(T * K + rows[0] * H // 2, dtype=torch.int32, device="cuda")
+        combo[:T * K] = src_tok[0]
+        exp0 = combo[T * K - 4:T * K - 4 + rows[0] * H // 2].view(torch.bfloat16).view(rows[0], H)
+        rejected(ccr_mod.ccr_moe_dispatch_fused, d_x, [combo[:T * K], src_tok[1]], ecnt, K,
+                 [exp0, exp[1]])
+        # combine: out over send
+        outs = torch.zeros(T * K + T * K, H, dtype=torch.bfloat16, device="cuda")
+        rejected(ccr_mod.ccr_moe_combine, exp, slot, ecnt, T, K, recv,
+                 [outs[:T * K], send[1]],
+                 [outs[T * K - 1:2 * T * K - 1].view(T, K, H), torch.zeros(T, K, H, dtype=torch.bfloat16, device="cuda")])
+        # the valid calls still work and give the three-stage placement
+        ccr_mod.ccr_moe_dispatch(c, d_x, src_tok, ecnt, K, send, recv, exp)
+        exp2 = [torch.zeros_like(e) for e in exp]
+        ccr_mod.ccr_moe_dispatch_fused(c, d_x, src_tok, ecnt, K, exp2)
+        torch.cuda.synchronize()
+        for d in range(R):
+            assert torch.equal(exp[d][:rows[d]], exp2[d][:rows[d]])
