@@ -609,7 +609,7 @@ def main():
     gemm = pp = occ = launch = None
     if not args.no_gemm:
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
-        runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32) for m in ("kernel", "sdma")]
+        runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32, 16) for m in ("kernel", "sdma")]
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
         gemm = overlap_runs(ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs,
                             (8192, 8192, 8192), 20, 6)
