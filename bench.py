@@ -306,6 +306,48 @@ def moe_probe(ccr, workloads, steps):
     log(f"moe probe: {steps} fused dispatch + combine")
 
 
+PROBE_WORKLOADS = ("ring_allreduce_r4_1m_f32", "rs_ag_r32_8m_f32", "pp_sendrecv_4x2048x4096_bf16",
+                   "moe_dispatch_combine_three_stage")
+
+
+def workload_probe(ccr, workloads, name, steps):
+    """Only `steps` calls of one of the other workloads, kernel copies, full
+    CUs (the runs behind their kernel-trace profiles)."""
+    import torch
+    if name in ("ring_allreduce_r4_1m_f32", "rs_ag_r32_8m_f32"):
+        w = workloads.RING_SMALL_F32 if name == "ring_allreduce_r4_1m_f32" else workloads.RS_AG_R32_F32
+        bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
+        with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
+            for _ in range(steps):
+                if name == "ring_allreduce_r4_1m_f32":
+                    ccr.ccr_allreduce(ctx, bufs)
+                else:
+                    ccr.ccr_reduce_scatter(ctx, bufs)
+                    ccr.ccr_all_gather(ctx, bufs)
+            torch.cuda.synchronize()
+    elif name == "pp_sendrecv_4x2048x4096_bf16":
+        pw = workloads.PP_STAGING_BF16
+        mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
+               for _ in range(pw.microbatches)]
+        outs = [torch.empty_like(x) for x in mbs]
+        cfg = ccr.Config(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
+        with ccr.Context(0, cfg) as ctx:
+            for _ in range(steps):
+                ccr.ccr_sendrecv(ctx, mbs, outs)
+            torch.cuda.synchronize()
+    else:
+        m = workloads.MOE_DISPATCH_BF16
+        b = moe_buffers(ccr, m)
+        with ccr.Context(0) as ctx:
+            for _ in range(steps):
+                ccr.ccr_moe_dispatch(ctx, b["xs"], b["src_tok"], b["ecnt"], m.topk, b["send"],
+                                     b["recv"], b["exp"])
+                ccr.ccr_moe_combine(ctx, b["exp"], b["slot"], b["ecnt"], m.tokens, m.topk,
+                                    b["recv"], b["send"], b["out"])
+            torch.cuda.synchronize()
+    log(f"workload probe: {steps} calls of {name}")
+
+
 def workload_timings(ccr, workloads):
     """The other workloads, for context (each is also a full-size parity
     test): median time per call and the figures of merit of each."""
@@ -549,6 +591,8 @@ def main():
                     help="only the timed all-reduce steps and the per-launch pass (for profiler runs)")
     ap.add_argument("--moe-probe", action="store_true",
                     help="only run --steps fused MoE dispatch + combine calls (gather kernel profiles)")
+    ap.add_argument("--workload-probe", choices=PROBE_WORKLOADS, default=None,
+                    help="only run --steps calls of one of the other workloads (kernel-trace profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "
@@ -565,6 +609,9 @@ def main():
         return
     if args.moe_probe:
         moe_probe(ccr, workloads, max(1, args.steps))
+        return
+    if args.workload_probe:
+        workload_probe(ccr, workloads, args.workload_probe, max(1, args.steps))
         return
 
     w = workloads.DP_BUCKET_BF16
