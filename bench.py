@@ -191,6 +191,7 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             out["runs"].append({
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
                 "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
+                "dma_engines": (conf.get("dma_engines", 0) or "all") if conf["copy_mode"] == "sdma" else None,
                 "gemm_alone_ms": round(alone_i, 3),
                 "gemm_ms": round(gemm, 3), "slowdown_pct": round(100.0 * (gemm / alone_i - 1.0), 2),
                 "slowdown_pct_spread": [round(100.0 * (min(r[0] for r in b_runs) / alone_i - 1.0), 2),
@@ -657,6 +658,7 @@ def main():
     if not args.no_gemm:
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
         runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32, 16) for m in ("kernel", "sdma")]
+        runs += [dict(cfg, copy_mode="sdma", dma_engines=e) for e in (8, 4, 2)]
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
         gemm = overlap_runs(ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs,
                             (8192, 8192, 8192), 20, 6)
@@ -667,7 +669,8 @@ def main():
         outs = [torch.empty_like(x) for x in mbs]
         stg = dict(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
         pp = overlap_runs(ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
-                          [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma")],
+                          [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
+                           dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2)],
                           (4096, 4096, 16384), 20, 20)
         pp["workload"] = pw.name
         log("bench: compute units reached under each CU budget; host time per call")
@@ -737,7 +740,8 @@ def main():
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
         "gemm_slowdown_pct": None if gemm is None else {
-            r["copy_mode"]: r["slowdown_pct"] for r in gemm["runs"]
+            (r["copy_mode"] if r["dma_engines"] in (None, "all") else f"sdma_{r['dma_engines']}_engines"):
+            r["slowdown_pct"] for r in gemm["runs"]
             if r["cu_budget"] == 256 and r["dma_sync"] in (None, "host_func")},
         "gemm_slowdown": gemm,
         "pp_staging_gemm_slowdown": pp,

@@ -148,6 +148,8 @@ ccr_status_t check_config(const ccr_config_t* c) {
   if (c->dma_sync != CCR_DMA_SYNC_HOST_FUNC && c->dma_sync != CCR_DMA_SYNC_STREAM_FLAGS)
     return fail(CCR_ERR_INVALID_ARG, "dma_sync %d is not host_func (0) or stream_flags (1)",
                 c->dma_sync);
+  if (c->dma_engines < 0 || c->dma_engines > 16)
+    return fail(CCR_ERR_INVALID_ARG, "dma_engines %d outside [0, 16]", c->dma_engines);
   return CCR_OK;
 }
 
@@ -402,6 +404,12 @@ ccr_status_t ensure_dma(ccr_ctx* ctx) {
   return CCR_OK;
 }
 
+// Engines one call may use: the configured number, at most the usable ones.
+int dma_engine_limit(const ccr_ctx* ctx) {
+  const int n = ctx->dma->engine_count();
+  return ctx->cfg.dma_engines > 0 ? std::min(ctx->cfg.dma_engines, n) : n;
+}
+
 ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s) {
   std::string err;
   if (!ctx->dma->submit_copies(std::move(copies), s, (DmaSync)ctx->cfg.dma_sync, &err))
@@ -651,7 +659,7 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
     }
     if (which != kWhichRS && sdma) {
       CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
-      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, ctx->dma->engine_count(),
+      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, dma_engine_limit(ctx),
                                         fuse ? 1 : 0),
                          ag));
     } else if (which != kWhichRS) {
@@ -705,7 +713,7 @@ ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* re
   CCR_TRY(ensure_dma(ctx));
   int64_t total = 0;
   for (const Piece& x : p) total += x.nbytes;
-  const int E = ctx->dma->engine_count();
+  const int E = dma_engine_limit(ctx);
   const int64_t C = ctx->cfg.dma_chunk_bytes > 0 ? ctx->cfg.dma_chunk_bytes : auto_chunk(total, E);
   return dma_submit(ctx, flow_chunks(p, C, E), s);
 }
@@ -751,6 +759,7 @@ ccr_status_t ccr_config_default(ccr_config_t* cfg) {
   cfg->staging_slots = (int32_t)env_int("CCR_STAGING_SLOTS", cfg->staging_slots);
   cfg->dma_stripe = (int32_t)env_int("CCR_DMA_STRIPE", cfg->dma_stripe);
   cfg->dma_chunk_bytes = env_int("CCR_DMA_CHUNK", cfg->dma_chunk_bytes);
+  cfg->dma_engines = (int32_t)env_int("CCR_DMA_ENGINES", 0);
   return check_config(cfg);
 }
 
@@ -937,8 +946,8 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     plan.chunk = ctx->cfg.staging_chunk_bytes;
     plan.slots = ctx->cfg.staging_slots;
     plan.slot_mem = ctx->staging;
-    plan.stripe = ctx->cfg.dma_stripe > 0 ? ctx->cfg.dma_stripe
-                                          : std::max(1, ctx->dma->engine_count() / 2);
+    plan.engines = dma_engine_limit(ctx);
+    plan.stripe = ctx->cfg.dma_stripe > 0 ? ctx->cfg.dma_stripe : std::max(1, plan.engines / 2);
     std::string err;
     if (!ctx->dma->submit_staged(plan, caller, (DmaSync)ctx->cfg.dma_sync, &err))
       return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());

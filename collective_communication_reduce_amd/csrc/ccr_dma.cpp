@@ -191,9 +191,6 @@ bool DmaProxy::start(int device, std::string* err) {
     *err = "no usable SDMA engine for device-to-device copies";
     return false;
   }
-  if (const char* cap = getenv("CCR_DMA_ENGINES"); cap && atoi(cap) > 0 &&
-      (size_t)atoi(cap) < engines_.size())
-    engines_.resize((size_t)atoi(cap));
 
   if (hipHostMalloc(reinterpret_cast<void**>(&flags_), sizeof(uint32_t) * kFlagStride * 2 * kFlags,
                     hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
@@ -433,7 +430,7 @@ bool DmaProxy::advance(Job& j) {
   // Staged transfer: the per-slot state machine (idle -> filling ->
   // draining -> idle); chunk i always uses slot i mod slots.
   const StagedPlan& p = j.plan;
-  const int n_eng = (int)engines_.size();
+  const int n_eng = p.engines > 0 ? std::min(p.engines, (int)engines_.size()) : (int)engines_.size();
   const int stripe = std::max(1, std::min(p.stripe, n_eng));
   const int drain_base = n_eng >= 2 * stripe ? n_eng / 2 : 0;
   auto all_done = [](const std::vector<hsa_signal_t>& v) {

@@ -67,6 +67,7 @@ struct StagedPlan {
   int slots = 0;
   char* slot_mem = nullptr;
   int stripe = 1;
+  int engines = 0;  // engines the job may use (the first of the proxy's list); 0 = all
 };
 
 // One slot transition of a staged job: state 0 idle, 1 filling, 2 draining.

@@ -111,6 +111,11 @@ typedef struct {
     int64_t dma_chunk_bytes;     /* SDMA: all-to-all flows are cut into chunks of at
                                     most this size (multiple of 16); 0 = automatic  */
     int32_t dma_sync;            /* ccr_dma_sync_t                                  */
+    int32_t dma_engines;         /* SDMA: engines one call may use, 1..16 (the first
+                                    of the usable ones); 0 = all.  Fewer engines
+                                    move the copies at a lower rate: longer
+                                    collectives, less traffic beside concurrent
+                                    compute at any moment                          */
 } ccr_config_t;
 
 typedef struct ccr_ctx *ccr_ctx_t;
@@ -120,7 +125,7 @@ typedef struct ccr_ctx *ccr_ctx_t;
  * chunking), then apply the environment overrides CCR_COPY_MODE
  * (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES, CCR_OVERLAP, CCR_STAGING_CHUNK,
  * CCR_STAGING_SLOTS, CCR_BF16_ACC (per_hop|fp32_partials), CCR_DMA_STRIPE,
- * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags).  HOCCL §4 switches backends by an environment variable;
+ * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags), CCR_DMA_ENGINES.  HOCCL §4 switches backends by an environment variable;
  * this mirrors that. */
 ccr_status_t ccr_config_default(ccr_config_t *cfg);
 

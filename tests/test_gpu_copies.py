@@ -54,7 +54,7 @@ def test_sendrecv_full_pp_activations(ccr_mod, mode):
             np.testing.assert_array_equal(to_host(a), x)
 
 
-@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+@pytest.mark.parametrize("mode", ["kernel", "sdma", "sdma-3-engines"])
 @pytest.mark.parametrize("R,row_bytes", [(1, 16), (2, 48), (3, 4096), (8, 256), (20, 32)])
 def test_alltoall_bytes(ccr_mod, mode, R, row_bytes):
     import torch
@@ -65,7 +65,9 @@ def test_alltoall_bytes(ccr_mod, mode, R, row_bytes):
     sends = [rng.integers(0, 256, int(counts[r].sum()) * row_bytes, dtype=np.uint8) for r in range(R)]
     ref = oracle.alltoall(sends, counts, row_bytes)
     say(f"alltoall {mode} R={R} row_bytes={row_bytes}")
-    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode)) as c:
+    cfg = ccr_mod.Config(copy_mode="sdma", dma_engines=3) if mode == "sdma-3-engines" else \
+        ccr_mod.Config(copy_mode=mode)
+    with ccr_mod.Context(0, cfg) as c:
         s = [raw_to_dev(x) if x.size else torch.zeros(16, dtype=torch.uint8, device="cuda") for x in sends]
         r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
         ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
@@ -114,18 +116,22 @@ def test_dma_engines_available(ccr_mod):
 
 
 @pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
-@pytest.mark.parametrize("m,nbytes,chunk,slots,stripe", [(4, 1 << 20, 1 << 18, 2, 0), (3, 100000 // 16 * 16, 16384, 3, 2),
-                                                         (1, 4096, 4096, 1, 1)])
-def test_sdma_staged_slot_state_machine(ccr_mod, m, nbytes, chunk, slots, stripe, sync):
+@pytest.mark.parametrize("m,nbytes,chunk,slots,stripe,engines",
+                         [(4, 1 << 20, 1 << 18, 2, 0, 0), (3, 100000 // 16 * 16, 16384, 3, 2, 0),
+                          (1, 4096, 4096, 1, 1, 0), (4, 1 << 20, 1 << 18, 2, 0, 2),
+                          (2, 1 << 20, 1 << 17, 3, 3, 1)])
+def test_sdma_staged_slot_state_machine(ccr_mod, m, nbytes, chunk, slots, stripe, engines, sync):
     """The proxy's staging slots follow idle -> filling -> draining -> idle,
     chunk i uses slot i mod slots, chunks fill in order, every chunk once,
     and the bytes arrive intact."""
     import torch
     rng = np.random.default_rng(nbytes)
     srcs = [rng.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(m)]
-    say(f"sdma staged m={m} nbytes={nbytes} chunk={chunk} slots={slots} stripe={stripe} sync={sync}")
+    say(f"sdma staged m={m} nbytes={nbytes} chunk={chunk} slots={slots} stripe={stripe} "
+        f"engines={engines} sync={sync}")
     with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma", staging_chunk_bytes=chunk,
-                                           staging_slots=slots, dma_stripe=stripe, dma_sync=sync)) as c:
+                                           staging_slots=slots, dma_stripe=stripe, dma_sync=sync,
+                                           dma_engines=engines)) as c:
         s = [raw_to_dev(x) for x in srcs]
         r = [torch.zeros_like(x) for x in s]
         ccr_mod.ccr_sendrecv(c, s, r)
@@ -223,7 +229,9 @@ def test_alltoall_max_ranks_and_empty(ccr_mod, mode):
     sends = [rng.integers(0, 256, int(counts[r].sum()) * row_bytes, dtype=np.uint8) for r in range(R)]
     ref = oracle.alltoall(sends, counts, row_bytes)
     say(f"alltoall R=64 {mode}")
-    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode)) as c:
+    cfg = ccr_mod.Config(copy_mode="sdma", dma_engines=3) if mode == "sdma-3-engines" else \
+        ccr_mod.Config(copy_mode=mode)
+    with ccr_mod.Context(0, cfg) as c:
         s = [raw_to_dev(x) if x.size else torch.zeros(16, dtype=torch.uint8, device="cuda") for x in sends]
         r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
         ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)

@@ -89,7 +89,8 @@ def test_bf16_fp32_partials_bitwise(ccr_mod, ctx, R, n, S, mode):
 MODES = [dict(overlap=True, slices=4), dict(copy_mode="sdma", slices=2),
          dict(copy_mode="sdma", overlap=True, slices=3), dict(cu_budget=64, slices=2),
          dict(cu_budget=16, overlap=True, slices=2, copy_mode="sdma"),
-         dict(copy_mode="sdma", slices=2, dma_sync="stream_flags")]
+         dict(copy_mode="sdma", slices=2, dma_sync="stream_flags"),
+         dict(copy_mode="sdma", slices=3, dma_engines=1), dict(copy_mode="sdma", dma_engines=4)]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=lambda m: "-".join(f"{k}={v}" for k, v in m.items()))
