@@ -97,6 +97,9 @@ def _new_own_queue_stream():
     return torch.cuda.ExternalStream(s.value)
 
 
+PAIRS = 9  # interleaved GEMM-alone / loaded window pairs per overlap configuration
+
+
 def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
     """Fixed-work overlap protocol.  G back-to-back GEMMs on stream g, alone
     and then with n_coll calls of `collective(ctx, stream)` issued on
@@ -178,15 +181,15 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             collective(ctx, c)  # first use starts the SDMA proxy
             torch.cuda.synchronize()
             t1 = time_steps(lambda: collective(ctx, c), 3)
-            # A/B interleaved: GEMM alone, then with the collectives, five times;
+            # A/B interleaved: GEMM alone, then with the collectives, nine times;
             # each run is compared with its own alone windows, so slow drift of
             # the GEMM's own time (clocks, temperature) does not count as slowdown
             a_ms, b_runs = [], []
-            for _ in range(5):
+            for _ in range(PAIRS):
                 a_ms.append(window()[0])
                 b_runs.append(window(ctx))
-            alone_i = sorted(a_ms)[2]
-            gemm, coll, span = sorted(b_runs)[2]
+            alone_i = sorted(a_ms)[PAIRS // 2]
+            gemm, coll, span = sorted(b_runs)[PAIRS // 2]
             i_coll = contention(ctx)
             out["runs"].append({
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
