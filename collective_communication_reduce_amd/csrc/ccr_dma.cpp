@@ -498,6 +498,7 @@ bool DmaProxy::advance(Job& j) {
 }
 
 void DmaProxy::loop() {
+  int idle = 0;  // polls in a row without progress
   for (;;) {
     {
       std::unique_lock<std::mutex> lk(mu_);
@@ -576,7 +577,11 @@ void DmaProxy::loop() {
       }
       ++it;
     }
-    if (!progress) _mm_pause();
+    // Spin while copies are short; on a long one, give the core away between
+    // polls (after ~4096 idle polls) so the proxy does not hold a CPU busy.
+    if (progress) idle = 0;
+    else if (++idle < 4096) _mm_pause();
+    else std::this_thread::yield();
   }
 }
 

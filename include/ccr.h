@@ -41,6 +41,13 @@
  *     them may run at the same time and race on that scratch; keep them on
  *     one stream or order the streams with events.  Every other call keeps
  *     no device state between launches.
+ *   - That scratch grows on demand: the first call that needs more than the
+ *     context holds allocates it, and when it replaces a smaller buffer it
+ *     synchronises the device first (work still in flight may use the old
+ *     one).  The fused MoE calls cycle through 4 segment-table slots and
+ *     block the host until the call that last used their slot has finished.
+ *     Warm a context up with its largest call before timing or capturing
+ *     work around it.
  */
 #ifndef CCR_H
 #define CCR_H
