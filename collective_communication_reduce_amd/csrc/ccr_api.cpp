@@ -206,6 +206,17 @@ ccr_status_t order_after(ccr_ctx* ctx, size_t ev_index, hipStream_t from, hipStr
   return CCR_OK;
 }
 
+// A call whose work depends on context scratch that may be reallocated, on
+// host memory copied at launch time, or on the DMA proxy (a job runs once)
+// cannot be replayed from a graph: refuse it while `s` is being captured.
+ccr_status_t refuse_capture(hipStream_t s, const char* what) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(s, &st));
+  if (st != hipStreamCaptureStatusNone)
+    return fail(CCR_ERR_UNSUPPORTED, "%s cannot be captured into a graph", what);
+  return CCR_OK;
+}
+
 ccr_status_t check_ctx(ccr_ctx* ctx) {
   if (!ctx) return fail(CCR_ERR_INVALID_ARG, "ctx is NULL");
   HIP_TRY(hipSetDevice(ctx->device));
@@ -576,7 +587,6 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   const bool partials = dtype == CCR_BF16 && which != kWhichAG && R > 2 &&
                         ctx->cfg.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS;
   const int64_t Lc = align_up(ceil_div(count, R), V);
-  if (partials) CCR_TRY(ensure_partials(ctx, 2 * (int64_t)R * Lc * 4));
   // Reduce-scatter runs on the CU-masked stream when a budget is set, else
   // directly on the caller's stream.  All-gather follows it on the same
   // stream, or, with several slices, on the second side stream when overlap
@@ -584,6 +594,9 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   // with several slices its handshake sits on the second side stream, so
   // the reduce-scatter of the next slice keeps going while the engines copy.
   const bool sdma = ctx->cfg.copy_mode == CCR_COPY_SDMA && which != kWhichRS;
+  if (sdma) CCR_TRY(refuse_capture(caller, "a ring collective with SDMA copies"));
+  if (partials) CCR_TRY(refuse_capture(caller, "a bf16 ring collective with fp32 partials"));
+  if (partials) CCR_TRY(ensure_partials(ctx, 2 * (int64_t)R * Lc * 4));
   if (sdma) CCR_TRY(ensure_dma(ctx));
   // Slices exist so that one slice's all-gather can run while the next
   // slice's reduce-scatter does.  When nothing runs beside them (a single
@@ -931,8 +944,9 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     ranges.push_back(Range{b, b + (uintptr_t)nbytes, 2 * m + 1});
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
-  CCR_TRY(ensure_staging(ctx));
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  CCR_TRY(refuse_capture(caller, "ccr_sendrecv (context staging slots)"));
+  CCR_TRY(ensure_staging(ctx));
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
     // One DMA job: the proxy runs the slot state machine itself, each fill
     // and drain striped over several engines.
@@ -1018,6 +1032,8 @@ ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* r
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
+    CCR_TRY(refuse_capture(caller, "ccr_alltoall with SDMA copies"));
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
   CCR_TRY(run_alltoall(ctx, send, recv, R, counts, row_bytes, s));
@@ -1068,6 +1084,7 @@ ccr_status_t ccr_moe_plan(ccr_ctx_t ctx, const int32_t* topk, int64_t T, int E, 
       R > kMaxRanks || E % R != 0)
     return fail(CCR_ERR_INVALID_ARG, "need 0 <= T, 1 <= K <= min(E, 16), E <= 1024, R | E");
   if (!h_ecnt) return fail(CCR_ERR_INVALID_ARG, "h_ecnt is NULL");
+  CCR_TRY(refuse_capture(static_cast<hipStream_t>(stream), "ccr_moe_plan (blocking)"));
   if (T > 0) {
     CCR_TRY(check_dev_ptr(ctx, topk, T * K * 4, "topk", 0));
     CCR_TRY(check_dev_ptr(ctx, src_tok, T * K * 4, "src_tok", 0));
@@ -1222,6 +1239,8 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
   add_bufs(&bufs, exp, R, rb.data(), true, true, "exp");
   CCR_TRY(check_writes_disjoint(bufs));
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
+    CCR_TRY(refuse_capture(caller, "ccr_moe_dispatch with SDMA copies"));
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
   // pack: send[r] row j = x[r] row src_tok[r][j]
@@ -1262,6 +1281,8 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   add_bufs(&bufs, out, R, &sb, false, true, "out");
   CCR_TRY(check_writes_disjoint(bufs));
   hipStream_t caller = static_cast<hipStream_t>(stream);
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
+    CCR_TRY(refuse_capture(caller, "ccr_moe_combine with SDMA copies"));
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
   // inverse unpack: expert-major rows back to source-segment order
@@ -1336,6 +1357,7 @@ ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int6
         row += h_ecnt[(size_t)r * E + e];
       }
   }
+  CCR_TRY(refuse_capture(caller, "a fused MoE call (segment table copied from host memory)"));
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
   ccr_ctx::TableSlot* slot = nullptr;

@@ -48,6 +48,16 @@
  *     block the host until the call that last used their slot has finished.
  *     Warm a context up with its largest call before timing or capturing
  *     work around it.
+ *   - HIP graphs: a call made of kernel launches only can be captured on a
+ *     capturing stream and replayed (the ring collectives with kernel copies
+ *     and per-hop bf16, with or without CU budget, slices or overlap;
+ *     ccr_alltoall, ccr_moe_dispatch and ccr_moe_combine with kernel copies;
+ *     ccr_permute_rows; ccr_moe_topk).  A replay reuses the device pointers
+ *     given at capture time.  Calls that would depend on context scratch
+ *     that may be reallocated, on host memory copied at launch, or on the
+ *     DMA proxy (SDMA copies, fp32 partials, ccr_sendrecv, ccr_moe_plan,
+ *     the fused MoE calls) return CCR_ERR_UNSUPPORTED while `stream` is
+ *     capturing, and enqueue nothing.
  */
 #ifndef CCR_H
 #define CCR_H

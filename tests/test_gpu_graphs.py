@@ -1,0 +1,147 @@
+"""HIP graph capture of the collectives.  Calls made of kernel launches only
+(the ring with kernel copies and per-hop bf16, with or without side
+streams; the kernel-copy all-to-all; row permutes; top-K) are captured and
+replayed several times, with eager work and synchronisations between the
+replays, every replay checked bit for bit against the oracle.  Calls that
+depend on context scratch that may be reallocated, on host memory copied at
+launch, or on the DMA proxy are refused while the stream is capturing."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import raw_to_dev, say, to_dev, to_host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ccr_mod():
+    torch_cuda()
+    import collective_communication_reduce_amd as ccr
+    return ccr
+
+
+def _replays(torch, g, reset, check, other):
+    for rep in range(4):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(rep)
+        other()  # eager work of the program between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", [dict(), dict(slices=2), dict(cu_budget=64, overlap=True, slices=2)],
+                         ids=["default", "slices2", "budget-overlap"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_captured_allreduce_replays(ccr_mod, mode, dt):
+    import torch
+    R, n = 4, 3 * 65536 + 5
+    xs = workloads.random_buffers(R, n, dt, seed=77, dist="normal", scale=1e-2)
+    expect = oracle.ring_allreduce(xs, S=1)
+    say(f"graph allreduce {dt} mode={mode}")
+    with ccr_mod.Context(0, ccr_mod.Config(**mode)) as c:
+        src = [to_dev(x) for x in xs]
+        bufs = [t.clone() for t in src]
+        scratch = [t.clone() for t in src]
+        ccr_mod.ccr_allreduce(c, bufs)  # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=s):
+            ccr_mod.ccr_allreduce(c, bufs)
+
+        def reset():
+            for b, t in zip(bufs, src):
+                b.copy_(t)
+
+        def check(rep):
+            for q in range(R):
+                assert to_host(bufs[q]).tobytes() == expect[q].tobytes(), f"replay {rep} rank {q}"
+
+        def other():
+            for b, t in zip(scratch, src):
+                b.copy_(t)
+            ccr_mod.ccr_allreduce(c, scratch)
+
+        _replays(torch, g, reset, check, other)
+        for q in range(R):  # the eager calls between replays were right too
+            assert to_host(scratch[q]).tobytes() == expect[q].tobytes()
+
+
+def test_captured_alltoall_permute_topk_replays(ccr_mod):
+    import torch
+    R, row = 4, 48
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 9, (R, R))
+    sends = [rng.integers(0, 256, int(counts[r].sum()) * row, dtype=np.uint8) for r in range(R)]
+    ref = oracle.alltoall(sends, counts, row)
+    T, E, K = 64, 16, 3
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ref_topk = oracle.moe_topk(logits, K)
+    nsrc, nrows = 50, 70
+    src_rows = rng.integers(0, 256, (nsrc, 32), dtype=np.uint8)
+    idx = rng.integers(0, nsrc, nrows).astype(np.int32)
+    say("graph alltoall / permute / topk")
+    with ccr_mod.Context(0) as c:
+        s_d = [raw_to_dev(x) for x in sends]
+        r_d = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
+        d_logits = to_dev(logits)
+        d_topk = torch.zeros(T, K, dtype=torch.int32, device="cuda")
+        d_src = torch.from_numpy(src_rows).cuda()
+        d_idx = torch.from_numpy(idx).cuda()
+        d_dst = torch.zeros(nrows, 32, dtype=torch.uint8, device="cuda")
+        calls = lambda: (ccr_mod.ccr_alltoall(c, s_d, r_d, counts, row),  # noqa: E731
+                         ccr_mod.ccr_moe_topk(c, d_logits, d_topk),
+                         ccr_mod.ccr_permute_rows(c, d_dst, d_src, d_idx))
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            calls()
+
+        def reset():
+            for t in r_d:
+                t.zero_()
+            d_topk.zero_()
+            d_dst.zero_()
+
+        def check(rep):
+            for a, b in zip(r_d, ref):
+                assert to_host(a)[:b.size].tobytes() == b.tobytes(), f"replay {rep}"
+            np.testing.assert_array_equal(to_host(d_topk), ref_topk)
+            np.testing.assert_array_equal(to_host(d_dst), src_rows[idx])
+
+        _replays(torch, g, reset, check, calls)
+
+
+def test_calls_that_cannot_replay_are_refused(ccr_mod):
+    import torch
+    R, n = 4, 4096
+    xs = workloads.random_buffers(R, n, "bf16", seed=3, dist="normal", scale=1e-2)
+    cases = [("sdma all-reduce", dict(copy_mode="sdma"),
+              lambda c, b, m: ccr_mod.ccr_allreduce(c, b)),
+             ("fp32-partials all-reduce", dict(bf16_acc="fp32_partials"),
+              lambda c, b, m: ccr_mod.ccr_allreduce(c, b)),
+             ("staged send/recv", dict(),
+              lambda c, b, m: ccr_mod.ccr_sendrecv(c, b[:2], b[2:])),
+             ("sdma all-to-all", dict(copy_mode="sdma"),
+              lambda c, b, m: ccr_mod.ccr_alltoall(c, m[0], m[1], np.ones((R, R), np.int64), 16))]
+    for name, cfg, call in cases:
+        say(f"graph refusal: {name}")
+        with ccr_mod.Context(0, ccr_mod.Config(**cfg)) as c:
+            bufs = [to_dev(x) for x in xs]
+            a2a = ([torch.zeros(R * 16, dtype=torch.uint8, device="cuda") for _ in range(R)],
+                   [torch.zeros(R * 16, dtype=torch.uint8, device="cuda") for _ in range(R)])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                with pytest.raises(ccr_mod.CcrError) as e:
+                    call(c, bufs, a2a)
+                bufs[0].add_(0)  # keep the captured graph non-empty
+            assert e.value.status == ccr_mod.CCR_ERR_UNSUPPORTED, name
+            assert "graph" in ccr_mod.ccr_last_error()
+            call(c, bufs, a2a)  # the same call still runs eagerly
+            torch.cuda.synchronize()
