@@ -1,6 +1,7 @@
 """HIP graph capture of the collectives.  Calls made of kernel launches only
 (the ring with kernel copies and per-hop bf16, with or without side
-streams; the kernel-copy all-to-all; row permutes; top-K) are captured and
+streams; the kernel-copy all-to-all; the three-stage MoE dispatch and
+combine; row permutes; top-K) are captured and
 replayed several times, with eager work and synchronisations between the
 replays, every replay checked bit for bit against the oracle.  Calls that
 depend on context scratch that may be reallocated, on host memory copied at
@@ -145,3 +146,50 @@ def test_calls_that_cannot_replay_are_refused(ccr_mod):
             assert "graph" in ccr_mod.ccr_last_error()
             call(c, bufs, a2a)  # the same call still runs eagerly
             torch.cuda.synchronize()
+
+
+def test_captured_three_stage_moe_replays(ccr_mod):
+    """Pack, exchange and unpack (kernel copies) and the combine, captured
+    once from a plan made eagerly, replayed against the oracle."""
+    import torch
+    R, T, E, K, H = 4, 96, 16, 2, 64
+    w = workloads.MOE_DISPATCH_BF16
+    xs, logits = workloads.moe_inputs(w, tokens=T, R=R)
+    xs = [x[:, :H].copy() for x in xs]
+    logits = [l[:, :E].copy() for l in logits]
+    ref = oracle.moe_dispatch(xs, [oracle.moe_topk(l, K) for l in logits], E)
+    rows = [int(ref["counts"][:, d].sum()) for d in range(R)]
+    say("graph three-stage moe")
+    with ccr_mod.Context(0) as c:
+        d_x = [to_dev(x) for x in xs]
+        topk = [torch.zeros(T, K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        src_tok = [torch.zeros(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        slot = [torch.zeros(T * K, dtype=torch.int32, device="cuda") for _ in range(R)]
+        ecnt = []
+        for r in range(R):
+            ccr_mod.ccr_moe_topk(c, to_dev(logits[r]), topk[r])
+            ecnt.append(ccr_mod.ccr_moe_plan(c, topk[r], E, R, src_tok[r], slot[r]))
+        ecnt = np.stack(ecnt)
+        send = [torch.zeros(T * K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        recv = [torch.zeros(max(1, n), H, dtype=torch.bfloat16, device="cuda") for n in rows]
+        exp = [torch.zeros(max(1, n), H, dtype=torch.bfloat16, device="cuda") for n in rows]
+        out = [torch.zeros(T, K, H, dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        calls = lambda: (ccr_mod.ccr_moe_dispatch(c, d_x, src_tok, ecnt, K, send, recv, exp),  # noqa: E731
+                         ccr_mod.ccr_moe_combine(c, exp, slot, ecnt, T, K, recv, send, out))
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            calls()
+
+        def reset():
+            for t in send + recv + exp + out:
+                t.zero_()
+
+        def check(rep):
+            for d in range(R):
+                np.testing.assert_array_equal(to_host(exp[d])[:rows[d]], ref["exp"][d])
+            for r in range(R):
+                np.testing.assert_array_equal(to_host(out[r]), np.repeat(xs[r][:, None, :], K, axis=1))
+
+        _replays(torch, g, reset, check, calls)
