@@ -40,7 +40,7 @@ class ccr_config_t(ctypes.Structure):
                 ("staging_chunk_bytes", ctypes.c_int64), ("staging_slots", ctypes.c_int32),
                 ("bf16_acc", ctypes.c_int32), ("dma_stripe", ctypes.c_int32),
                 ("dma_chunk_bytes", ctypes.c_int64), ("dma_sync", ctypes.c_int32),
-                ("dma_engines", ctypes.c_int32)]
+                ("dma_engines", ctypes.c_int32), ("graph_cache", ctypes.c_int32)]
 
 
 class ccr_ring_op_t(ctypes.Structure):
@@ -154,6 +154,7 @@ class Config:
     dma_chunk_bytes: int = 0         # SDMA all-to-all chunk; 0 = automatic
     dma_sync: str = "host_func"      # "host_func" | "stream_flags"
     dma_engines: int = 0             # SDMA engines one call may use; 0 = all
+    graph_cache: bool = True         # replay small kernel-only ring calls from captured graphs
 
     def to_c(self) -> ccr_config_t:
         return ccr_config_t(CCR_COPY_SDMA if self.copy_mode == "sdma" else CCR_COPY_KERNEL,
@@ -161,7 +162,8 @@ class Config:
                             self.staging_chunk_bytes, self.staging_slots,
                             CCR_BF16_ACC_FP32_PARTIALS if self.bf16_acc == "fp32_partials"
                             else CCR_BF16_ACC_PER_HOP, self.dma_stripe, self.dma_chunk_bytes,
-                            1 if self.dma_sync == "stream_flags" else 0, self.dma_engines)
+                            1 if self.dma_sync == "stream_flags" else 0, self.dma_engines,
+                            int(self.graph_cache))
 
     @staticmethod
     def from_c(c: ccr_config_t) -> "Config":
@@ -169,7 +171,8 @@ class Config:
                       c.slices, bool(c.overlap), c.staging_chunk_bytes, c.staging_slots,
                       "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop",
                       c.dma_stripe, c.dma_chunk_bytes,
-                      "stream_flags" if c.dma_sync == 1 else "host_func", c.dma_engines)
+                      "stream_flags" if c.dma_sync == 1 else "host_func", c.dma_engines,
+                      bool(c.graph_cache))
 
 
 def ccr_config_default() -> Config:

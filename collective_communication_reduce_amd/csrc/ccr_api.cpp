@@ -110,6 +110,19 @@ struct ccr_ctx {
   static constexpr int kTableSlots = 4;
   TableSlot tables[kTableSlots];
   int next_table = 0;
+  // Small ring calls made of kernel launches only are captured once into a
+  // graph and replayed (run_ring): one host call instead of 2(R-1) launches.
+  struct RingGraph {
+    std::vector<void*> bufs;
+    int64_t count = 0;
+    int dtype = 0, which = 0;
+    int uses = 0;                   // calls seen with this key
+    uint64_t last = 0;              // tick of the last use (least recently used is replaced)
+    hipGraphExec_t exec = nullptr;
+  };
+  static constexpr size_t kMaxRingGraphs = 32;
+  std::vector<RingGraph> graphs;
+  uint64_t graph_tick = 0;
   // per-launch timing (ccr_profile_enable): event pairs and payload bytes
   bool prof_on = false;
   struct Timed {
@@ -150,6 +163,8 @@ ccr_status_t check_config(const ccr_config_t* c) {
                 c->dma_sync);
   if (c->dma_engines < 0 || c->dma_engines > 16)
     return fail(CCR_ERR_INVALID_ARG, "dma_engines %d outside [0, 16]", c->dma_engines);
+  if (c->graph_cache != 0 && c->graph_cache != 1)
+    return fail(CCR_ERR_INVALID_ARG, "graph_cache %d is not 0 or 1", c->graph_cache);
   return CCR_OK;
 }
 
@@ -553,6 +568,108 @@ std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, i
   return out;
 }
 
+ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
+                          int which, hipStream_t caller);
+
+// Replaying a captured graph pays up to this size per rank (8 bf16 ranks,
+// one call at a time: 48 instead of 78 us at 2 MiB, 48 instead of 65 us at
+// 4 MiB); from 8 MiB on, back-to-back replays run slower than eager launches.
+constexpr int64_t kGraphMaxRankBytes = int64_t(4) << 20;
+
+// A ring call is replayed from a graph when it is small, made of kernel
+// launches on the caller's stream only (kernel copies, no CU budget, no
+// overlap, no fp32 partials), not profiled, and not itself being captured.
+bool ring_graph_eligible(ccr_ctx* ctx, int64_t rank_bytes, int dtype, int which,
+                         hipStream_t caller) {
+  const ccr_config_t& c = ctx->cfg;
+  if (!c.graph_cache || ctx->prof_on || ctx->masked || c.overlap || rank_bytes > kGraphMaxRankBytes)
+    return false;
+  if (c.copy_mode == CCR_COPY_SDMA && which != kWhichRS) return false;
+  if (dtype == CCR_BF16 && which != kWhichAG && c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS) return false;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return st == hipStreamCaptureStatusNone;
+}
+
+// A graph is destroyed only after the device has drained: its last replay
+// may still be running on any caller stream (an event recorded after every
+// replay would cost each replay a gap on the GPU).  Replacing an entry of a
+// full cache therefore synchronises the device once.
+void drop_graph(ccr_ctx::RingGraph* g) {
+  if (g->exec) {
+    (void)hipDeviceSynchronize();
+    (void)hipGraphExecDestroy(g->exec);
+  }
+  g->exec = nullptr;
+}
+
+void flush_graphs(ccr_ctx* ctx) {
+  bool any = false;
+  for (auto& g : ctx->graphs) any |= g.exec != nullptr;
+  if (any) (void)hipDeviceSynchronize();
+  for (auto& g : ctx->graphs)
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  ctx->graphs.clear();
+}
+
+// The first call with a given (buffers, count, dtype, operation) runs
+// eagerly; the second is captured on the context's own stream (the legacy
+// default stream cannot be captured) and every call from then on replays
+// the graph on the caller's stream.  Kernel arguments are captured by value,
+// so a replay repeats exactly the launches of an eager call.
+ccr_status_t run_ring_graph(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
+                            int which, hipStream_t caller, bool* launched) {
+  ccr_ctx::RingGraph* g = nullptr;
+  for (auto& e : ctx->graphs)
+    if (e.count == count && e.dtype == dtype && e.which == which && (int)e.bufs.size() == R &&
+        std::equal(e.bufs.begin(), e.bufs.end(), bufs)) {
+      g = &e;
+      break;
+    }
+  if (!g) {
+    if (ctx->graphs.size() < ccr_ctx::kMaxRingGraphs) {
+      ctx->graphs.emplace_back();
+      g = &ctx->graphs.back();
+    } else {
+      g = &*std::min_element(ctx->graphs.begin(), ctx->graphs.end(),
+                             [](const ccr_ctx::RingGraph& a, const ccr_ctx::RingGraph& b) {
+                               return a.last < b.last;
+                             });
+      drop_graph(g);
+      *g = ccr_ctx::RingGraph();
+    }
+    g->bufs.assign(bufs, bufs + R);
+    g->count = count;
+    g->dtype = dtype;
+    g->which = which;
+  }
+  g->last = ++ctx->graph_tick;
+  if (!g->exec && ++g->uses >= 2) {
+    hipStream_t cs = ctx->s_a;
+    HIP_TRY(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    const ccr_status_t st = enqueue_ring(ctx, bufs, R, count, dtype, which, cs);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(cs, &graph);
+    if (st != CCR_OK || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st != CCR_OK ? st : hip_fail(e, "hipStreamEndCapture");
+    }
+    const hipError_t ei = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) {
+      g->exec = nullptr;
+      return hip_fail(ei, "hipGraphInstantiate");
+    }
+  }
+  if (!g->exec) return CCR_OK;  // first sight: the caller launches eagerly
+  HIP_TRY(hipGraphLaunch(g->exec, caller));
+  *launched = true;
+  return CCR_OK;
+}
+
 ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
                       int which, hipStream_t caller) {
   CCR_TRY(check_ctx(ctx));
@@ -570,7 +687,19 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   }
   CCR_TRY(check_disjoint(ranges, "bufs"));
   if (R == 1) return CCR_OK;
+  if (ring_graph_eligible(ctx, count * esize, dtype, which, caller)) {
+    bool launched = false;
+    CCR_TRY(run_ring_graph(ctx, bufs, R, count, dtype, which, caller, &launched));
+    if (launched) return CCR_OK;
+  }
+  return enqueue_ring(ctx, bufs, R, count, dtype, which, caller);
+}
 
+// The launches of a validated ring call, on `caller` (and the context's side
+// streams, SDMA engines or scratch as the configuration asks).
+ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
+                          int which, hipStream_t caller) {
+  const int esize = dtype_size(dtype);
   const int V = 16 / esize;
   const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
   const HopKind reduce_fwd = dtype == CCR_F32 ? HopKind::kReduceFwdF32 : HopKind::kReduceFwdBf16;
@@ -773,6 +902,7 @@ ccr_status_t ccr_config_default(ccr_config_t* cfg) {
   cfg->dma_stripe = (int32_t)env_int("CCR_DMA_STRIPE", cfg->dma_stripe);
   cfg->dma_chunk_bytes = env_int("CCR_DMA_CHUNK", cfg->dma_chunk_bytes);
   cfg->dma_engines = (int32_t)env_int("CCR_DMA_ENGINES", 0);
+  cfg->graph_cache = (int32_t)env_int("CCR_GRAPH_CACHE", 1);
   return check_config(cfg);
 }
 
@@ -811,6 +941,7 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   if (!ctx) return CCR_OK;
   (void)hipSetDevice(ctx->device);
   ctx->dma.reset();  // drains outstanding DMA operations, stops the proxy
+  flush_graphs(ctx);
   ccr_status_t st = destroy_streams(ctx);
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   for (auto& t : ctx->timed) {
@@ -839,6 +970,7 @@ ccr_status_t ccr_ctx_set_config(ccr_ctx_t ctx, const ccr_config_t* cfg) {
   const bool restream = cfg->cu_budget != ctx->cfg.cu_budget;
   HIP_TRY(hipStreamSynchronize(ctx->s_a));
   HIP_TRY(hipStreamSynchronize(ctx->s_b));
+  flush_graphs(ctx);
   ctx->cfg = *cfg;
   if (restream) CCR_TRY(make_streams(ctx));
   return CCR_OK;

@@ -133,6 +133,18 @@ typedef struct {
                                     move the copies at a lower rate: longer
                                     collectives, less traffic beside concurrent
                                     compute at any moment                          */
+    int32_t graph_cache;         /* 1 (default): a ring collective of at most 4 MiB
+                                    per rank made of kernel launches only (kernel
+                                    copies, no CU budget, no overlap, no fp32
+                                    partials) is captured into a HIP graph on its
+                                    second call with the same buffers, count,
+                                    dtype and operation, and replayed from then
+                                    on (one host call instead of 2(R-1)
+                                    launches); 0: always launch eagerly.  The
+                                    context keeps up to 32 graphs; replacing one
+                                    of a full cache, ccr_ctx_set_config and
+                                    ccr_ctx_destroy synchronise the device before
+                                    destroying graphs                               */
 } ccr_config_t;
 
 typedef struct ccr_ctx *ccr_ctx_t;
@@ -142,7 +154,8 @@ typedef struct ccr_ctx *ccr_ctx_t;
  * chunking), then apply the environment overrides CCR_COPY_MODE
  * (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES, CCR_OVERLAP, CCR_STAGING_CHUNK,
  * CCR_STAGING_SLOTS, CCR_BF16_ACC (per_hop|fp32_partials), CCR_DMA_STRIPE,
- * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags), CCR_DMA_ENGINES.  HOCCL §4 switches backends by an environment variable;
+ * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags), CCR_DMA_ENGINES,
+ * CCR_GRAPH_CACHE (0|1).  HOCCL §4 switches backends by an environment variable;
  * this mirrors that. */
 ccr_status_t ccr_config_default(ccr_config_t *cfg);
 

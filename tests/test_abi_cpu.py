@@ -34,10 +34,10 @@ def test_library_exports_every_declared_symbol():
 def test_config_defaults_and_environment(monkeypatch):
     for k in ("CCR_COPY_MODE", "CCR_CU_BUDGET", "CCR_SLICES", "CCR_OVERLAP",
               "CCR_STAGING_CHUNK", "CCR_STAGING_SLOTS", "CCR_BF16_ACC", "CCR_DMA_STRIPE",
-              "CCR_DMA_CHUNK", "CCR_DMA_SYNC", "CCR_DMA_ENGINES"):
+              "CCR_DMA_CHUNK", "CCR_DMA_SYNC", "CCR_DMA_ENGINES", "CCR_GRAPH_CACHE"):
         monkeypatch.delenv(k, raising=False)
     c = ccr.ccr_config_default()
-    assert c == ccr.Config("kernel", 0, 1, False, 4 << 20, 2, "per_hop", 0, 0, "host_func")
+    assert c == ccr.Config("kernel", 0, 1, False, 4 << 20, 2, "per_hop", 0, 0, "host_func", 0, True)
     monkeypatch.setenv("CCR_COPY_MODE", "sdma")
     monkeypatch.setenv("CCR_CU_BUDGET", "32")
     monkeypatch.setenv("CCR_SLICES", "4")
@@ -49,8 +49,13 @@ def test_config_defaults_and_environment(monkeypatch):
     monkeypatch.setenv("CCR_DMA_CHUNK", str(1 << 21))
     monkeypatch.setenv("CCR_DMA_SYNC", "stream_flags")
     monkeypatch.setenv("CCR_DMA_ENGINES", "4")
+    monkeypatch.setenv("CCR_GRAPH_CACHE", "0")
     assert ccr.ccr_config_default() == ccr.Config("sdma", 32, 4, True, 1 << 20, 3, "fp32_partials", 4,
-                                                  1 << 21, "stream_flags", 4)
+                                                  1 << 21, "stream_flags", 4, False)
+    monkeypatch.setenv("CCR_GRAPH_CACHE", "2")
+    with pytest.raises(ccr.CcrError):
+        ccr.ccr_config_default()
+    monkeypatch.setenv("CCR_GRAPH_CACHE", "1")
     monkeypatch.setenv("CCR_DMA_ENGINES", "17")
     with pytest.raises(ccr.CcrError) as e:
         ccr.ccr_config_default()

@@ -193,3 +193,67 @@ def test_captured_three_stage_moe_replays(ccr_mod):
                 np.testing.assert_array_equal(to_host(out[r]), np.repeat(xs[r][:, None, :], K, axis=1))
 
         _replays(torch, g, reset, check, calls)
+
+
+# ------------------------------------------------ the library's graph cache
+_ORACLE = {"allreduce": lambda xs: oracle.ring_allreduce(xs, S=1),
+           "reduce_scatter": lambda xs: oracle.ring_reduce_scatter(xs, S=1),
+           "all_gather": lambda xs: oracle.ring_all_gather(xs, S=1)}
+
+
+@pytest.mark.parametrize("which", ["allreduce", "reduce_scatter", "all_gather"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_graph_cache_matches_eager(ccr_mod, dt, which):
+    """Small ring calls repeated on the same buffers: the first runs eagerly,
+    the second is captured, the rest replay; two buffer sets alternate; every
+    call bit-exact against the oracle, before and after a configuration
+    change (which drops the graphs) and with the cache off."""
+    import torch
+    R, n = 8, 3 * 65536 + 9
+    xs = workloads.random_buffers(R, n, dt, seed=61, dist="normal", scale=1e-2)
+    expect = _ORACLE[which](xs)
+    fn = getattr(ccr_mod, f"ccr_{which}")
+    say(f"graph cache {which} {dt}")
+    with ccr_mod.Context(0) as c:
+        src = [to_dev(x) for x in xs]
+        sets = [[t.clone() for t in src] for _ in range(2)]
+
+        def rounds(k):
+            for call in range(k):
+                for b in sets:
+                    for t, x in zip(b, src):
+                        t.copy_(x)
+                for b in sets:
+                    fn(c, b)
+                torch.cuda.synchronize()
+                for b in sets:
+                    for q in range(R):
+                        assert to_host(b[q]).tobytes() == expect[q].tobytes(), f"call {call} rank {q}"
+
+        rounds(5)
+        c.set_config(ccr_mod.Config(slices=2))  # drops the graphs; still cached afterwards
+        rounds(3)
+        c.set_config(ccr_mod.Config(graph_cache=False))
+        rounds(2)
+
+
+def test_graph_cache_replaces_least_recent(ccr_mod):
+    """More buffer sets than the cache holds (32), each called three times in
+    turn: graphs are captured, replaced and replayed; every result exact."""
+    import torch
+    R, n, sets_n = 4, 4096 + 8, 36
+    xs = workloads.random_buffers(R, n, "bf16", seed=62, dist="normal", scale=1e-2)
+    expect = oracle.ring_allreduce(xs, S=1)
+    say("graph cache eviction")
+    with ccr_mod.Context(0) as c:
+        src = [to_dev(x) for x in xs]
+        sets = [[t.clone() for t in src] for _ in range(sets_n)]
+        for rep in range(3):
+            for b in sets:
+                for t, x in zip(b, src):
+                    t.copy_(x)
+                ccr_mod.ccr_allreduce(c, b)
+            torch.cuda.synchronize()
+            for i, b in enumerate(sets):
+                for q in range(R):
+                    assert to_host(b[q]).tobytes() == expect[q].tobytes(), f"rep {rep} set {i} rank {q}"
