@@ -255,9 +255,9 @@ def bf16_modes(ccr, xs):
 def size_sweep(ccr, R=8, sizes_mib=(2, 4, 8, 16, 64, 256, 1024)):
     """The pages' message-size sweep (nccl-tests style), at R = 8 bf16 ranks:
     busBW of the all-reduce and of the all-gather alone, with kernel and
-    with SDMA copies, per-rank sizes in MiB; up to 4 MiB the kernel calls
-    replay from the context's graph cache; up to 16 MiB the eager all-reduce
-    is timed beside them."""
+    with SDMA copies, per-rank sizes in MiB; up to 2 MiB the kernel
+    all-reduce replays from the context's graph cache; up to 16 MiB the eager
+    all-reduce is timed beside it."""
     import torch
     out = []
     for mib in sizes_mib:
@@ -272,8 +272,8 @@ def size_sweep(ccr, R=8, sizes_mib=(2, 4, 8, 16, 64, 256, 1024)):
             row[f"allreduce_{mode}_busbw"] = round(2 * N / (ar * 1e-3) * 2 * (R - 1) / R / 1e9, 1)
             row[f"allgather_{mode}_busbw"] = round(2 * N / (ag * 1e-3) * (R - 1) / R / 1e9, 1)
         if mib <= 16:
-            # up to 4 MiB per rank the kernel rows above are replayed from the
-            # context's graph cache; the same calls launched eagerly:
+            # up to 2 MiB per rank the 8-rank all-reduce above is replayed from
+            # the context's graph cache; the same calls launched eagerly:
             with ccr.Context(0, ccr.Config(graph_cache=False)) as ctx:
                 ar = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 10, warm=2)
             row["allreduce_kernel_eager_busbw"] = round(2 * N / (ar * 1e-3) * 2 * (R - 1) / R / 1e9, 1)

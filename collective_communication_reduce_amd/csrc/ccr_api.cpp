@@ -571,18 +571,25 @@ std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, i
 ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int dtype,
                           int which, hipStream_t caller);
 
-// Replaying a captured graph pays up to this size per rank (8 bf16 ranks,
-// one call at a time: 48 instead of 78 us at 2 MiB, 48 instead of 65 us at
-// 4 MiB); from 8 MiB on, back-to-back replays run slower than eager launches.
-constexpr int64_t kGraphMaxRankBytes = int64_t(4) << 20;
+// A graph replay has a fixed cost of its own on this runtime, so it pays only
+// for a call of many small launches: measured on fp32 and bf16 rings, an
+// 8-rank all-reduce (13 launches) at 0.5-2 MiB per rank takes 39-42 us per
+// call instead of 46-49 (32-35 instead of 42-45 back to back), a 16-rank one
+// at 0.5 MiB 80 instead of 96; with 5-7 launches, or from 4 MiB per rank on,
+// replays are as slow as eager launches or slower.
+constexpr int64_t kGraphMaxRankBytes = int64_t(2) << 20;
+constexpr int kGraphMinLaunches = 12;
 
-// A ring call is replayed from a graph when it is small, made of kernel
-// launches on the caller's stream only (kernel copies, no CU budget, no
-// overlap, no fp32 partials), not profiled, and not itself being captured.
-bool ring_graph_eligible(ccr_ctx* ctx, int64_t rank_bytes, int dtype, int which,
+// A ring call is replayed from a graph when it is made of at least
+// kGraphMinLaunches small launches on the caller's stream only (kernel
+// copies, no CU budget, no overlap, no fp32 partials), is not profiled, and
+// is not itself being captured.
+bool ring_graph_eligible(ccr_ctx* ctx, int R, int64_t rank_bytes, int dtype, int which,
                          hipStream_t caller) {
   const ccr_config_t& c = ctx->cfg;
-  if (!c.graph_cache || ctx->prof_on || ctx->masked || c.overlap || rank_bytes > kGraphMaxRankBytes)
+  const int launches = which == kWhichAllreduce ? 2 * R - 3 : R - 1;  // one per hop
+  if (!c.graph_cache || ctx->prof_on || ctx->masked || c.overlap || rank_bytes > kGraphMaxRankBytes ||
+      launches < kGraphMinLaunches)
     return false;
   if (c.copy_mode == CCR_COPY_SDMA && which != kWhichRS) return false;
   if (dtype == CCR_BF16 && which != kWhichAG && c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS) return false;
@@ -687,7 +694,7 @@ ccr_status_t run_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count, int
   }
   CCR_TRY(check_disjoint(ranges, "bufs"));
   if (R == 1) return CCR_OK;
-  if (ring_graph_eligible(ctx, count * esize, dtype, which, caller)) {
+  if (ring_graph_eligible(ctx, R, count * esize, dtype, which, caller)) {
     bool launched = false;
     CCR_TRY(run_ring_graph(ctx, bufs, R, count, dtype, which, caller, &launched));
     if (launched) return CCR_OK;

@@ -133,8 +133,11 @@ typedef struct {
                                     move the copies at a lower rate: longer
                                     collectives, less traffic beside concurrent
                                     compute at any moment                          */
-    int32_t graph_cache;         /* 1 (default): a ring collective of at most 4 MiB
-                                    per rank made of kernel launches only (kernel
+    int32_t graph_cache;         /* 1 (default): a ring collective of at most 2 MiB
+                                    per rank and at least 12 hops (an all-reduce
+                                    over 8 or more ranks, a reduce-scatter or
+                                    all-gather over 13 or more) made of kernel
+                                    launches only (kernel
                                     copies, no CU budget, no overlap, no fp32
                                     partials) is captured into a HIP graph on its
                                     second call with the same buffers, count,

@@ -209,7 +209,8 @@ def test_graph_cache_matches_eager(ccr_mod, dt, which):
     call bit-exact against the oracle, before and after a configuration
     change (which drops the graphs) and with the cache off."""
     import torch
-    R, n = 8, 3 * 65536 + 9
+    # at least 12 hops, at most 2 MiB per rank: the calls the cache takes
+    R, n = (8 if which == "allreduce" else 14), 3 * 65536 + 9
     xs = workloads.random_buffers(R, n, dt, seed=61, dist="normal", scale=1e-2)
     expect = _ORACLE[which](xs)
     fn = getattr(ccr_mod, f"ccr_{which}")
@@ -241,7 +242,7 @@ def test_graph_cache_replaces_least_recent(ccr_mod):
     """More buffer sets than the cache holds (32), each called three times in
     turn: graphs are captured, replaced and replayed; every result exact."""
     import torch
-    R, n, sets_n = 4, 4096 + 8, 36
+    R, n, sets_n = 8, 4096 + 8, 36
     xs = workloads.random_buffers(R, n, "bf16", seed=62, dist="normal", scale=1e-2)
     expect = oracle.ring_allreduce(xs, S=1)
     say("graph cache eviction")
