@@ -59,9 +59,10 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     # libhsa-runtime64 (SDMA engine copies): resolved at load time to the HSA
-    # runtime already in the process (torch's), like libamdhip64.
+    # runtime already in the process (torch's), like libamdhip64.  The roctx
+    # library marks each entry point for rocprofv3's marker trace.
     r = subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-                        "-L/opt/rocm/lib", "-lhsa-runtime64"],
+                        "-L/opt/rocm/lib", "-lhsa-runtime64", "-lrocprofiler-sdk-roctx"],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of libccr.so failed:\n{r.stdout}{r.stderr}")

@@ -17,6 +17,7 @@
 // The ring order itself is the textbook ring (the paper describes none).
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <chrono>
@@ -63,6 +64,16 @@ ccr_status_t hip_fail(hipError_t e, const char* what) {
     hipError_t _e = (expr);                            \
     if (_e != hipSuccess) return hip_fail(_e, #expr);  \
   } while (0)
+
+// A roctx range around each entry point: `rocprofv3 --marker-trace` shows
+// every call's host span next to the kernels and copies it enqueued.
+struct Mark {
+  explicit Mark(const char* name) { roctxRangePushA(name); }
+  ~Mark() { roctxRangePop(); }
+  Mark(const Mark&) = delete;
+  Mark& operator=(const Mark&) = delete;
+};
+#define CCR_MARK(name) Mark ccr_mark_(name)
 
 #define CCR_TRY(expr)                    \
   do {                                   \
@@ -1007,6 +1018,7 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
 
 ccr_status_t ccr_traffic_matrix(const int64_t* C, int G, const int32_t* node, const int32_t* peer,
                                 int64_t* T) {
+  CCR_MARK("ccr_traffic_matrix");
   ScheduleProblem p;
   p.G = G;
   p.C = C;
@@ -1023,6 +1035,7 @@ ccr_status_t ccr_schedule_stages(const int64_t* C, int G, const int32_t* node, c
                                  int64_t bw_scaleup, int64_t bw_rdma, ccr_stage_entry_t* entries,
                                  int64_t max_entries, int64_t* n_entries, ccr_stage_time_t* times,
                                  int64_t max_stages, int64_t* n_stages) {
+  CCR_MARK("ccr_schedule_stages");
   ScheduleProblem p;
   p.G = G;
   p.C = C;
@@ -1054,21 +1067,25 @@ ccr_status_t ccr_schedule_stages(const int64_t* C, int G, const int32_t* node, c
 
 ccr_status_t ccr_allreduce(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
                            void* stream) {
+  CCR_MARK("ccr_allreduce");
   return run_ring(ctx, bufs, R, count, dtype, kWhichAllreduce, static_cast<hipStream_t>(stream));
 }
 
 ccr_status_t ccr_reduce_scatter(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
                                 void* stream) {
+  CCR_MARK("ccr_reduce_scatter");
   return run_ring(ctx, bufs, R, count, dtype, kWhichRS, static_cast<hipStream_t>(stream));
 }
 
 ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void* const* bufs, int R, int64_t count, int dtype,
                             void* stream) {
+  CCR_MARK("ccr_all_gather");
   return run_ring(ctx, bufs, R, count, dtype, kWhichAG, static_cast<hipStream_t>(stream));
 }
 
 ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* recv, int n,
                           int64_t nbytes, void* stream) {
+  CCR_MARK("ccr_sendrecv");
   CCR_TRY(check_ctx(ctx));
   if (n < 0 || nbytes < 0) return fail(CCR_ERR_INVALID_ARG, "n or nbytes < 0");
   if (nbytes % 16 != 0) return fail(CCR_ERR_INVALID_ARG, "nbytes %lld is not a multiple of 16", (long long)nbytes);
@@ -1143,6 +1160,7 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
 
 ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
                           const int64_t* counts, int64_t row_bytes, void* stream) {
+  CCR_MARK("ccr_alltoall");
   CCR_TRY(check_ctx(ctx));
   if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
   if (!send || !recv || !counts) return fail(CCR_ERR_INVALID_ARG, "send, recv or counts is NULL");
@@ -1182,6 +1200,7 @@ ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* r
 
 ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void* dst, const void* src, const int32_t* d_idx,
                               int64_t nrows, int64_t nsrc, int64_t row_bytes, void* stream) {
+  CCR_MARK("ccr_permute_rows");
   CCR_TRY(check_ctx(ctx));
   if (nrows < 0 || nsrc < 0) return fail(CCR_ERR_INVALID_ARG, "nrows or nsrc < 0");
   if (row_bytes <= 0 || row_bytes % 16 != 0)
@@ -1206,6 +1225,7 @@ ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void* dst, const void* src, const i
 
 ccr_status_t ccr_moe_topk(ccr_ctx_t ctx, const float* logits, int32_t* topk, int64_t T, int E,
                           int K, void* stream) {
+  CCR_MARK("ccr_moe_topk");
   CCR_TRY(check_ctx(ctx));
   if (T < 0 || E < 1 || E > 1024 || K < 1 || K > 16 || K > E)
     return fail(CCR_ERR_INVALID_ARG, "need T >= 0, 1 <= E <= 1024, 1 <= K <= min(E, 16)");
@@ -1218,6 +1238,7 @@ ccr_status_t ccr_moe_topk(ccr_ctx_t ctx, const float* logits, int32_t* topk, int
 
 ccr_status_t ccr_moe_plan(ccr_ctx_t ctx, const int32_t* topk, int64_t T, int E, int K, int R,
                           int32_t* src_tok, int32_t* slot, int64_t* h_ecnt, void* stream) {
+  CCR_MARK("ccr_moe_plan");
   CCR_TRY(check_ctx(ctx));
   if (T < 0 || T > INT32_MAX / 16 || E < 1 || E > 1024 || K < 1 || K > 16 || K > E || R < 1 ||
       R > kMaxRanks || E % R != 0)
@@ -1358,6 +1379,7 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
                               const int64_t* h_ecnt, int R, int64_t T, int E, int K,
                               int64_t row_bytes, void* const* send, void* const* recv,
                               void* const* exp, void* stream) {
+  CCR_MARK("ccr_moe_dispatch");
   MoeShape m;
   CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
   if (T == 0) return CCR_OK;
@@ -1400,6 +1422,7 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
                              const int64_t* h_ecnt, int R, int64_t T, int E, int K,
                              int64_t row_bytes, void* const* recv, void* const* send,
                              void* const* out, void* stream) {
+  CCR_MARK("ccr_moe_combine");
   MoeShape m;
   CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
   if (T == 0) return CCR_OK;
@@ -1525,6 +1548,7 @@ ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void* const* x,
                                     const int32_t* const* src_tok, const int64_t* h_ecnt, int R,
                                     int64_t T, int E, int K, int64_t row_bytes, void* const* exp,
                                     void* stream) {
+  CCR_MARK("ccr_moe_dispatch_fused");
   MoeShape m;
   CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
   if (T == 0) return CCR_OK;
@@ -1547,6 +1571,7 @@ ccr_status_t ccr_moe_dispatch_fused(ccr_ctx_t ctx, const void* const* x,
 ccr_status_t ccr_moe_combine_fused(ccr_ctx_t ctx, const void* const* exp, const int32_t* const* slot,
                                    const int64_t* h_ecnt, int R, int64_t T, int E, int K,
                                    int64_t row_bytes, void* const* out, void* stream) {
+  CCR_MARK("ccr_moe_combine_fused");
   MoeShape m;
   CCR_TRY(moe_shape(ctx, h_ecnt, R, T, E, K, row_bytes, &m));
   if (T == 0) return CCR_OK;

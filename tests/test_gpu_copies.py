@@ -244,3 +244,23 @@ def test_alltoall_max_ranks_and_empty(ccr_mod, mode):
         torch.cuda.synchronize()
         for a, b in zip(r[:3], keep):
             assert to_host(a).tobytes() == b.tobytes()
+
+
+def test_staging_allocation_failure_is_reported(ccr_mod):
+    """A staging pool larger than the device holds: the call returns
+    CCR_ERR_OOM and enqueues nothing, and the context works again once the
+    configuration asks for a pool that fits."""
+    import torch
+    say("staging allocation failure")
+    x = torch.arange(4096, dtype=torch.int32, device="cuda")
+    y = torch.zeros_like(x)
+    with ccr_mod.Context(0, ccr_mod.Config(staging_chunk_bytes=1 << 42, staging_slots=2)) as c:
+        with pytest.raises(ccr_mod.CcrError) as e:
+            ccr_mod.ccr_sendrecv(c, [x], [y])
+        assert e.value.status == ccr_mod.CCR_ERR_OOM, ccr_mod.ccr_last_error()
+        torch.cuda.synchronize()
+        assert not y.any()
+        c.set_config(ccr_mod.Config())
+        ccr_mod.ccr_sendrecv(c, [x], [y])
+        torch.cuda.synchronize()
+        assert torch.equal(x, y)
