@@ -426,6 +426,35 @@ def workload_timings(ccr, workloads):
     return out
 
 
+def oracle_timings(workloads):
+    """The CPU oracle on the other workloads, one host core, each at its full
+    size (inputs generated beforehand, outside the timing; one call each)."""
+    import oracle
+    out = {}
+
+    def once(fn):
+        t = time.perf_counter()
+        fn()
+        return round((time.perf_counter() - t) * 1e3, 1)
+
+    w = workloads.RING_SMALL_F32
+    xs = workloads.ring_inputs(w)
+    out[w.name] = once(lambda: oracle.ring_allreduce(xs, S=w.slices))
+    w = workloads.RS_AG_R32_F32
+    xs = workloads.ring_inputs(w)
+    out[w.name] = once(lambda: oracle.ring_all_gather(oracle.ring_reduce_scatter(xs, S=w.slices),
+                                                      S=w.slices))
+    del xs
+    pw = workloads.PP_STAGING_BF16
+    mbs = workloads.staging_inputs(pw)
+    out[pw.name] = once(lambda: oracle.staged_copy(mbs, pw.chunk_bytes, pw.slots))
+    m = workloads.MOE_DISPATCH_BF16
+    xs, logits = workloads.moe_inputs(m)
+    out[m.name] = once(lambda: oracle.moe_dispatch(xs, [oracle.moe_topk(l, m.topk) for l in logits],
+                                                   m.experts))
+    return {k: {"oracle_ms": v, "cores": 1} for k, v in out.items()}
+
+
 def schedule_timings(ccr, workloads):
     """Stage decomposition (host only) of a skewed expert-parallel dispatch
     over a modelled two-node, 16-GPU MI355X cluster: the stage count, the
@@ -729,6 +758,9 @@ def main():
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
         cpu = cpu_baseline(xs, R, count, esize, S)
+        if others is not None:
+            log("bench: CPU oracle on the other workloads")
+            cpu["other_workloads"] = oracle_timings(workloads)
 
     line = {
         "metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1,
