@@ -874,7 +874,9 @@ ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* re
   int64_t total = 0;
   for (const Piece& x : p) total += x.nbytes;
   const int E = dma_engine_limit(ctx);
-  const int64_t C = ctx->cfg.dma_chunk_bytes > 0 ? ctx->cfg.dma_chunk_bytes : auto_chunk(total, E);
+  int64_t C = ctx->cfg.dma_chunk_bytes > 0 ? ctx->cfg.dma_chunk_bytes : auto_chunk(total, E);
+  // at most ~64 Ki chunks per job, whatever chunk size was asked for
+  C = std::max(C, (ceil_div(total, int64_t(1) << 16) + 15) & ~int64_t(15));
   return dma_submit(ctx, flow_chunks(p, C, E), s);
 }
 

@@ -126,7 +126,8 @@ typedef struct {
     int32_t dma_stripe;          /* SDMA: engines each staging fill/drain is striped
                                     over; 0 = half the engines                      */
     int64_t dma_chunk_bytes;     /* SDMA: all-to-all flows are cut into chunks of at
-                                    most this size (multiple of 16); 0 = automatic  */
+                                    most this size (multiple of 16); 0 = automatic;
+                                    raised if a job would need over 64 Ki chunks    */
     int32_t dma_sync;            /* ccr_dma_sync_t                                  */
     int32_t dma_engines;         /* SDMA: engines one call may use, 1..16 (the first
                                     of the usable ones); 0 = all.  Fewer engines
