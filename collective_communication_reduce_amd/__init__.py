@@ -127,6 +127,14 @@ def _load():
 _lib = _load()
 
 
+def _raw_stream_getter():
+    import torch
+    return getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+_raw_stream = _raw_stream_getter()
+
+
 def _check(status: int):
     if status != CCR_OK:
         raise CcrError(status, _lib.ccr_last_error().decode())
@@ -232,6 +240,9 @@ def _dtype_code(t) -> int:
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
+        # the raw handle of the current stream, without building a Stream object
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
@@ -248,6 +259,21 @@ def _same(tensors):
     if any(t.numel() != n or t.dtype != dt for t in tensors):
         raise ValueError("all ranks need the same element count and dtype")
     return n
+
+
+def _ring_args(bufs):
+    """(pointer array, count, dtype code) of R same-shaped contiguous device
+    tensors, in one pass."""
+    t0 = bufs[0]
+    n, dt = t0.numel(), t0.dtype
+    ptrs = (ctypes.c_void_p * len(bufs))()
+    for i, t in enumerate(bufs):
+        if t.numel() != n or t.dtype != dt:
+            raise ValueError("all ranks need the same element count and dtype")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        ptrs[i] = t.data_ptr()
+    return ptrs, n, _dtype_code(t0)
 
 
 # --------------------------------------------------------------- C entries
@@ -302,21 +328,18 @@ def ccr_schedule_stages(C, node, peer, bw_scaleup: int, bw_rdma: int):
 
 
 def ccr_allreduce(ctx: Context, bufs: Sequence, stream=None):
-    n = _same(bufs)
-    _check(_lib.ccr_allreduce(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
-                              _stream(stream)))
+    ptrs, n, dt = _ring_args(bufs)
+    _check(_lib.ccr_allreduce(ctx.handle, ptrs, len(bufs), n, dt, _stream(stream)))
 
 
 def ccr_reduce_scatter(ctx: Context, bufs: Sequence, stream=None):
-    n = _same(bufs)
-    _check(_lib.ccr_reduce_scatter(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
-                                   _stream(stream)))
+    ptrs, n, dt = _ring_args(bufs)
+    _check(_lib.ccr_reduce_scatter(ctx.handle, ptrs, len(bufs), n, dt, _stream(stream)))
 
 
 def ccr_all_gather(ctx: Context, bufs: Sequence, stream=None):
-    n = _same(bufs)
-    _check(_lib.ccr_all_gather(ctx.handle, _ptrs(bufs), len(bufs), n, _dtype_code(bufs[0]),
-                               _stream(stream)))
+    ptrs, n, dt = _ring_args(bufs)
+    _check(_lib.ccr_all_gather(ctx.handle, ptrs, len(bufs), n, dt, _stream(stream)))
 
 
 def ccr_sendrecv(ctx: Context, send: Sequence, recv: Sequence, stream=None):
