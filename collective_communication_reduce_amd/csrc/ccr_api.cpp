@@ -127,7 +127,7 @@ struct ccr_ctx {
     std::vector<void*> bufs;
     int64_t count = 0;
     int dtype = 0, which = 0;
-    int uses = 0;                   // calls seen with this key
+    int uses = 0;                   // calls seen with this key; < 0: never capture it
     uint64_t last = 0;              // tick of the last use (least recently used is replaced)
     hipGraphExec_t exec = nullptr;
   };
@@ -665,24 +665,27 @@ ccr_status_t run_ring_graph(ccr_ctx* ctx, void* const* bufs, int R, int64_t coun
     g->which = which;
   }
   g->last = ++ctx->graph_tick;
-  if (!g->exec && ++g->uses >= 2) {
+  if (!g->exec && g->uses >= 0 && ++g->uses >= 2) {
+    // A capture that the runtime refuses or cannot instantiate leaves this
+    // key to eager launches for good (uses < 0); the call itself goes on.
     hipStream_t cs = ctx->s_a;
-    HIP_TRY(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-    const ccr_status_t st = enqueue_ring(ctx, bufs, R, count, dtype, which, cs);
     hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      (void)hipGetLastError();
+      g->uses = -1;
+      return CCR_OK;
+    }
+    const ccr_status_t st = enqueue_ring(ctx, bufs, R, count, dtype, which, cs);
     const hipError_t e = hipStreamEndCapture(cs, &graph);
-    if (st != CCR_OK || e != hipSuccess) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return st != CCR_OK ? st : hip_fail(e, "hipStreamEndCapture");
-    }
-    const hipError_t ei = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (ei != hipSuccess) {
+    if (st != CCR_OK || e != hipSuccess ||
+        hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+      (void)hipGetLastError();
       g->exec = nullptr;
-      return hip_fail(ei, "hipGraphInstantiate");
+      g->uses = -1;
     }
+    if (graph) (void)hipGraphDestroy(graph);
   }
-  if (!g->exec) return CCR_OK;  // first sight: the caller launches eagerly
+  if (!g->exec) return CCR_OK;  // first sight, or not capturable: the caller launches eagerly
   HIP_TRY(hipGraphLaunch(g->exec, caller));
   *launched = true;
   return CCR_OK;
