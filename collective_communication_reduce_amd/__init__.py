@@ -91,6 +91,7 @@ _SIGNATURES = {
     "ccr_sendrecv_slot_log": [_vp, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_stream_wait": [_vp, _vp, _i32],
     "ccr_dma_hold_finish": [_vp, _i32],
+    "ccr_graph_cache_stats": [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
 }
 
 
@@ -491,3 +492,10 @@ def ccr_stream_wait(ctx: Context, timeout_ms: int, stream=None) -> int:
 
 def ccr_dma_hold_finish(ctx: Context, us: int):
     _check(_lib.ccr_dma_hold_finish(ctx.handle, us))
+
+
+def ccr_graph_cache_stats(ctx: Context) -> tuple:
+    """(graphs held, ring calls served by a replay so far)."""
+    g, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.ccr_graph_cache_stats(ctx.handle, ctypes.byref(g), ctypes.byref(r)))
+    return g.value, r.value

@@ -134,6 +134,7 @@ struct ccr_ctx {
   static constexpr size_t kMaxRingGraphs = 32;
   std::vector<RingGraph> graphs;
   uint64_t graph_tick = 0;
+  int64_t graph_replays = 0;
   // per-launch timing (ccr_profile_enable): event pairs and payload bytes
   bool prof_on = false;
   struct Timed {
@@ -687,6 +688,7 @@ ccr_status_t run_ring_graph(ccr_ctx* ctx, void* const* bufs, int R, int64_t coun
   }
   if (!g->exec) return CCR_OK;  // first sight, or not capturable: the caller launches eagerly
   HIP_TRY(hipGraphLaunch(g->exec, caller));
+  ctx->graph_replays++;
   *launched = true;
   return CCR_OK;
 }
@@ -1635,6 +1637,15 @@ ccr_status_t ccr_profile_intervals(ccr_ctx_t ctx, int kind, void* ref_event, dou
     k++;
   }
   *n = k;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_graph_cache_stats(ccr_ctx_t ctx, int64_t* graphs, int64_t* replays) {
+  if (!ctx) return fail(CCR_ERR_INVALID_ARG, "ctx is NULL");
+  int64_t n = 0;
+  for (const auto& g : ctx->graphs) n += g.exec != nullptr;
+  if (graphs) *graphs = n;
+  if (replays) *replays = ctx->graph_replays;
   return CCR_OK;
 }
 

@@ -406,6 +406,10 @@ const char *ccr_version(void);
  * [3*nblocks].  Used to show which compute units a CU budget leaves to the
  * collective. */
 ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *stream);
+/* The context's graph cache (ccr_config_t.graph_cache): *graphs = captured
+ * graphs it holds now, *replays = ring calls served by a replay since the
+ * context was created.  Host only; either pointer may be NULL. */
+ccr_status_t ccr_graph_cache_stats(ccr_ctx_t ctx, int64_t *graphs, int64_t *replays);
 
 /* Per-launch timing of the collectives' own kernels and SDMA copies.
  * While enabled, every reduce launch, copy launch and SDMA copy issued by

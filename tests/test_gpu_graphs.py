@@ -232,15 +232,21 @@ def test_graph_cache_matches_eager(ccr_mod, dt, which):
                         assert to_host(b[q]).tobytes() == expect[q].tobytes(), f"call {call} rank {q}"
 
         rounds(5)
+        graphs, replays = ccr_mod.ccr_graph_cache_stats(c)
+        assert graphs == 2 and replays == 2 * 4  # per set: eager, capture + replay, 3 replays
         c.set_config(ccr_mod.Config(slices=2))  # drops the graphs; still cached afterwards
+        assert ccr_mod.ccr_graph_cache_stats(c) == (0, replays)
         rounds(3)
+        assert ccr_mod.ccr_graph_cache_stats(c) == (2, replays + 2 * 2)
         c.set_config(ccr_mod.Config(graph_cache=False))
         rounds(2)
+        assert ccr_mod.ccr_graph_cache_stats(c) == (0, replays + 2 * 2)
 
 
 def test_graph_cache_replaces_least_recent(ccr_mod):
-    """More buffer sets than the cache holds (32), each called three times in
-    turn: graphs are captured, replaced and replayed; every result exact."""
+    """More buffer sets than the cache holds (32): each set is called twice
+    in a row (eager, then captured and replayed), so every new set beyond
+    the 32nd replaces a captured graph; every result exact."""
     import torch
     R, n, sets_n = 8, 4096 + 8, 36
     xs = workloads.random_buffers(R, n, "bf16", seed=62, dist="normal", scale=1e-2)
@@ -249,12 +255,15 @@ def test_graph_cache_replaces_least_recent(ccr_mod):
     with ccr_mod.Context(0) as c:
         src = [to_dev(x) for x in xs]
         sets = [[t.clone() for t in src] for _ in range(sets_n)]
-        for rep in range(3):
-            for b in sets:
-                for t, x in zip(b, src):
-                    t.copy_(x)
-                ccr_mod.ccr_allreduce(c, b)
-            torch.cuda.synchronize()
+        for rep in range(2):
             for i, b in enumerate(sets):
-                for q in range(R):
-                    assert to_host(b[q]).tobytes() == expect[q].tobytes(), f"rep {rep} set {i} rank {q}"
+                for call in range(2):
+                    for t, x in zip(b, src):
+                        t.copy_(x)
+                    ccr_mod.ccr_allreduce(c, b)
+                    torch.cuda.synchronize()
+                    for q in range(R):
+                        assert to_host(b[q]).tobytes() == expect[q].tobytes(), \
+                            f"rep {rep} set {i} call {call} rank {q}"
+        graphs, replays = ccr_mod.ccr_graph_cache_stats(c)
+        assert graphs == 32 and replays == 2 * sets_n
