@@ -704,12 +704,26 @@ def main():
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
 
+    # Every part after the timed steps is context: a part that fails (e.g. no
+    # usable SDMA engine on a machine) is reported under "errors" instead of
+    # taking the headline line down with it.
+    errors = {}
+
+    def guarded(name, fn):
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001
+            log(f"bench: {name} failed: {e}")
+            errors[name] = f"{type(e).__name__}: {e}"
+            return None
+
     restored = copy_gbs = None
     if not args.ring_only:
         log("bench: per-step times with inputs restored before each step")
-        restored = percentiles(restored_steps(step, bufs, max(20, args.steps)))
+        restored = guarded("restored_inputs",
+                           lambda: percentiles(restored_steps(step, bufs, max(20, args.steps))))
         log("bench: plain 1 GiB copy (copy roofline)")
-        copy_gbs = copy_roofline(ccr)
+        copy_gbs = guarded("copy_roofline", lambda: copy_roofline(ccr))
     if args.ring_only:
         args.no_gemm = args.no_cpu = True
 
@@ -719,48 +733,54 @@ def main():
         runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32, 16) for m in ("kernel", "sdma")]
         runs += [dict(cfg, copy_mode="sdma", dma_engines=e) for e in (8, 4, 2)]
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
-        gemm = overlap_runs(ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs,
-                            (8192, 8192, 8192), 20, 6)
+        gemm = guarded("gemm_slowdown", lambda: overlap_runs(
+            ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs, (8192, 8192, 8192), 20, 6))
         log("bench: concurrent GEMM, pipeline-parallel send/recv through staging")
         pw = workloads.PP_STAGING_BF16
         mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
                for _ in range(pw.microbatches)]
         outs = [torch.empty_like(x) for x in mbs]
         stg = dict(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
-        pp = overlap_runs(ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
-                          [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
-                           dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2)],
-                          (4096, 4096, 16384), 20, 20)
-        pp["workload"] = pw.name
+        pp = guarded("pp_staging_gemm_slowdown", lambda: overlap_runs(
+            ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
+            [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
+             dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2)],
+            (4096, 4096, 16384), 20, 20))
+        if pp is not None:
+            pp["workload"] = pw.name
         log("bench: compute units reached under each CU budget; host time per call")
-        occ = cu_occupancy(ccr)
-        launch = {}
-        for m in ("kernel", "sdma"):
-            with ccr.Context(0, ccr.Config(**dict(cfg, copy_mode=m))) as c2:
-                ccr.ccr_allreduce(c2, bufs)
-                launch[f"allreduce_{m}"] = host_call_us(ccr, lambda: ccr.ccr_allreduce(c2, bufs), 20)
-            with ccr.Context(0, ccr.Config(**dict(stg, copy_mode=m))) as c2:
-                ccr.ccr_sendrecv(c2, mbs[:1], outs[:1])
-                launch[f"sendrecv_16MiB_{m}"] = host_call_us(
-                    ccr, lambda: ccr.ccr_sendrecv(c2, mbs[:1], outs[:1]), 20)
+        occ = guarded("cu_occupancy", lambda: cu_occupancy(ccr))
+
+        def host_costs():
+            out = {}
+            for m in ("kernel", "sdma"):
+                with ccr.Context(0, ccr.Config(**dict(cfg, copy_mode=m))) as c2:
+                    ccr.ccr_allreduce(c2, bufs)
+                    out[f"allreduce_{m}"] = host_call_us(ccr, lambda: ccr.ccr_allreduce(c2, bufs), 20)
+                with ccr.Context(0, ccr.Config(**dict(stg, copy_mode=m))) as c2:
+                    ccr.ccr_sendrecv(c2, mbs[:1], outs[:1])
+                    out[f"sendrecv_16MiB_{m}"] = host_call_us(
+                        ccr, lambda: ccr.ccr_sendrecv(c2, mbs[:1], outs[:1]), 20)
+            return out
+        launch = guarded("host_us_per_call", host_costs)
 
     others = None
     if not args.no_gemm:
         log("bench: the other workloads (context)")
-        others = workload_timings(ccr, workloads)
-        others["stage_schedule"] = schedule_timings(ccr, workloads)
+        others = guarded("other_workloads", lambda: workload_timings(ccr, workloads)) or {}
+        others["stage_schedule"] = guarded("stage_schedule", lambda: schedule_timings(ccr, workloads))
         log("bench: bf16 accumulation modes on the bucket")
-        others["dp_bucket_bf16_accumulation"] = bf16_modes(ccr, xs)
+        others["dp_bucket_bf16_accumulation"] = guarded("bf16_modes", lambda: bf16_modes(ccr, xs))
         log("bench: message-size sweep")
-        others["size_sweep_r8_bf16"] = size_sweep(ccr)
+        others["size_sweep_r8_bf16"] = guarded("size_sweep", lambda: size_sweep(ccr))
 
     cpu = None
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
-        cpu = cpu_baseline(xs, R, count, esize, S)
-        if others is not None:
+        cpu = guarded("cpu_baseline", lambda: cpu_baseline(xs, R, count, esize, S))
+        if others is not None and cpu is not None:
             log("bench: CPU oracle on the other workloads")
-            cpu["other_workloads"] = oracle_timings(workloads)
+            cpu["other_workloads"] = guarded("cpu_other_workloads", lambda: oracle_timings(workloads))
 
     line = {
         "metric": METRIC, "value": round(bus, 2), "unit": "GB/s", "n_gpus": 1,
@@ -811,6 +831,7 @@ def main():
         "host_us_per_call": launch,
         "other_workloads": others,
         "cpu_baseline": cpu,
+        **({"errors": errors} if errors else {}),
     }
     ctx.close()
     print(json.dumps(line), flush=True)
