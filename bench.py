@@ -97,6 +97,23 @@ def _new_own_queue_stream():
     return torch.cuda.ExternalStream(s.value)
 
 
+def contention_rate(intervals, window_ms, n_cu):
+    """HOCCL Eq. 1 over one window [0, window_ms] in which compute is active
+    throughout: the integral of the compute units held by communication
+    kernels, over n_cu times the window.  intervals: (start, end, cus) per
+    kernel in ms from the window's start; at any moment the kernels running
+    hold the sum of their cus, at most n_cu.  Computed by sweeping the
+    interval ends."""
+    edges = sorted([(max(0.0, s), cu) for s, e, cu in intervals if e > 0 and s < window_ms] +
+                   [(min(window_ms, e), -cu) for s, e, cu in intervals if e > 0 and s < window_ms])
+    held, level, last = 0.0, 0.0, 0.0
+    for t, d in edges:
+        held += min(n_cu, level) * (t - last)
+        level += d
+        last = t
+    return held / (n_cu * window_ms)
+
+
 PAIRS = 9  # interleaved GEMM-alone / loaded window pairs per overlap configuration
 
 
@@ -160,15 +177,7 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
         iv = np.concatenate([ccr.ccr_profile_intervals(ctx, k, ev[0])
                              for k in ("reduce", "copy_kernel", "reduce_forward")])
         ccr.ccr_profile_enable(ctx, False)
-        # sweep the interval ends: CUs held at t = min(n_cu, sum over running kernels)
-        edges = sorted([(max(0.0, s), cu) for s, e, cu in iv if e > 0 and s < gemm] +
-                       [(min(gemm, e), -cu) for s, e, cu in iv if e > 0 and s < gemm])
-        held, level, last = 0.0, 0.0, 0.0
-        for t, d in edges:
-            held += min(n_cu, level) * (t - last)
-            level += d
-            last = t
-        return held / (n_cu * gemm)
+        return contention_rate(iv, gemm, n_cu)
 
     with torch.cuda.stream(g):
         gemms()

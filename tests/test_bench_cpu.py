@@ -1,8 +1,9 @@
 """The benchmark's own arithmetic and contract, on the CPU: the algorithmic
 byte count of a ring all-reduce against a hop-by-hop count, the traffic
 figure read from the committed counter summary (and dropped when the kernel
-source no longer matches it), the percentile summary, and the refusal of
-more than one GPU."""
+source no longer matches it), the percentile summary, the contention rate
+(HOCCL Eq. 1) against a direct integral, and the refusal of more than one
+GPU."""
 import os
 import subprocess
 import sys
@@ -60,3 +61,28 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def _contention_brute(intervals, window, n_cu, steps=20000):
+    dt = window / steps
+    held = 0.0
+    for i in range(steps):
+        t = (i + 0.5) * dt
+        held += min(n_cu, sum(cu for s, e, cu in intervals if s <= t < e)) * dt
+    return held / (n_cu * window)
+
+
+def test_contention_rate_matches_a_direct_integral():
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        iv = []
+        for _ in range(rng.integers(0, 12)):
+            s = rng.uniform(-2.0, 11.0)
+            iv.append((s, s + rng.uniform(0.01, 4.0), int(rng.integers(1, 300))))
+        got = bench.contention_rate(iv, 10.0, 256)
+        assert abs(got - _contention_brute(iv, 10.0, 256)) < 2e-3
+    assert bench.contention_rate([], 5.0, 256) == 0.0
+    # one kernel holding every CU for the whole window, another on top: capped at 1
+    assert bench.contention_rate([(0.0, 5.0, 256), (1.0, 2.0, 64)], 5.0, 256) == pytest.approx(1.0)
+    # half the CUs for half the window
+    assert bench.contention_rate([(2.5, 9.0, 128)], 5.0, 256) == pytest.approx(0.25)
