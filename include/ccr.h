@@ -138,17 +138,18 @@ typedef struct {
                                     per rank and at least 12 hops (an all-reduce
                                     over 8 or more ranks, a reduce-scatter or
                                     all-gather over 13 or more) made of kernel
-                                    launches only (kernel
-                                    copies, no CU budget, no overlap, no fp32
-                                    partials) is captured into a HIP graph on its
-                                    second call with the same buffers, count,
-                                    dtype and operation, and replayed from then
-                                    on (one host call instead of 2(R-1)
-                                    launches); 0: always launch eagerly.  The
-                                    context keeps up to 32 graphs; replacing one
-                                    of a full cache, ccr_ctx_set_config and
-                                    ccr_ctx_destroy synchronise the device before
-                                    destroying graphs                               */
+                                    launches only (kernel copies, no CU budget,
+                                    no overlap, no fp32 partials) is captured
+                                    into a HIP graph on its second call with the
+                                    same buffers, count, dtype and operation,
+                                    and replayed from then on (one host call
+                                    instead of one launch per hop); arguments
+                                    are still checked on every call.  0: always
+                                    launch eagerly.  The context keeps up to 32
+                                    graphs; replacing one of a full cache,
+                                    ccr_ctx_set_config and ccr_ctx_destroy
+                                    synchronise the device before destroying
+                                    graphs.  See ccr_graph_cache_stats.        */
 } ccr_config_t;
 
 typedef struct ccr_ctx *ccr_ctx_t;
