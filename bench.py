@@ -186,6 +186,9 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
     out = {"gemm": f"{M}x{N}x{K} bf16 x{n_gemm}", "gemm_alone_ms": round(alone, 3),
            "collectives_per_window": n_coll, "runs": []}
     for conf in runs:
+        if conf.get("dma_deadline_us") == "window":
+            # each collective may take its share of the GEMMs' window alone
+            conf = dict(conf, dma_deadline_us=int(alone * 1e3 / n_coll))
         with ccr.Context(0, ccr.Config(**conf)) as ctx:
             collective(ctx, c)  # first use starts the SDMA proxy
             torch.cuda.synchronize()
@@ -200,6 +203,11 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
             alone_i = sorted(a_ms)[PAIRS // 2]
             gemm, coll, span = sorted(b_runs)[PAIRS // 2]
             i_coll = contention(ctx)
+            paced = None
+            if conf["copy_mode"] == "sdma" and conf.get("dma_deadline_us"):
+                gbs, used = ccr.ccr_dma_rate(ctx)
+                paced = {"deadline_us": conf["dma_deadline_us"], "engine_gbs": round(gbs, 1),
+                         "engines_used": used}
             out["runs"].append({
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
                 "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
@@ -212,8 +220,18 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
                 "collectives_under_load_ms": round(coll, 3),
                 "makespan_ms": round(span, 3),
                 "makespan_over_gemm_alone_pct": round(100.0 * (span / alone_i - 1.0), 2),
-                "contention_rate": round(i_coll, 4)})
+                "contention_rate": round(i_coll, 4),
+                **({"dma_deadline": paced} if paced else {})})
     return out
+
+
+def slowdown_key(r):
+    """Name of a full-CU overlap run in the GEMM-slowdown summary."""
+    if "dma_deadline" in r:
+        return "sdma_deadline"
+    if r["dma_engines"] in (None, "all"):
+        return r["copy_mode"]
+    return f"sdma_{r['dma_engines']}_engines"
 
 
 def median_ms(fn, reps=10, warm=3, before=None):
@@ -741,6 +759,7 @@ def main():
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
         runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32, 16) for m in ("kernel", "sdma")]
         runs += [dict(cfg, copy_mode="sdma", dma_engines=e) for e in (8, 4, 2)]
+        runs.append(dict(cfg, copy_mode="sdma", dma_deadline_us="window"))
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
         gemm = guarded("gemm_slowdown", lambda: overlap_runs(
             ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs, (8192, 8192, 8192), 20, 6))
@@ -753,7 +772,8 @@ def main():
         pp = guarded("pp_staging_gemm_slowdown", lambda: overlap_runs(
             ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
             [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
-             dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2)],
+             dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2),
+             dict(stg, copy_mode="sdma", dma_deadline_us="window")],
             (4096, 4096, 16384), 20, 20))
         if pp is not None:
             pp["workload"] = pw.name
@@ -831,8 +851,7 @@ def main():
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
         "gemm_slowdown_pct": None if gemm is None else {
-            (r["copy_mode"] if r["dma_engines"] in (None, "all") else f"sdma_{r['dma_engines']}_engines"):
-            r["slowdown_pct"] for r in gemm["runs"]
+            slowdown_key(r): r["slowdown_pct"] for r in gemm["runs"]
             if r["cu_budget"] == 256 and r["dma_sync"] in (None, "host_func")},
         "gemm_slowdown": gemm,
         "pp_staging_gemm_slowdown": pp,

@@ -40,7 +40,8 @@ class ccr_config_t(ctypes.Structure):
                 ("staging_chunk_bytes", ctypes.c_int64), ("staging_slots", ctypes.c_int32),
                 ("bf16_acc", ctypes.c_int32), ("dma_stripe", ctypes.c_int32),
                 ("dma_chunk_bytes", ctypes.c_int64), ("dma_sync", ctypes.c_int32),
-                ("dma_engines", ctypes.c_int32), ("graph_cache", ctypes.c_int32)]
+                ("dma_engines", ctypes.c_int32), ("graph_cache", ctypes.c_int32),
+                ("dma_deadline_us", ctypes.c_int32)]
 
 
 class ccr_ring_op_t(ctypes.Structure):
@@ -88,6 +89,8 @@ _SIGNATURES = {
     "ccr_profile_read": [_vp, _i32, _vp],
     "ccr_profile_intervals": [_vp, _i32, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_dma_info": [_vp, _vp, _vp],
+    "ccr_dma_pace": [_i64, _i64, ctypes.c_double, _i32],
+    "ccr_dma_rate": [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)],
     "ccr_sendrecv_slot_log": [_vp, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_stream_wait": [_vp, _vp, _i32],
     "ccr_dma_hold_finish": [_vp, _i32],
@@ -164,6 +167,7 @@ class Config:
     dma_sync: str = "host_func"      # "host_func" | "stream_flags"
     dma_engines: int = 0             # SDMA engines one call may use; 0 = all
     graph_cache: bool = True         # replay small kernel-only ring calls from captured graphs
+    dma_deadline_us: int = 0         # SDMA: time a call's copies may take; > 0 paces the engines
 
     def to_c(self) -> ccr_config_t:
         return ccr_config_t(CCR_COPY_SDMA if self.copy_mode == "sdma" else CCR_COPY_KERNEL,
@@ -172,7 +176,7 @@ class Config:
                             CCR_BF16_ACC_FP32_PARTIALS if self.bf16_acc == "fp32_partials"
                             else CCR_BF16_ACC_PER_HOP, self.dma_stripe, self.dma_chunk_bytes,
                             1 if self.dma_sync == "stream_flags" else 0, self.dma_engines,
-                            int(self.graph_cache))
+                            int(self.graph_cache), self.dma_deadline_us)
 
     @staticmethod
     def from_c(c: ccr_config_t) -> "Config":
@@ -181,7 +185,7 @@ class Config:
                       "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop",
                       c.dma_stripe, c.dma_chunk_bytes,
                       "stream_flags" if c.dma_sync == 1 else "host_func", c.dma_engines,
-                      bool(c.graph_cache))
+                      bool(c.graph_cache), c.dma_deadline_us)
 
 
 def ccr_config_default() -> Config:
@@ -470,6 +474,18 @@ def ccr_dma_info(ctx: Context) -> list:
     ids = (ctypes.c_int32 * 16)()
     _check(_lib.ccr_dma_info(ctx.handle, ctypes.byref(n), ids))
     return list(ids[:n.value])
+
+
+def ccr_dma_pace(nbytes: int, deadline_us: int, engine_gbs: float, max_engines: int) -> int:
+    """Fewest SDMA engines that move nbytes within deadline_us at engine_gbs each (host only)."""
+    return int(_lib.ccr_dma_pace(nbytes, deadline_us, engine_gbs, max_engines))
+
+
+def ccr_dma_rate(ctx: Context) -> tuple:
+    """(one engine's measured copy rate in GB/s, engines the last SDMA job was allowed)."""
+    g, e = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.ccr_dma_rate(ctx.handle, ctypes.byref(g), ctypes.byref(e)))
+    return g.value, e.value
 
 
 def ccr_sendrecv_slot_log(ctx: Context) -> np.ndarray:

@@ -21,6 +21,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -101,6 +102,7 @@ struct ccr_ctx {
   hipStream_t s_a = nullptr;    // reduce / fill / exchange side stream
   hipStream_t s_b = nullptr;    // all-gather (overlap, SDMA handshake) / drain side stream
   std::unique_ptr<DmaProxy> dma;  // SDMA engines + CPU proxy, started on first SDMA use
+  int last_dma_engines = 0;     // engines the most recent SDMA job was allowed
   std::vector<hipEvent_t> ev;   // event pool, grown on demand
   char* staging = nullptr;      // staging_slots x staging_chunk_bytes
   int64_t staging_bytes = 0;
@@ -177,6 +179,8 @@ ccr_status_t check_config(const ccr_config_t* c) {
     return fail(CCR_ERR_INVALID_ARG, "dma_engines %d outside [0, 16]", c->dma_engines);
   if (c->graph_cache != 0 && c->graph_cache != 1)
     return fail(CCR_ERR_INVALID_ARG, "graph_cache %d is not 0 or 1", c->graph_cache);
+  if (c->dma_deadline_us < 0)
+    return fail(CCR_ERR_INVALID_ARG, "dma_deadline_us %d is negative", c->dma_deadline_us);
   return CCR_OK;
 }
 
@@ -442,10 +446,16 @@ ccr_status_t ensure_dma(ccr_ctx* ctx) {
   return CCR_OK;
 }
 
-// Engines one call may use: the configured number, at most the usable ones.
-int dma_engine_limit(const ccr_ctx* ctx) {
+// Engines one call that moves `bytes` over SDMA may use: the configured
+// number, at most the usable ones, and with a deadline only as many as
+// that time needs at the proxy's measured per-engine rate.
+int dma_engine_limit(ccr_ctx* ctx, int64_t bytes) {
   const int n = ctx->dma->engine_count();
-  return ctx->cfg.dma_engines > 0 ? std::min(ctx->cfg.dma_engines, n) : n;
+  int e = ctx->cfg.dma_engines > 0 ? std::min(ctx->cfg.dma_engines, n) : n;
+  if (ctx->cfg.dma_deadline_us > 0)
+    e = ccr_dma_pace(bytes, ctx->cfg.dma_deadline_us, ctx->dma->engine_gbs(), e);
+  ctx->last_dma_engines = e;
+  return e;
 }
 
 ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s) {
@@ -824,8 +834,11 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
     }
     if (which != kWhichRS && sdma) {
       CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
-      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, dma_engine_limit(ctx),
-                                        fuse ? 1 : 0),
+      // every all-gather hop copies one chunk per rank: count elements over
+      // the R-1 hops (R-2 when the last reduce hop forwarded), all slices
+      const int64_t call_bytes = (int64_t)(R - 1 - (fuse ? 1 : 0)) * count * esize;
+      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize,
+                                        dma_engine_limit(ctx, call_bytes), fuse ? 1 : 0),
                          ag));
     } else if (which != kWhichRS) {
       if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
@@ -878,7 +891,7 @@ ccr_status_t run_alltoall(ccr_ctx* ctx, const void* const* send, void* const* re
   CCR_TRY(ensure_dma(ctx));
   int64_t total = 0;
   for (const Piece& x : p) total += x.nbytes;
-  const int E = dma_engine_limit(ctx);
+  const int E = dma_engine_limit(ctx, total);
   int64_t C = ctx->cfg.dma_chunk_bytes > 0 ? ctx->cfg.dma_chunk_bytes : auto_chunk(total, E);
   // at most ~64 Ki chunks per job, whatever chunk size was asked for
   C = std::max(C, (ceil_div(total, int64_t(1) << 16) + 15) & ~int64_t(15));
@@ -928,6 +941,7 @@ ccr_status_t ccr_config_default(ccr_config_t* cfg) {
   cfg->dma_chunk_bytes = env_int("CCR_DMA_CHUNK", cfg->dma_chunk_bytes);
   cfg->dma_engines = (int32_t)env_int("CCR_DMA_ENGINES", 0);
   cfg->graph_cache = (int32_t)env_int("CCR_GRAPH_CACHE", 1);
+  cfg->dma_deadline_us = (int32_t)env_int("CCR_DMA_DEADLINE_US", 0);
   return check_config(cfg);
 }
 
@@ -1123,7 +1137,7 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     plan.chunk = ctx->cfg.staging_chunk_bytes;
     plan.slots = ctx->cfg.staging_slots;
     plan.slot_mem = ctx->staging;
-    plan.engines = dma_engine_limit(ctx);
+    plan.engines = dma_engine_limit(ctx, 2 * (int64_t)n * nbytes);  // a fill and a drain per byte
     plan.stripe = ctx->cfg.dma_stripe > 0 ? ctx->cfg.dma_stripe : std::max(1, plan.engines / 2);
     std::string err;
     if (!ctx->dma->submit_staged(plan, caller, (DmaSync)ctx->cfg.dma_sync, &err))
@@ -1646,6 +1660,23 @@ ccr_status_t ccr_graph_cache_stats(ccr_ctx_t ctx, int64_t* graphs, int64_t* repl
   for (const auto& g : ctx->graphs) n += g.exec != nullptr;
   if (graphs) *graphs = n;
   if (replays) *replays = ctx->graph_replays;
+  return CCR_OK;
+}
+
+int32_t ccr_dma_pace(int64_t bytes, int64_t deadline_us, double engine_gbs, int32_t max_engines) {
+  if (max_engines < 1) return 0;
+  if (deadline_us <= 0 || !(engine_gbs > 0) || bytes <= 0) return max_engines;
+  const double per_engine = (double)deadline_us * 1e-6 * engine_gbs * 1e9;  // bytes in the deadline
+  const double need = std::ceil((double)bytes / per_engine);
+  return need >= (double)max_engines ? max_engines : std::max<int32_t>(1, (int32_t)need);
+}
+
+ccr_status_t ccr_dma_rate(ccr_ctx_t ctx, double* engine_gbs, int32_t* last_engines) {
+  CCR_TRY(check_ctx(ctx));
+  if (!engine_gbs || !last_engines) return fail(CCR_ERR_INVALID_ARG, "engine_gbs or last_engines is NULL");
+  CCR_TRY(ensure_dma(ctx));
+  *engine_gbs = ctx->dma->engine_gbs();
+  *last_engines = ctx->last_dma_engines;
   return CCR_OK;
 }
 

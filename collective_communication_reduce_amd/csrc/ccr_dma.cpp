@@ -191,6 +191,7 @@ bool DmaProxy::start(int device, std::string* err) {
     *err = "no usable SDMA engine for device-to-device copies";
     return false;
   }
+  measure_engine_rate();
 
   if (hipHostMalloc(reinterpret_cast<void**>(&flags_), sizeof(uint32_t) * kFlagStride * 2 * kFlags,
                     hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
@@ -203,6 +204,43 @@ bool DmaProxy::start(int device, std::string* err) {
   thread_ = std::thread(&DmaProxy::loop, this);
   started_ = true;
   return true;
+}
+
+// One engine's device-to-device rate, for pacing calls by a deadline: a
+// 16 MiB copy on the first usable engine (already warm), nothing else
+// running.  Left at 0 (no pacing) if the copy cannot be made or timed.
+void DmaProxy::measure_engine_rate() {
+  constexpr int64_t kBytes = int64_t(16) << 20;
+  char* buf = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&buf), (size_t)(2 * kBytes)) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  (void)hipMemset(buf, 0, (size_t)(2 * kBytes));
+  (void)hipDeviceSynchronize();
+  hsa_signal_t sg;
+  if (hsa_signal_create(1, 0, nullptr, &sg) != HSA_STATUS_SUCCESS) {
+    (void)hipFree(buf);
+    return;
+  }
+  const auto t = clk::now();
+  bool ok = hsa_amd_memory_async_copy_on_engine(buf + kBytes, agent_, buf, agent_, (size_t)kBytes, 0,
+                                                nullptr, sg,
+                                                (hsa_amd_sdma_engine_id_t)(1u << engines_[0]),
+                                                true) == HSA_STATUS_SUCCESS;
+  bool stuck = false;
+  while (ok && hsa_signal_load_scacquire(sg) > 0) {
+    if (seconds_since(t) > 20.0) {
+      stuck = ok = false;
+      break;
+    }
+  }
+  const double s = seconds_since(t);
+  if (ok && s > 0) engine_gbs_ = (double)kBytes / s * 1e-9;
+  if (!stuck) {  // else the engine may still write the buffer
+    hsa_signal_destroy(sg);
+    (void)hipFree(buf);
+  }
 }
 
 bool DmaProxy::take_flag(int* f, std::string* err) {

@@ -94,6 +94,9 @@ class DmaProxy {
   bool start(int device, std::string* err);
   int engine_count() const { return (int)engines_.size(); }
   int engine_id(int i) const { return engines_[(size_t)i]; }
+  // One engine's device-to-device copy rate measured at start (GB/s; 0 if
+  // it could not be measured).
+  double engine_gbs() const { return engine_gbs_; }
 
   // Enqueue on `stream` the handshake around a job and hand the job to the
   // proxy.  Returns false (with *err) if no flag pair frees up in time.
@@ -129,9 +132,11 @@ class DmaProxy {
   hsa_signal_t get_signal();
   void put_signal(hsa_signal_t s);
   void note_error(const std::string& e);
+  void measure_engine_rate();
 
   hsa_agent_t agent_{};
   std::vector<int> engines_;  // HSA SDMA engine indices (bit positions)
+  double engine_gbs_ = 0;     // one engine's measured copy rate
   uint32_t* flags_ = nullptr;  // pinned host: start flag of pair f at word 2f*stride, finish at (2f+1)*stride
   std::vector<int> free_flags_;
   std::list<Job*> active_;    // owned by the proxy thread

@@ -150,6 +150,15 @@ typedef struct {
                                     ccr_ctx_set_config and ccr_ctx_destroy
                                     synchronise the device before destroying
                                     graphs.  See ccr_graph_cache_stats.        */
+    int32_t dma_deadline_us;     /* SDMA: time one call's copies may take, in us;
+                                    > 0: the call uses the fewest engines whose
+                                    measured rate moves its copy bytes within
+                                    that time (ccr_dma_pace; never more than
+                                    dma_engines when that is set).  The rate is
+                                    the engines' rate with nothing else running,
+                                    so under concurrent load the copies can take
+                                    longer.  0 (default): dma_engines alone
+                                    decides                                    */
 } ccr_config_t;
 
 typedef struct ccr_ctx *ccr_ctx_t;
@@ -390,6 +399,24 @@ ccr_status_t ccr_sendrecv_slot_log(ccr_ctx_t ctx, int32_t *out, int64_t max_even
  * Returns CCR_ERR_TIMEOUT if it has not (the work keeps running), or
  * CCR_ERR_HIP with the proxy's message if the DMA proxy reported an error. */
 ccr_status_t ccr_stream_wait(ccr_ctx_t ctx, void *stream, int timeout_ms);
+
+/* SDMA pacing from a time budget (host only, touches no device): the
+ * fewest engines whose combined rate moves `bytes` within `deadline_us`,
+ * ceil(bytes / (deadline_us * 1e-6 * engine_gbs * 1e9)), at least 1 and at
+ * most max_engines.  Returns max_engines when deadline_us <= 0,
+ * engine_gbs <= 0 or bytes <= 0 would leave nothing to pace, and 0 when
+ * max_engines < 1.  HOCCL §3.3.1 spreads a transfer over several queues to
+ * raise its rate; this picks how many from the time it may take, so that
+ * copies that are not waited on keep their HBM traffic beside concurrent
+ * compute low. */
+int32_t ccr_dma_pace(int64_t bytes, int64_t deadline_us, double engine_gbs, int32_t max_engines);
+
+/* The context's SDMA pacing figures.  *engine_gbs: one engine's
+ * device-to-device copy rate in GB/s, measured when the DMA proxy starts (a
+ * 16 MiB copy on the first usable engine, nothing else running).
+ * *last_engines: the engines the context's most recent SDMA job was allowed
+ * (0 before any).  Starts the DMA proxy if it is not running. */
+ccr_status_t ccr_dma_rate(ccr_ctx_t ctx, double *engine_gbs, int32_t *last_engines);
 
 /* Fault injection for watchdog tests: the DMA proxy holds every
  * operation's finish flag for `us` microseconds after its copies complete

@@ -34,10 +34,11 @@ def test_library_exports_every_declared_symbol():
 def test_config_defaults_and_environment(monkeypatch):
     for k in ("CCR_COPY_MODE", "CCR_CU_BUDGET", "CCR_SLICES", "CCR_OVERLAP",
               "CCR_STAGING_CHUNK", "CCR_STAGING_SLOTS", "CCR_BF16_ACC", "CCR_DMA_STRIPE",
-              "CCR_DMA_CHUNK", "CCR_DMA_SYNC", "CCR_DMA_ENGINES", "CCR_GRAPH_CACHE"):
+              "CCR_DMA_CHUNK", "CCR_DMA_SYNC", "CCR_DMA_ENGINES", "CCR_GRAPH_CACHE",
+              "CCR_DMA_DEADLINE_US"):
         monkeypatch.delenv(k, raising=False)
     c = ccr.ccr_config_default()
-    assert c == ccr.Config("kernel", 0, 1, False, 4 << 20, 2, "per_hop", 0, 0, "host_func", 0, True)
+    assert c == ccr.Config("kernel", 0, 1, False, 4 << 20, 2, "per_hop", 0, 0, "host_func", 0, True, 0)
     monkeypatch.setenv("CCR_COPY_MODE", "sdma")
     monkeypatch.setenv("CCR_CU_BUDGET", "32")
     monkeypatch.setenv("CCR_SLICES", "4")
@@ -50,8 +51,14 @@ def test_config_defaults_and_environment(monkeypatch):
     monkeypatch.setenv("CCR_DMA_SYNC", "stream_flags")
     monkeypatch.setenv("CCR_DMA_ENGINES", "4")
     monkeypatch.setenv("CCR_GRAPH_CACHE", "0")
+    monkeypatch.setenv("CCR_DMA_DEADLINE_US", "2500")
     assert ccr.ccr_config_default() == ccr.Config("sdma", 32, 4, True, 1 << 20, 3, "fp32_partials", 4,
-                                                  1 << 21, "stream_flags", 4, False)
+                                                  1 << 21, "stream_flags", 4, False, 2500)
+    monkeypatch.setenv("CCR_DMA_DEADLINE_US", "-1")
+    with pytest.raises(ccr.CcrError):
+        ccr.ccr_config_default()
+    assert "dma_deadline_us" in ccr.ccr_last_error()
+    monkeypatch.setenv("CCR_DMA_DEADLINE_US", "0")
     monkeypatch.setenv("CCR_GRAPH_CACHE", "2")
     with pytest.raises(ccr.CcrError):
         ccr.ccr_config_default()
@@ -128,3 +135,22 @@ def test_null_arguments_are_rejected_without_a_device():
     assert lib.ccr_ctx_create(0, None, None) == ccr.CCR_ERR_INVALID_ARG
     assert lib.ccr_ctx_destroy(None) == ccr.CCR_OK
     assert lib.ccr_config_default(None) == ccr.CCR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("nbytes,deadline_us,gbs,max_e", [
+    (314_572_800, 2950, 60.0, 14), (314_572_800, 1, 60.0, 14), (314_572_800, 10**7, 60.0, 14),
+    (1, 1, 60.0, 3), (268_435_456, 700, 55.5, 4), (60_000, 1, 60.0, 16), (60_001, 1, 60.0, 16),
+    (120_000, 1, 60.0, 16), (10**12, 1000, 0.5, 16)])
+def test_dma_pace_is_the_fewest_engines_that_meet_the_deadline(nbytes, deadline_us, gbs, max_e):
+    """The pick equals a brute-force search: the smallest E in 1..max_e with
+    E engines x gbs x deadline >= bytes (exact integer arithmetic on the
+    per-engine byte budget), else max_e."""
+    got = ccr.ccr_dma_pace(nbytes, deadline_us, gbs, max_e)
+    per_engine = deadline_us * 1e-6 * gbs * 1e9
+    want = next((e for e in range(1, max_e + 1) if e * per_engine >= nbytes), max_e)
+    assert got == want
+    # no deadline, no rate, nothing to move, or no engines: nothing to pace
+    assert ccr.ccr_dma_pace(nbytes, 0, gbs, max_e) == max_e
+    assert ccr.ccr_dma_pace(nbytes, deadline_us, 0.0, max_e) == max_e
+    assert ccr.ccr_dma_pace(0, deadline_us, gbs, max_e) == max_e
+    assert ccr.ccr_dma_pace(nbytes, deadline_us, gbs, 0) == 0

@@ -86,3 +86,12 @@ def test_contention_rate_matches_a_direct_integral():
     assert bench.contention_rate([(0.0, 5.0, 256), (1.0, 2.0, 64)], 5.0, 256) == pytest.approx(1.0)
     # half the CUs for half the window
     assert bench.contention_rate([(2.5, 9.0, 128)], 5.0, 256) == pytest.approx(0.25)
+
+
+def test_slowdown_summary_names_every_full_cu_run_apart():
+    runs = [{"copy_mode": "kernel", "dma_engines": None},
+            {"copy_mode": "sdma", "dma_engines": "all"},
+            {"copy_mode": "sdma", "dma_engines": 2},
+            {"copy_mode": "sdma", "dma_engines": "all", "dma_deadline": {"deadline_us": 2900}}]
+    keys = [bench.slowdown_key(r) for r in runs]
+    assert keys == ["kernel", "sdma", "sdma_2_engines", "sdma_deadline"]

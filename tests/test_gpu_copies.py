@@ -115,6 +115,58 @@ def test_dma_engines_available(ccr_mod):
     assert len(ids) >= 1 and len(set(ids)) == len(ids) and all(0 <= i < 16 for i in ids)
 
 
+def test_dma_deadline_paces_every_sdma_call(ccr_mod):
+    """With a deadline, each SDMA call is allowed ccr_dma_pace(its copy
+    bytes, deadline, the measured engine rate, all engines) engines, and the
+    results stay those of the oracle, bit for bit."""
+    import torch
+    say("dma deadline pacing")
+    R, n = 8, (1 << 18) + 40
+    xs = workloads.random_buffers(R, n, "bf16", seed=91, dist="normal", scale=1.0)
+    ref = oracle.ring_allreduce(xs, S=1)
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 200, (R, R))
+    row = 4096
+    sends = [rng.integers(0, 256, int(counts[r].sum()) * row, dtype=np.uint8) for r in range(R)]
+    a2a_ref = oracle.alltoall(sends, counts, row)
+    mbs = [rng.integers(0, 256, 3 << 20, dtype=np.uint8) for _ in range(2)]
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma")) as c:
+        gbs, last = ccr_mod.ccr_dma_rate(c)
+        assert last == 0 and 1.0 < gbs < 1000.0, gbs
+        E = len(ccr_mod.ccr_dma_info(c))
+        seen = set()
+        for deadline in (1, 100, 2000, 10 ** 7, 0):
+            c.set_config(ccr_mod.Config(copy_mode="sdma", dma_deadline_us=deadline))
+            assert ccr_mod.ccr_dma_rate(c)[0] == gbs  # measured once, at proxy start
+            # all-reduce: the all-gather's R-2 hops (the last reduce hop forwards)
+            ts = [to_dev(x) for x in xs]
+            ccr_mod.ccr_allreduce(c, ts)
+            torch.cuda.synchronize()
+            want = ccr_mod.ccr_dma_pace((R - 2) * n * 2, deadline, gbs, E)
+            assert ccr_mod.ccr_dma_rate(c)[1] == want
+            seen.add(want)
+            for t, r in zip(ts, ref):
+                assert to_host(t).tobytes() == r.tobytes()
+            # all-to-all: every segment once
+            sd = [raw_to_dev(x) for x in sends]
+            rv = [torch.zeros(x.size, dtype=torch.uint8, device="cuda") for x in a2a_ref]
+            ccr_mod.ccr_alltoall(c, sd, rv, counts, row)
+            torch.cuda.synchronize()
+            assert ccr_mod.ccr_dma_rate(c)[1] == ccr_mod.ccr_dma_pace(int(counts.sum()) * row,
+                                                                      deadline, gbs, E)
+            for a, b in zip(rv, a2a_ref):
+                assert to_host(a).tobytes() == b.tobytes()
+            # staged send/recv: a fill and a drain per byte
+            s = [raw_to_dev(x) for x in mbs]
+            r = [torch.zeros_like(x) for x in s]
+            ccr_mod.ccr_sendrecv(c, s, r)
+            torch.cuda.synchronize()
+            assert ccr_mod.ccr_dma_rate(c)[1] == ccr_mod.ccr_dma_pace(2 * 2 * (3 << 20), deadline, gbs, E)
+            for a, b in zip(r, mbs):
+                assert to_host(a).tobytes() == b.tobytes()
+        assert E in seen and (E == 1 or 1 in seen)  # both ends of the range were taken
+
+
 @pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
 @pytest.mark.parametrize("m,nbytes,chunk,slots,stripe,engines",
                          [(4, 1 << 20, 1 << 18, 2, 0, 0), (3, 100000 // 16 * 16, 16384, 3, 2, 0),
