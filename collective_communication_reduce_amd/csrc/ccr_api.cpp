@@ -458,9 +458,10 @@ int dma_engine_limit(ccr_ctx* ctx, int64_t bytes) {
   return e;
 }
 
-ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s) {
+ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s,
+                        int max_engines = 0) {
   std::string err;
-  if (!ctx->dma->submit_copies(std::move(copies), s, (DmaSync)ctx->cfg.dma_sync, &err))
+  if (!ctx->dma->submit_copies(std::move(copies), s, (DmaSync)ctx->cfg.dma_sync, &err, max_engines))
     return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
   return CCR_OK;
 }
@@ -548,18 +549,22 @@ ccr_status_t copy_pieces(ccr_ctx* ctx, const Piece* p, size_t n, hipStream_t s) 
 
 // The all-gather of slice s as DMA copies.  Chunk c's copies form a chain
 // (rank c -> c+1 -> ... -> c-1, one hop each).  Each chain is cut into m
-// sub-chains over equal byte ranges, m = E / gcd(R, E) (fewer if pieces
-// would drop below 256 KiB), so the R*m chains spread evenly over the E
-// engines; chain i runs on engine i mod E.  Hops before first_hop are
-// already done (an all-reduce's last reduce-scatter hop forwards, which is
-// hop 0).  Copies are listed hop by hop;
-// each waits for the previous link of its chain, and the DMA proxy issues it
-// when that link completes.
+// sub-chains over equal byte ranges (fewer if pieces would drop below
+// 256 KiB).  By default (any_engine) m = ceil(E / R), just enough chains to
+// keep the E engines busy, or more where links would exceed 8 MiB (so the
+// last links of a large call leave no engine idle for long), and the DMA
+// proxy issues each link on the
+// least-loaded engine when it becomes ready: every SDMA copy carries a fixed
+// cost of several microseconds on its engine, so fewer, larger links placed
+// where an engine is free beat many small ones on fixed engines.  With fixed
+// placement (CCR_DMA_PLACE=static) m = E / gcd(R, E), so the R*m chains
+// spread evenly, and chain i runs on engine i mod E.  Hops before first_hop
+// are already done (an all-reduce's last reduce-scatter hop forwards, which
+// is hop 0).  Copies are listed hop by hop; each waits for the previous link
+// of its chain, and the DMA proxy issues it when that link completes.
 std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, int s, int V,
-                               int esize, int engines, int first_hop) {
+                               int esize, int engines, int first_hop, bool any_engine) {
   const int E = std::max(1, engines);
-  int m = E / std::gcd(R, E);
-  if (const char* e = getenv("CCR_DMA_SPLIT"); e && atoi(e) > 0) m = atoi(e);
   std::vector<int64_t> lo((size_t)R), hi((size_t)R);
   int64_t widest = 0;
   for (int c = 0; c < R; c++) {
@@ -568,6 +573,10 @@ std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, i
     slice_range(clo, chi, S, V, s, &lo[(size_t)c], &hi[(size_t)c]);
     widest = std::max(widest, (hi[(size_t)c] - lo[(size_t)c]) * esize);
   }
+  constexpr int64_t kMaxLink = int64_t(8) << 20;  // past this a link's fixed cost is ~1% of it
+  int m = any_engine ? std::max<int64_t>((E + R - 1) / R, (widest + kMaxLink - 1) / kMaxLink)
+                     : E / std::gcd(R, E);
+  if (const char* e = getenv("CCR_DMA_SPLIT"); e && atoi(e) > 0) m = atoi(e);
   while (m > 1 && widest / m < (256 << 10)) m--;
   std::vector<DmaCopy> out;
   std::vector<int32_t> prev((size_t)R * m, -1);
@@ -582,7 +591,7 @@ std::vector<DmaCopy> ag_chains(void* const* bufs, int R, int64_t count, int S, i
         const size_t chain = (size_t)c * m + j;
         out.push_back(DmaCopy{static_cast<char*>(bufs[q]) + b0 + a,
                               static_cast<const char*>(bufs[p]) + b0 + a, z - a, prev[chain],
-                              (int32_t)(chain % (size_t)E)});
+                              any_engine ? -1 : (int32_t)(chain % (size_t)E)});
         prev[chain] = (int32_t)(out.size() - 1);
       }
     }
@@ -837,9 +846,11 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
       // every all-gather hop copies one chunk per rank: count elements over
       // the R-1 hops (R-2 when the last reduce hop forwarded), all slices
       const int64_t call_bytes = (int64_t)(R - 1 - (fuse ? 1 : 0)) * count * esize;
-      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize,
-                                        dma_engine_limit(ctx, call_bytes), fuse ? 1 : 0),
-                         ag));
+      const int E = dma_engine_limit(ctx, call_bytes);
+      const char* place = getenv("CCR_DMA_PLACE");
+      const bool any = !(place && strcmp(place, "static") == 0);
+      CCR_TRY(dma_submit(ctx, ag_chains(bufs, R, count, S, s, V, esize, E, fuse ? 1 : 0, any), ag,
+                         E));
     } else if (which != kWhichRS) {
       if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
       for (int k = fuse ? 1 : 0; k + 1 < R; k++) {

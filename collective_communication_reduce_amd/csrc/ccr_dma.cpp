@@ -81,6 +81,8 @@ struct DmaProxy::Job {
   int64_t bytes = 0, ncopies = 0;
   // kCopies
   std::vector<DmaCopy> copies;
+  int max_engines = 0;             // engines a copy with engine -1 may use; 0 = all
+  std::vector<int32_t> eng;        // per copy: the engine it was issued on
   std::vector<hsa_signal_t> sig;   // per copy; handle 0 until issued
   std::vector<int32_t> kid_start;  // copies that wait for copy i: kids[kid_start[i] .. kid_start[i+1])
   std::vector<int32_t> kids;
@@ -191,6 +193,7 @@ bool DmaProxy::start(int device, std::string* err) {
     *err = "no usable SDMA engine for device-to-device copies";
     return false;
   }
+  load_.assign(engines_.size(), 0);
   measure_engine_rate();
 
   if (hipHostMalloc(reinterpret_cast<void**>(&flags_), sizeof(uint32_t) * kFlagStride * 2 * kFlags,
@@ -330,11 +333,12 @@ bool DmaProxy::submit(Job* j, hipStream_t stream, std::string* err) {
 }
 
 bool DmaProxy::submit_copies(std::vector<DmaCopy> copies, hipStream_t stream, DmaSync sync,
-                             std::string* err) {
+                             std::string* err, int max_engines) {
   if (copies.empty()) return true;
   Job* j = new Job();
   j->kind = Job::kCopies;
   j->sync = sync;
+  j->max_engines = max_engines;
   for (const DmaCopy& c : copies) j->bytes += c.bytes;
   j->ncopies = (int64_t)copies.size();
   j->copies = std::move(copies);
@@ -399,16 +403,29 @@ bool DmaProxy::issue(char* dst, const char* src, int64_t bytes, hsa_signal_t don
                                              true) == HSA_STATUS_SUCCESS;
 }
 
+// The allowed engine with the fewest bytes outstanding (the lowest index on
+// a tie).
+int DmaProxy::least_loaded(int max_engines) const {
+  const int n = max_engines > 0 ? std::min(max_engines, (int)engines_.size()) : (int)engines_.size();
+  int best = 0;
+  for (int e = 1; e < n; e++)
+    if (load_[(size_t)e] < load_[(size_t)best]) best = e;
+  return best;
+}
+
 bool DmaProxy::start_copy(Job& j, int32_t i) {
   const DmaCopy& c = j.copies[(size_t)i];
+  const int e = c.engine >= 0 ? c.engine % (int)engines_.size() : least_loaded(j.max_engines);
   hsa_signal_t s = get_signal();
-  if (!issue(c.dst, c.src, c.bytes, s, c.engine)) {
+  if (!issue(c.dst, c.src, c.bytes, s, e)) {
     put_signal(s);
     j.failed = true;
     note_error("an SDMA copy could not be issued");
     return false;
   }
   j.sig[(size_t)i] = s;
+  j.eng[(size_t)i] = e;
+  load_[(size_t)e] += c.bytes;
   j.inflight.push_back(i);
   return true;
 }
@@ -423,6 +440,7 @@ bool DmaProxy::begin(Job& j) {
   if (j.kind == Job::kCopies) {
     const size_t n = j.copies.size();
     j.sig.assign(n, hsa_signal_t{0});
+    j.eng.assign(n, 0);
     j.kid_start.assign(n + 1, 0);
     for (size_t i = 0; i < n; i++) {
       const int32_t a = j.copies[i].after;
@@ -459,6 +477,7 @@ bool DmaProxy::advance(Job& j) {
         continue;
       }
       j.ndone++;
+      load_[(size_t)j.eng[(size_t)i]] -= j.copies[(size_t)i].bytes;
       for (int32_t q = j.kid_start[(size_t)i]; q < j.kid_start[(size_t)i + 1] && !j.failed; q++)
         start_copy(j, j.kids[(size_t)q]);
     }

@@ -47,7 +47,9 @@ namespace ccr {
 
 // One copy of a job.  `after` indexes an earlier copy of the same job that
 // must have finished before this one starts (-1: none); the proxy issues the
-// copy when that one completes.  `engine` indexes the proxy's engine list.
+// copy when that one completes.  `engine` indexes the proxy's engine list;
+// -1 lets the proxy issue the copy, when it is ready, on whichever of the
+// job's engines has the fewest bytes outstanding.
 struct DmaCopy {
   char* dst;
   const char* src;
@@ -100,8 +102,10 @@ class DmaProxy {
 
   // Enqueue on `stream` the handshake around a job and hand the job to the
   // proxy.  Returns false (with *err) if no flag pair frees up in time.
+  // max_engines: the engines (the first of the proxy's list) that copies
+  // with engine -1 may go to; 0 = all.
   bool submit_copies(std::vector<DmaCopy> copies, hipStream_t stream, DmaSync sync,
-                     std::string* err);
+                     std::string* err, int max_engines = 0);
   bool submit_staged(const StagedPlan& plan, hipStream_t stream, DmaSync sync, std::string* err);
 
   // Wait until every submitted job has completed its handshake; false on
@@ -129,6 +133,7 @@ class DmaProxy {
   bool advance(Job& j);
   bool issue(char* dst, const char* src, int64_t bytes, hsa_signal_t done, int engine);
   bool start_copy(Job& j, int32_t i);
+  int least_loaded(int max_engines) const;
   hsa_signal_t get_signal();
   void put_signal(hsa_signal_t s);
   void note_error(const std::string& e);
@@ -136,6 +141,7 @@ class DmaProxy {
 
   hsa_agent_t agent_{};
   std::vector<int> engines_;  // HSA SDMA engine indices (bit positions)
+  std::vector<int64_t> load_;  // per engine: bytes of copy-job copies issued, not yet seen done
   double engine_gbs_ = 0;     // one engine's measured copy rate
   uint32_t* flags_ = nullptr;  // pinned host: start flag of pair f at word 2f*stride, finish at (2f+1)*stride
   std::vector<int> free_flags_;

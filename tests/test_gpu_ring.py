@@ -109,6 +109,26 @@ def test_modes_do_not_change_bits(ccr_mod, ctx, mode, dt):
     ctx.set_config(ccr_mod.Config())
 
 
+@pytest.mark.parametrize("place", ["static", "any"])
+@pytest.mark.parametrize("R,n,engines", [(8, (1 << 20) + 24, 0), (5, 300007, 3), (16, 4096 * 64 + 8, 0)])
+def test_sdma_engine_placement_does_not_change_bits(ccr_mod, ctx, monkeypatch, place, R, n, engines):
+    """All-gather links on fixed engines or on the least-loaded engine when
+    they become ready: the same bits as the oracle either way."""
+    if place == "static":
+        monkeypatch.setenv("CCR_DMA_PLACE", "static")
+    else:
+        monkeypatch.delenv("CCR_DMA_PLACE", raising=False)
+    ctx.set_config(ccr_mod.Config(copy_mode="sdma", dma_engines=engines))
+    xs = workloads.random_buffers(R, n, "bf16", seed=R + n, dist="normal", scale=1.0)
+    say(f"allreduce sdma place={place} R={R} n={n} engines={engines}")
+    got = _run(ccr_mod, ctx, xs)
+    _assert_bitwise(got, oracle.ring_allreduce(xs, S=1), f"sdma placement {place}")
+    ag_in = oracle.ring_reduce_scatter(xs, S=1)
+    got = _run(ccr_mod, ctx, ag_in, "all_gather")
+    _assert_bitwise(got, oracle.ring_all_gather(ag_in, S=1), f"sdma all-gather placement {place}")
+    ctx.set_config(ccr_mod.Config())
+
+
 def test_repeated_calls_on_one_stream(ccr_mod, ctx):
     """Back-to-back collectives on one stream see each other's results."""
     import torch
