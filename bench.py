@@ -234,9 +234,10 @@ def slowdown_key(r):
     return f"sdma_{r['dma_engines']}_engines"
 
 
-def median_ms(fn, reps=10, warm=3, before=None):
-    """Median event time of fn; `before` (untimed) runs ahead of each rep,
-    e.g. a scratch write that evicts the caches."""
+def event_times(fn, reps=20, warm=5, before=None):
+    """Event times (ms) of `reps` calls of fn, each alone, after `warm`
+    untimed calls; `before` (untimed) runs ahead of each timed call, e.g. a
+    scratch write that evicts the caches."""
     import torch
     for _ in range(warm):
         fn()
@@ -251,7 +252,19 @@ def median_ms(fn, reps=10, warm=3, before=None):
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
+    return ts
+
+
+def median_ms(fn, reps=10, warm=3, before=None):
+    """Median event time of fn (see event_times)."""
+    ts = event_times(fn, reps, warm, before)
     return sorted(ts)[len(ts) // 2]
+
+
+def spread(ts):
+    """p10 and p90 of event times, for a workload figure reported as its median."""
+    p = percentiles(ts)
+    return {"p10_ms": p["p10_ms"], "p90_ms": p["p90_ms"], "n": p["n"]}
 
 
 def bf16_modes(ccr, xs):
@@ -389,27 +402,31 @@ def workload_probe(ccr, workloads, name, steps):
 
 def workload_timings(ccr, workloads):
     """The other workloads, for context (each is also a full-size parity
-    test): median time per call and the figures of merit of each."""
+    test): per call, 5 untimed warm-up calls, then 20 calls each timed alone
+    with events; the median, p10 and p90, and the figures of merit."""
     import torch
     out = {}
     for w, how in ((workloads.RING_SMALL_F32, "allreduce"), (workloads.RS_AG_R32_F32, "rs_then_ag")):
         bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
         b, R, N = 4, w.R, w.count
-        cold = None
+        cold = cold_ts = None
         with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
             if how == "allreduce":
-                ms = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 20)
+                ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs))
                 algo = b * N * (3 * (R - 1) + 1 + 2 * (R - 2))
                 if R * N * b <= (128 << 20):  # fits the 256 MB MALL: also time it cold
                     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-                    cold = median_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 20,
-                                     before=lambda: scratch.fill_(1))
+                    cold_ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs),
+                                          before=lambda: scratch.fill_(1))
+                    cold = sorted(cold_ts)[len(cold_ts) // 2]
                     del scratch
             else:
-                ms = median_ms(lambda: (ccr.ccr_reduce_scatter(ctx, bufs),
-                                        ccr.ccr_all_gather(ctx, bufs)), 10)
+                ts = event_times(lambda: (ccr.ccr_reduce_scatter(ctx, bufs),
+                                          ccr.ccr_all_gather(ctx, bufs)))
                 algo = b * N * 5 * (R - 1)
-        out[w.name] = {"ms": round(ms, 4), "cold_ms": None if cold is None else round(cold, 4),
+        ms = sorted(ts)[len(ts) // 2]
+        out[w.name] = {"ms": round(ms, 4), **spread(ts), "cold_ms": None if cold is None else round(cold, 4),
+                       **({"cold": spread(cold_ts)} if cold_ts else {}),
                        "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
                        "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "slices": w.slices}
@@ -424,15 +441,18 @@ def workload_timings(ccr, workloads):
            "exchange_bytes": moved}
     for mode in ("kernel", "sdma"):
         with ccr.Context(0, ccr.Config(copy_mode=mode)) as ctx:
-            d_ms = median_ms(lambda: ccr.ccr_moe_dispatch(ctx, xs, src_tok, ecnt, K, send, recv, exp), 10)
-            c_ms = median_ms(lambda: ccr.ccr_moe_combine(ctx, exp, slot, ecnt, T, K, recv, send, outb), 10)
+            d_ts = event_times(lambda: ccr.ccr_moe_dispatch(ctx, xs, src_tok, ecnt, K, send, recv, exp))
+            c_ts = event_times(lambda: ccr.ccr_moe_combine(ctx, exp, slot, ecnt, T, K, recv, send, outb))
+        d_ms, c_ms = sorted(d_ts)[len(d_ts) // 2], sorted(c_ts)[len(c_ts) // 2]
         # three stages (pack, exchange, unpack), each reading and writing `moved` bytes
         res[mode] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
+                     "dispatch": spread(d_ts), "combine": spread(c_ts),
                      "dispatch_algorithmic_gbs": round(3 * 2 * moved / (d_ms * 1e-3) / 1e9, 1),
                      "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
     with ccr.Context(0) as ctx:
-        d_ms = median_ms(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp), 10)
-        c_ms = median_ms(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb), 10)
+        d_ts = event_times(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp))
+        c_ts = event_times(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb))
+        d_ms, c_ms = sorted(d_ts)[len(d_ts) // 2], sorted(c_ts)[len(c_ts) // 2]
         gbs = {}
         for name, fn in (("dispatch", lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp)),
                          ("combine", lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb))):
@@ -445,11 +465,28 @@ def workload_timings(ccr, workloads):
         ccr.ccr_profile_enable(ctx, False)
     # one gather: every row read once and written once
     res["fused"] = {"dispatch_ms": round(d_ms, 4), "combine_ms": round(c_ms, 4),
+                    "dispatch": spread(d_ts), "combine": spread(c_ts),
                     "dispatch_algorithmic_gbs": round(2 * moved / (d_ms * 1e-3) / 1e9, 1),
                     "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1),
                     "dispatch_gather_kernel": {"gbs": gbs["dispatch"][0], "us": gbs["dispatch"][1]},
                     "combine_gather_kernel": {"gbs": gbs["combine"][0], "us": gbs["combine"][1]}}
     out[m.name] = res
+    # pipeline-parallel activations through the staging slots, each copy mode
+    pw = workloads.PP_STAGING_BF16
+    mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16) for _ in range(pw.microbatches)]
+    outs = [torch.empty_like(x) for x in mbs]
+    payload = sum(x.numel() * x.element_size() for x in mbs)
+    pp = {"payload_bytes": payload, "chunk_bytes": pw.chunk_bytes, "slots": pw.slots}
+    for mode in ("kernel", "sdma"):
+        with ccr.Context(0, ccr.Config(copy_mode=mode, staging_chunk_bytes=pw.chunk_bytes,
+                                       staging_slots=pw.slots)) as ctx:
+            ts = event_times(lambda: ccr.ccr_sendrecv(ctx, mbs, outs))
+        ms = sorted(ts)[len(ts) // 2]
+        # every chunk is copied in (fill) and out (drain): 2 reads + 2 writes per byte
+        pp[mode] = {"ms": round(ms, 4), **spread(ts),
+                    "algbw_gbs": round(payload / (ms * 1e-3) / 1e9, 1),
+                    "algorithmic_gbs": round(4 * payload / (ms * 1e-3) / 1e9, 1)}
+    out[pw.name] = pp
     return out
 
 
