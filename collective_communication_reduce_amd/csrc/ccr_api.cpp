@@ -416,14 +416,16 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
     HIP_TRY(launch_pieces(kind, p, n, tuning(), s));
     return CCR_OK;
   }
-  const bool reduce = kind != HopKind::kCopy;
   const bool fwd = kind == HopKind::kReduceFwdF32 || kind == HopKind::kReduceFwdBf16;
+  const bool reduce = fwd || kind == HopKind::kReduceF32 || kind == HopKind::kReduceBf16;
+  const bool drain_fill = kind == HopKind::kDrainFill;
   hipEvent_t start, stop;
   CCR_TRY(timing_event(ctx, &start));
   CCR_TRY(timing_event(ctx, &stop));
   HIP_TRY(launch_pieces(kind, p, n, tuning(), s, start, stop));
   // algorithmic bytes: reduce reads 2 and writes 1 (forwarding writes 2),
-  // copy reads 1 and writes 1, per byte of payload
+  // copy reads 1 and writes 1, drain-and-fill reads 2 and writes 2, per byte
+  // of payload
   // workgroups: one per kBlock x unroll 16-byte vectors of each piece
   const LaunchTuning tune = tuning();
   const int64_t per_wg = (int64_t)kBlock * std::max(1, tune.unroll) * 16;
@@ -431,7 +433,8 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
   for (int i = 0; i < n; i++) wgs += (p[i].nbytes + per_wg - 1) / per_wg;
   if (tune.grid > 0) wgs = std::min<int64_t>(wgs, tune.grid);
   ctx->timed.push_back(ccr_ctx::Timed{fwd ? kProfReduceFwd : reduce ? kProfReduce : kProfCopyKernel,
-                                      start, stop, payload(p, (size_t)n) * (fwd ? 4 : reduce ? 3 : 2),
+                                      start, stop,
+                                      payload(p, (size_t)n) * (fwd || drain_fill ? 4 : reduce ? 3 : 2),
                                       cus_held(ctx, wgs)});
   return CCR_OK;
 }
@@ -1155,37 +1158,55 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
       return fail(CCR_ERR_HIP, "SDMA proxy: %s", err.c_str());
     return CCR_OK;
   }
-  // Compute-unit copies: rounds of P chunks on one stream.  A round fills
-  // slots 0..P-1 in one launch and drains them in the next; stream order
-  // keeps each slot idle -> filling -> draining -> idle, and a slot is
-  // refilled only after its previous chunk has drained.  Filling and
-  // draining are both compute-unit copies sharing HBM, so running them on
-  // two streams would gain nothing on one GPU -- and a cross-stream wait
-  // costs ~27 us of host time on this runtime.
+  // Compute-unit copies on one stream, in rounds of P chunks (chunk c, over
+  // all transfers in order, uses slot c mod P).  Round r hands slot p's
+  // chunk (r-1)P+p to the receiver and refills the slot with chunk rP+p in
+  // the same launch: each thread reads its part of the slot before it
+  // overwrites it, so every slot still goes idle -> filling -> draining ->
+  // idle and is refilled only after its chunk has drained, with one launch
+  // per round instead of a fill launch and a drain launch.  Bytes of one
+  // chunk that the other does not cover (a short last chunk of a transfer,
+  // or no chunk left to fill) go to a plain copy launch: those byte ranges
+  // are disjoint from the fused ones.  Filling and draining are both
+  // compute-unit copies sharing HBM, so running them on two streams would
+  // gain nothing on one GPU -- and a cross-stream wait costs ~27 us of host
+  // time on this runtime.
   hipStream_t s = ctx->masked ? ctx->s_a : caller;
   CCR_TRY(order_after(ctx, 0, caller, s));
   const int P = ctx->cfg.staging_slots;
   const int64_t C = ctx->cfg.staging_chunk_bytes;
-  std::vector<Piece> fills, drains;
-  auto flush = [&]() -> ccr_status_t {
-    CCR_TRY(copy_pieces(ctx, fills.data(), fills.size(), s));
-    CCR_TRY(copy_pieces(ctx, drains.data(), drains.size(), s));
-    fills.clear();
-    drains.clear();
-    return CCR_OK;
+  const int64_t per = ceil_div(nbytes, C), T = per * n, rounds = ceil_div(T, (int64_t)P);
+  auto chunk_io = [&](int64_t c, const char** src, char** dst, int64_t* len) {
+    const int64_t m = c / per, off = (c % per) * C;
+    *src = static_cast<const char*>(send[m]) + off;
+    *dst = static_cast<char*>(recv[m]) + off;
+    *len = std::min<int64_t>(C, nbytes - off);
   };
-  int64_t chunk = 0;
-  for (int m = 0; m < n; m++) {
-    for (int64_t off = 0; off < nbytes; off += C, chunk++) {
-      const int p = (int)(chunk % P);
-      const int64_t len = std::min<int64_t>(C, nbytes - off);
+  std::vector<Piece> fused, copies;
+  for (int64_t r = 0; r <= rounds; r++) {
+    fused.clear();
+    copies.clear();
+    for (int p = 0; p < P; p++) {
+      const int64_t a = (r - 1) * P + p, b = r * P + p;  // chunk drained, chunk filled
       char* slot = ctx->staging + (int64_t)p * C;
-      fills.push_back(Piece{slot, static_cast<const char*>(send[m]) + off, len});
-      drains.push_back(Piece{static_cast<char*>(recv[m]) + off, slot, len});
-      if (p == P - 1) CCR_TRY(flush());
+      const char* unused_src;
+      char* unused_dst;
+      char* to = nullptr;
+      const char* from = nullptr;
+      int64_t la = 0, lb = 0;
+      if (r >= 1 && a < T) chunk_io(a, &unused_src, &to, &la);
+      if (r < rounds && b < T) chunk_io(b, &from, &unused_dst, &lb);
+      const int64_t both = std::min(la, lb);
+      if (both > 0) fused.push_back(Piece{slot, from, both, to});
+      if (la > both) copies.push_back(Piece{to + both, slot + both, la - both});
+      if (lb > both) copies.push_back(Piece{slot + both, from + both, lb - both});
     }
+    for (size_t i = 0; i < fused.size(); i += kMaxPieces) {
+      const int m = (int)std::min<size_t>(kMaxPieces, fused.size() - i);
+      CCR_TRY(launch_timed(ctx, HopKind::kDrainFill, fused.data() + i, m, s));
+    }
+    CCR_TRY(copy_pieces(ctx, copies.data(), copies.size(), s));
   }
-  if (!fills.empty()) CCR_TRY(flush());
   CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
 }

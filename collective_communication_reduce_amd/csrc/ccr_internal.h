@@ -16,7 +16,8 @@ struct Piece {
   char* dst;
   const char* src;
   int64_t nbytes;
-  char* dst2 = nullptr;  // reduce-and-forward only: second copy of the result
+  char* dst2 = nullptr;  // reduce-and-forward: second copy of the result;
+                         // drain-and-fill: where dst's old contents go
 };
 
 // Up to kMaxPieces pieces go into one launch, passed by value as kernel
@@ -29,13 +30,16 @@ constexpr int kBlock = 256;
 // kReduce*: dst = dst + src.  kReduceFwd*: the same, and the result is also
 // written to dst2 (the last reduce-scatter hop forwarding the reduced chunk
 // to the next rank, which replaces the first all-gather hop).  kCopy:
-// dst = src.
+// dst = src.  kDrainFill: dst2 = dst, then dst = src, element by element in
+// the same thread (a staging slot handing its chunk to the receiver and
+// taking the sender's next chunk in one pass).
 enum class HopKind : int {
   kReduceF32 = 0,
   kReduceBf16 = 1,
   kCopy = 2,
   kReduceFwdF32 = 3,
-  kReduceFwdBf16 = 4
+  kReduceFwdBf16 = 4,
+  kDrainFill = 5
 };
 
 struct LaunchTuning {

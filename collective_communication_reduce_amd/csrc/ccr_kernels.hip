@@ -111,6 +111,11 @@ __device__ __forceinline__ void apply_tail(char* dst, const char* src, char* dst
     const uint16_t r = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
     *d = r;
     if constexpr (forwards<K>()) reinterpret_cast<uint16_t*>(dst2)[unit] = r;
+  } else if constexpr (K == HopKind::kDrainFill) {
+    uint16_t* d = reinterpret_cast<uint16_t*>(dst) + unit;
+    const uint16_t old = *d;
+    reinterpret_cast<uint16_t*>(dst2)[unit] = old;
+    *d = reinterpret_cast<const uint16_t*>(src)[unit];
   } else {
     reinterpret_cast<uint16_t*>(dst)[unit] = reinterpret_cast<const uint16_t*>(src)[unit];
   }
@@ -160,6 +165,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const u32x4 r = apply16<K>(loc[u], in[u]);
+        if constexpr (K == HopKind::kDrainFill) store16<NT>(f16 + v0 + u * kBlock, loc[u]);
         store16<NT>(d16 + v0 + u * kBlock, r);
         if constexpr (forwards<K>()) store16<NT>(f16 + v0 + u * kBlock, r);
       }
@@ -171,6 +177,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
           u32x4 loc = {0, 0, 0, 0};
           if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
           const u32x4 r = apply16<K>(loc, load16<NT>(s16 + v));
+          if constexpr (K == HopKind::kDrainFill) store16<NT>(f16 + v, loc);
           store16<NT>(d16 + v, r);
           if constexpr (forwards<K>()) store16<NT>(f16 + v, r);
         }
@@ -180,8 +187,8 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
     // that would hold vector index nvec (never a whole in-range tile).
     const int tail_units = (int)(nbytes & 15) / tail_unit_bytes<K>();
     if (tail_units > 0 && tile == nvec / (kBlock * U) && (int)threadIdx.x < tail_units)
-      apply_tail<K>(dst + (nvec << 4), src + (nvec << 4), dst2 + (forwards<K>() ? (nvec << 4) : 0),
-                    threadIdx.x);
+      apply_tail<K>(dst + (nvec << 4), src + (nvec << 4),
+                    dst2 + (forwards<K>() || K == HopKind::kDrainFill ? (nvec << 4) : 0), threadIdx.x);
   }
 }
 
@@ -388,6 +395,7 @@ hipError_t launch_pieces_np(HopKind kind, const Piece* pieces, int n, LaunchTuni
       return launch_unroll<HopKind::kReduceFwdF32>(a, unroll, nt, stream, t, g);
     case HopKind::kReduceFwdBf16:
       return launch_unroll<HopKind::kReduceFwdBf16>(a, unroll, nt, stream, t, g);
+    case HopKind::kDrainFill: return launch_unroll<HopKind::kDrainFill>(a, unroll, nt, stream, t, g);
     default: return launch_unroll<HopKind::kCopy>(a, unroll, nt, stream, t, g);
   }
 }

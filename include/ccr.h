@@ -292,8 +292,11 @@ ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void *const *bufs, int R, int64_t cou
  * slot is refilled only after it has drained.  SDMA copies: the DMA proxy
  * runs each slot's state machine, fills and drains on different engines, so
  * they overlap.  Kernel copies: rounds of staging_slots chunks on one
- * stream, one launch filling the round's slots and one draining them (both
- * stages share the compute units and HBM, so there is nothing to overlap).
+ * stream; one launch drains each slot's chunk of the previous round to the
+ * receiver and refills the slot with this round's chunk (each thread reads
+ * its part of the slot before overwriting it), so a transfer of T chunks
+ * takes ceil(T / staging_slots) + 1 launches (both stages share the compute
+ * units and HBM, so running them apart would overlap nothing).
  * Transfers run in order m = 0..n-1.  send/recv: host arrays of n device
  * pointers; the 2n ranges must not overlap.  nbytes must be a multiple of 16.
  * ---------------------------------------------------------------------- */
@@ -450,7 +453,8 @@ ccr_status_t ccr_graph_cache_stats(ccr_ctx_t ctx, int64_t *graphs, int64_t *repl
  * payload), the number of launches since the last
  * enable, the sum of their durations in milliseconds, and their algorithmic
  * bytes (a reduce moves 3 bytes per byte of payload: read local, read
- * incoming, write local; reduce-and-forward 4; a copy 2).  Kernel launches
+ * incoming, write local; reduce-and-forward 4; a copy 2; a staging
+ * drain-and-fill, counted with the copy kernels, 4).  Kernel launches
  * are timed by events attached to the launch itself (hipExtLaunchKernel),
  * SDMA copies by events recorded around them.  Enabling (on = 1) also
  * clears the counters. */
