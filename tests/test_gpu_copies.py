@@ -20,7 +20,9 @@ def ccr_mod():
 
 @pytest.mark.parametrize("mode", ["kernel", "sdma"])
 @pytest.mark.parametrize("nbytes,chunk,slots,m", [(16, 4096, 2, 1), (4096 * 3 + 48, 4096, 2, 3),
-                                                  (1 << 20, 1 << 18, 3, 2), (1 << 16, 1 << 16, 1, 2)])
+                                                  (1 << 20, 1 << 18, 3, 2), (1 << 16, 1 << 16, 1, 2),
+                                                  (4096, 4096, 4, 1), (5 * 4096 + 32, 4096, 4, 3),
+                                                  (4096 + 16, 4096, 3, 5)])
 def test_sendrecv_bytes(ccr_mod, mode, nbytes, chunk, slots, m):
     import torch
     rng = np.random.default_rng(nbytes + m)
