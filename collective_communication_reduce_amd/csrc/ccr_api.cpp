@@ -1176,12 +1176,10 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
   const int P = ctx->cfg.staging_slots;
   const int64_t C = ctx->cfg.staging_chunk_bytes;
   const int64_t per = ceil_div(nbytes, C), T = per * n, rounds = ceil_div(T, (int64_t)P);
-  auto chunk_io = [&](int64_t c, const char** src, char** dst, int64_t* len) {
-    const int64_t m = c / per, off = (c % per) * C;
-    *src = static_cast<const char*>(send[m]) + off;
-    *dst = static_cast<char*>(recv[m]) + off;
-    *len = std::min<int64_t>(C, nbytes - off);
-  };
+  // chunk c: transfer c / per, byte offset (c % per) * C
+  auto chunk_len = [&](int64_t c) { return std::min<int64_t>(C, nbytes - (c % per) * C); };
+  auto chunk_src = [&](int64_t c) { return static_cast<const char*>(send[c / per]) + (c % per) * C; };
+  auto chunk_dst = [&](int64_t c) { return static_cast<char*>(recv[c / per]) + (c % per) * C; };
   std::vector<Piece> fused, copies;
   for (int64_t r = 0; r <= rounds; r++) {
     fused.clear();
@@ -1189,13 +1187,10 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     for (int p = 0; p < P; p++) {
       const int64_t a = (r - 1) * P + p, b = r * P + p;  // chunk drained, chunk filled
       char* slot = ctx->staging + (int64_t)p * C;
-      const char* unused_src;
-      char* unused_dst;
-      char* to = nullptr;
-      const char* from = nullptr;
-      int64_t la = 0, lb = 0;
-      if (r >= 1 && a < T) chunk_io(a, &unused_src, &to, &la);
-      if (r < rounds && b < T) chunk_io(b, &from, &unused_dst, &lb);
+      const bool drain = r >= 1 && a < T, fill = r < rounds && b < T;
+      char* to = drain ? chunk_dst(a) : nullptr;
+      const char* from = fill ? chunk_src(b) : nullptr;
+      const int64_t la = drain ? chunk_len(a) : 0, lb = fill ? chunk_len(b) : 0;
       const int64_t both = std::min(la, lb);
       if (both > 0) fused.push_back(Piece{slot, from, both, to});
       if (la > both) copies.push_back(Piece{to + both, slot + both, la - both});
