@@ -103,6 +103,7 @@ struct ccr_ctx {
   hipStream_t s_b = nullptr;    // all-gather (overlap, SDMA handshake) / drain side stream
   std::unique_ptr<DmaProxy> dma;  // SDMA engines + CPU proxy, started on first SDMA use
   int last_dma_engines = 0;     // engines the most recent SDMA job was allowed
+  int64_t footprint = 0;        // bytes of the buffers the current call touches
   std::vector<hipEvent_t> ev;   // event pool, grown on demand
   char* staging = nullptr;      // staging_slots x staging_chunk_bytes
   int64_t staging_bytes = 0;
@@ -351,12 +352,30 @@ void ring_schedule(int R, int64_t count, int S, int V, int which,
 LaunchTuning tuning() {
   // Overridable for tuning sweeps; defaults chosen by measurement.
   static LaunchTuning t = [] {
-    LaunchTuning x{2, 0, 0};  // 2 x 16 B per operand per thread: best of 1/2/4/8 on gfx950
+    // 2 x 16 B per operand per thread (best of 1/2/4/8 on gfx950); the
+    // non-temporal mode is chosen per call (call_tuning) unless forced
+    LaunchTuning x{2, -1, 0};
     if (const char* e = getenv("CCR_UNROLL")) x.unroll = atoi(e);
     if (const char* e = getenv("CCR_NONTEMPORAL")) x.nontemporal = atoi(e);
     if (const char* e = getenv("CCR_GRID")) x.grid = atoi(e);
     return x;
   }();
+  return t;
+}
+
+// The MI355X's last-level cache (MALL, Infinity Cache) in front of HBM.
+constexpr int64_t kMallBytes = int64_t(256) << 20;
+
+// The launch tuning of one call.  A hop's incoming operand is read once and
+// is dead afterwards.  When the call's buffers cannot stay in the MALL
+// anyway, that load is non-temporal, so it does not displace the result,
+// which the next hop reads (every hop kind of the 400 MiB bucket 5-8%
+// faster).  When they fit, every access is temporal: the buffers stay
+// cached from one call to the next, which a non-temporal load would undo
+// (an 8-rank 4 MiB-per-rank all-reduce ran a third slower with it).
+LaunchTuning call_tuning(const ccr_ctx* ctx) {
+  LaunchTuning t = tuning();
+  if (t.nontemporal < 0) t.nontemporal = ctx->footprint > kMallBytes ? 2 : 0;
   return t;
 }
 
@@ -412,8 +431,9 @@ int64_t payload(const Piece* p, size_t n) {
 // A kernel launch; when profiling, its start/stop events are stamped by the
 // dispatch itself (hipExtLaunchKernelGGL), so they time the kernel alone.
 ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hipStream_t s) {
+  const LaunchTuning tune = call_tuning(ctx);
   if (!ctx->prof_on) {
-    HIP_TRY(launch_pieces(kind, p, n, tuning(), s));
+    HIP_TRY(launch_pieces(kind, p, n, tune, s));
     return CCR_OK;
   }
   const bool fwd = kind == HopKind::kReduceFwdF32 || kind == HopKind::kReduceFwdBf16;
@@ -422,12 +442,11 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
   hipEvent_t start, stop;
   CCR_TRY(timing_event(ctx, &start));
   CCR_TRY(timing_event(ctx, &stop));
-  HIP_TRY(launch_pieces(kind, p, n, tuning(), s, start, stop));
+  HIP_TRY(launch_pieces(kind, p, n, tune, s, start, stop));
   // algorithmic bytes: reduce reads 2 and writes 1 (forwarding writes 2),
   // copy reads 1 and writes 1, drain-and-fill reads 2 and writes 2, per byte
   // of payload
   // workgroups: one per kBlock x unroll 16-byte vectors of each piece
-  const LaunchTuning tune = tuning();
   const int64_t per_wg = (int64_t)kBlock * std::max(1, tune.unroll) * 16;
   int64_t wgs = 0;
   for (int i = 0; i < n; i++) wgs += (p[i].nbytes + per_wg - 1) / per_wg;
@@ -746,6 +765,7 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
                           int which, hipStream_t caller) {
   const int esize = dtype_size(dtype);
   const int V = 16 / esize;
+  ctx->footprint = (int64_t)R * count * esize;
   const HopKind reduce = dtype == CCR_F32 ? HopKind::kReduceF32 : HopKind::kReduceBf16;
   const HopKind reduce_fwd = dtype == CCR_F32 ? HopKind::kReduceFwdF32 : HopKind::kReduceFwdBf16;
   // An all-reduce's last reduce-scatter hop also forwards the reduced chunk
@@ -1135,6 +1155,7 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     ranges.push_back(Range{b, b + (uintptr_t)nbytes, 2 * m + 1});
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
+  ctx->footprint = 2 * (int64_t)n * nbytes + ctx->cfg.staging_chunk_bytes * ctx->cfg.staging_slots;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   CCR_TRY(refuse_capture(caller, "ccr_sendrecv (context staging slots)"));
   CCR_TRY(ensure_staging(ctx));
@@ -1236,6 +1257,8 @@ ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* r
     }
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
+  ctx->footprint = 0;
+  for (int r = 0; r < R; r++) ctx->footprint += (sent[(size_t)r] + got[(size_t)r]) * row_bytes;
   hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
     CCR_TRY(refuse_capture(caller, "ccr_alltoall with SDMA copies"));
@@ -1375,10 +1398,11 @@ void unpack_pieces(const MoeShape& m, const int64_t* h_ecnt, void* const* recv, 
   }
 }
 
-ccr_status_t launch_copies(const std::vector<Piece>& p, hipStream_t s) {
+ccr_status_t launch_copies(const ccr_ctx* ctx, const std::vector<Piece>& p, hipStream_t s) {
+  const LaunchTuning tune = call_tuning(ctx);
   for (size_t i = 0; i < p.size(); i += kMaxPieces) {
     const int n = (int)std::min<size_t>(kMaxPieces, p.size() - i);
-    HIP_TRY(launch_pieces(HopKind::kCopy, p.data() + i, n, tuning(), s));
+    HIP_TRY(launch_pieces(HopKind::kCopy, p.data() + i, n, tune, s));
   }
   return CCR_OK;
 }
@@ -1447,6 +1471,8 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
   add_bufs(&bufs, recv, R, rb.data(), true, true, "recv");
   add_bufs(&bufs, exp, R, rb.data(), true, true, "exp");
   CCR_TRY(check_writes_disjoint(bufs));
+  ctx->footprint = 0;
+  for (const CallBuf& b : bufs) ctx->footprint += (int64_t)(b.hi - b.lo);
   hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
     CCR_TRY(refuse_capture(caller, "ccr_moe_dispatch with SDMA copies"));
@@ -1461,7 +1487,7 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
   // unpack to (local expert, source rank, token)
   std::vector<Piece> p;
   unpack_pieces(m, h_ecnt, recv, exp, false, &p);
-  CCR_TRY(launch_copies(p, s));
+  CCR_TRY(launch_copies(ctx, p, s));
   CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
 }
@@ -1490,6 +1516,8 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   add_bufs(&bufs, send, R, &sb, false, true, "send");
   add_bufs(&bufs, out, R, &sb, false, true, "out");
   CCR_TRY(check_writes_disjoint(bufs));
+  ctx->footprint = 0;
+  for (const CallBuf& b : bufs) ctx->footprint += (int64_t)(b.hi - b.lo);
   hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
     CCR_TRY(refuse_capture(caller, "ccr_moe_combine with SDMA copies"));
@@ -1498,7 +1526,7 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   // inverse unpack: expert-major rows back to source-segment order
   std::vector<Piece> p;
   unpack_pieces(m, h_ecnt, recv, const_cast<void* const*>(exp), true, &p);
-  CCR_TRY(launch_copies(p, s));
+  CCR_TRY(launch_copies(ctx, p, s));
   // reverse exchange: rank d returns to r what it received from r
   std::vector<int64_t> back((size_t)R * R);
   for (int r = 0; r < R; r++)

@@ -44,7 +44,8 @@ enum class HopKind : int {
 
 struct LaunchTuning {
   int unroll;       // 16-byte vectors per thread per pass: 1, 2, 4 or 8
-  int nontemporal;  // 1 = streaming (non-temporal) loads and stores
+  int nontemporal;  // 1 = streaming (non-temporal) loads and stores; 2 = only
+                    // the incoming operand's load non-temporal
   int grid;         // 0 = one workgroup per tile; > 0 = that many workgroups
                     // looping over the tiles
 };

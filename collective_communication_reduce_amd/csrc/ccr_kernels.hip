@@ -132,8 +132,14 @@ constexpr int tail_unit_bytes() {
 // issued before the first add, so 2U vectors per thread are in flight.
 // Workgroup b processes tiles b, b + gridDim.x, ... (one tile when the grid
 // has one workgroup per tile).
-template <HopKind K, int U, bool NT, int NP>
+template <HopKind K, int U, int NTM, int NP>
 __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
+  // NTM: 0 = every access temporal; 1 = every load and store non-temporal;
+  // 2 = only the incoming operand's load non-temporal (it is read once and
+  // is dead afterwards, so it need not displace the result, which the next
+  // hop reads, from the caches)
+  constexpr bool NT = NTM == 1;
+  constexpr bool NTI = NTM != 0;
   const int ntiles = a.tile_start[a.n];
   for (int b = blockIdx.x; b < ntiles; b += gridDim.x) {
     int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
       u32x4 loc[U];
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        in[u] = load16<NT>(s16 + v0 + u * kBlock);
+        in[u] = load16<NTI>(s16 + v0 + u * kBlock);
         if constexpr (K != HopKind::kCopy) loc[u] = load16<NT>(d16 + v0 + u * kBlock);
       }
 #pragma unroll
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
         if (v < nvec) {
           u32x4 loc = {0, 0, 0, 0};
           if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
-          const u32x4 r = apply16<K>(loc, load16<NT>(s16 + v));
+          const u32x4 r = apply16<K>(loc, load16<NTI>(s16 + v));
           if constexpr (K == HopKind::kDrainFill) store16<NT>(f16 + v, loc);
           store16<NT>(d16 + v, r);
           if constexpr (forwards<K>()) store16<NT>(f16 + v, r);
@@ -196,32 +202,36 @@ struct Timing {
   hipEvent_t start, stop;
 };
 
-template <HopKind K, int U, bool NT, int NP>
+template <HopKind K, int U, int NTM, int NP>
 hipError_t launch_one(const PieceArgs<NP>& a, hipStream_t s, Timing t, int grid_cap) {
   int grid = a.tile_start[a.n];
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
   if (t.start && t.stop)
-    hipExtLaunchKernelGGL(pieces_kernel<K, U, NT, NP>, dim3(grid), dim3(kBlock), 0, s, t.start,
+    hipExtLaunchKernelGGL(pieces_kernel<K, U, NTM, NP>, dim3(grid), dim3(kBlock), 0, s, t.start,
                           t.stop, 0, a);
   else
-    pieces_kernel<K, U, NT, NP><<<grid, kBlock, 0, s>>>(a);
+    pieces_kernel<K, U, NTM, NP><<<grid, kBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <HopKind K, int U>
-hipError_t launch_kind(const PieceArgs<kMaxPieces>& a, bool nt, hipStream_t s, Timing t, int g) {
-  return nt ? launch_one<K, U, true>(a, s, t, g) : launch_one<K, U, false>(a, s, t, g);
+hipError_t launch_kind(const PieceArgs<kMaxPieces>& a, int ntm, hipStream_t s, Timing t, int g) {
+  switch (ntm) {
+    case 1: return launch_one<K, U, 1>(a, s, t, g);
+    case 2: return launch_one<K, U, 2>(a, s, t, g);
+    default: return launch_one<K, U, 0>(a, s, t, g);
+  }
 }
 
 // Every tuning variant exists for the full table; the small tables exist for
-// the default variant (2 vectors per operand per thread, temporal loads).
+// 2 vectors per operand per thread with temporal accesses or a non-temporal
+// incoming load.
 template <HopKind K, int NP>
-hipError_t launch_unroll(const PieceArgs<NP>& a, int unroll, bool nt, hipStream_t s, Timing t,
+hipError_t launch_unroll(const PieceArgs<NP>& a, int unroll, int nt, hipStream_t s, Timing t,
                          int g) {
   if constexpr (NP != kMaxPieces) {
     (void)unroll;
-    (void)nt;
-    return launch_one<K, 2, false>(a, s, t, g);
+    return nt == 2 ? launch_one<K, 2, 2>(a, s, t, g) : launch_one<K, 2, 0>(a, s, t, g);
   } else {
     switch (unroll) {
       case 1: return launch_kind<K, 1>(a, nt, s, t, g);
@@ -385,7 +395,7 @@ hipError_t launch_pieces_np(HopKind kind, const Piece* pieces, int n, LaunchTuni
   }
   for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  const bool nt = tune.nontemporal != 0;
+  const int nt = tune.nontemporal == 1 || tune.nontemporal == 2 ? tune.nontemporal : 0;
   const Timing t{start, stop};
   const int g = tune.grid;
   switch (kind) {
@@ -407,7 +417,7 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
   if (n <= 0) return hipSuccess;
   if (n > kMaxPieces) return hipErrorInvalidValue;
   const int unroll = (tune.unroll == 1 || tune.unroll == 2 || tune.unroll == 8) ? tune.unroll : 4;
-  const bool small_ok = unroll == 2 && tune.nontemporal == 0;
+  const bool small_ok = unroll == 2 && tune.nontemporal != 1;
   if (small_ok && n <= 8)
     return launch_pieces_np<8>(kind, pieces, n, tune, unroll, stream, start, stop);
   if (small_ok && n <= 16)

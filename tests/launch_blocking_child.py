@@ -1,7 +1,9 @@
-"""Child process of the launch-blocking invariance test: runs all-reduces
-through the library on inputs from an .npz file and saves the results.
-Started with HIP_LAUNCH_BLOCKING=1 in its environment, which HIP reads when
-it initialises (marshalling only: no reference arithmetic here)."""
+"""Child process of the environment-invariance tests: runs all-reduces and a
+staged send/recv through the library on inputs from an .npz file and saves
+the results.  Started with a variable in its environment that is read once
+per process (HIP_LAUNCH_BLOCKING=1, read when HIP initialises, or a forced
+CCR_NONTEMPORAL mode), so each setting needs a process of its own
+(marshalling only: no reference arithmetic here)."""
 import os
 import sys
 
@@ -29,6 +31,15 @@ def main(src, dst):
         for q, t in enumerate(ts):
             out[f"{name}_{q}"] = to_host(t)
         print(f"child: {name} done", flush=True)
+    # staged send/recv with kernel copies: 3 rounds of 2 slots, ragged end
+    send = [to_dev(x[: x.size // 8 * 8]) for x in xs]  # whole 16-byte vectors
+    recv = [torch.zeros_like(t) for t in send]
+    with ccr.Context(0, ccr.Config(staging_chunk_bytes=64 << 10, staging_slots=2)) as c:
+        ccr.ccr_sendrecv(c, send, recv)
+        torch.cuda.synchronize()
+    for q, t in enumerate(recv):
+        out[f"sendrecv_{q}"] = to_host(t)
+    print("child: sendrecv done", flush=True)
     np.savez(dst, **out)
 
 

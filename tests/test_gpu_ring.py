@@ -210,10 +210,15 @@ def test_profile_intervals(ccr_mod, budget):
     assert abs(np.sum(red[:, 1] - red[:, 0]) - stats["ms"]) < 1e-2
 
 
-def test_launch_blocking_does_not_change_bits(ccr_mod, tmp_path):
-    """HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one) leaves
-    the bits unchanged in every mode.  HIP reads the variable when it
-    initialises, so the case runs in one child process."""
+@pytest.mark.parametrize("env", [{"HIP_LAUNCH_BLOCKING": "1"}, {"CCR_NONTEMPORAL": "0"},
+                                 {"CCR_NONTEMPORAL": "1"}, {"CCR_NONTEMPORAL": "2"}],
+                         ids=lambda e: "-".join(f"{k}={v}" for k, v in e.items()))
+def test_process_settings_do_not_change_bits(ccr_mod, tmp_path, env):
+    """Settings read once per process leave the bits unchanged in every
+    mode: HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one)
+    and each forced non-temporal mode of the streaming kernels (none, every
+    load and store, the incoming load only).  Each case runs in a child
+    process of its own."""
     import os
     import subprocess
     import sys
@@ -221,16 +226,17 @@ def test_launch_blocking_does_not_change_bits(ccr_mod, tmp_path):
     xs = workloads.random_buffers(R, n, "bf16", seed=77, dist="normal", scale=1e-3)
     src, dst = tmp_path / "in.npz", tmp_path / "out.npz"
     np.savez(src, R=R, **{f"x{i}": x for i, x in enumerate(xs)})
-    say(f"launch-blocking child R={R} n={n}")
-    env = dict(os.environ, HIP_LAUNCH_BLOCKING="1")
+    say(f"child process {env} R={R} n={n}")
     child = os.path.join(os.path.dirname(__file__), "launch_blocking_child.py")
-    r = subprocess.run([sys.executable, child, str(src), str(dst)], env=env, timeout=150,
-                       capture_output=True, text=True)
+    r = subprocess.run([sys.executable, child, str(src), str(dst)], env=dict(os.environ, **env),
+                       timeout=150, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     got = np.load(dst)
     ref = oracle.ring_allreduce(xs, S=1)
     for name in ("kernel_s1", "kernel_overlap_s3", "sdma_s2"):
-        _assert_bitwise([got[f"{name}_{q}"] for q in range(R)], ref, f"launch blocking, {name}")
+        _assert_bitwise([got[f"{name}_{q}"] for q in range(R)], ref, f"{env}, {name}")
+    _assert_bitwise([got[f"sendrecv_{q}"] for q in range(R)], [x[: n // 8 * 8] for x in xs],
+                    f"{env}, sendrecv")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
