@@ -1603,15 +1603,21 @@ ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int6
   const MoeRank* d_rk = reinterpret_cast<const MoeRank*>(slot->dev);
   const MoeSeg* d_sg = reinterpret_cast<const MoeSeg*>(slot->dev + sizeof(MoeRank) * (size_t)R);
   const int64_t limit = combine ? rows : m.T;
+  // the combine reads every expert row once (non-temporal when the call's
+  // buffers exceed the MALL); the dispatch reads each token row once per
+  // chosen expert, so its loads stay temporal
+  ctx->footprint = (int64_t)R * ((combine ? rows : m.T) + rows) * m.row_bytes;
+  const bool nt_load = combine && call_tuning(ctx).nontemporal != 0;
   if (ctx->prof_on) {
     hipEvent_t start, stop;
     CCR_TRY(timing_event(ctx, &start));
     CCR_TRY(timing_event(ctx, &stop));
-    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s, start, stop));
+    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, nt_load, s, start,
+                              stop));
     ctx->timed.push_back(ccr_ctx::Timed{kProfGather, start, stop, 2 * R * rows * m.row_bytes,
                                         cus_held(ctx, R * ((rows + 7) / 8))});
   } else {
-    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, s));
+    HIP_TRY(launch_moe_gather(combine, d_rk, d_sg, R, E, rows, limit, m.row_bytes, nt_load, s));
   }
   HIP_TRY(hipEventRecord(slot->done, s));
   CCR_TRY(order_after(ctx, 1, s, caller));

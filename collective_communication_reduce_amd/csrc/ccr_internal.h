@@ -96,9 +96,10 @@ struct MoeSeg {
 // pack position p <- x row idx[p] (idx < T); combine = 1: out row q <- exp
 // row of pack position idx[q] (idx < T * K).  Out-of-range indices skip the
 // row.
+// nt_load: load the rows non-temporally (rows that are read once).
 hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
                              int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
-                             hipStream_t stream, hipEvent_t start = nullptr,
+                             bool nt_load, hipStream_t stream, hipEvent_t start = nullptr,
                              hipEvent_t stop = nullptr);
 hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,
                                int64_t nsrc, int64_t row_bytes, hipStream_t stream);

@@ -273,6 +273,8 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
 // One group of 8 elements: out = in + float(loc).  The loads and the
 // stores are split so that a tile issues all its loads before its first
 // store (the compiler may not move a load above a store that could alias).
+// Temporal loads throughout: a non-temporal load of the incoming partial
+// made the 8-rank bucket's all-reduce in this mode 9% slower.
 template <PartialKind K>
 __device__ __forceinline__ void partial_load(const PartialPiece& pc, int64_t g, u32x4* loc,
                                              f32x4* in) {

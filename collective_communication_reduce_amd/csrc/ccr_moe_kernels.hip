@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows_kernel(u32x4* dst, const 
 // expert whose segment starts at or before it (an empty segment shares its
 // start with the next one, so the search lands on the segment that holds
 // the position).
-template <int RPB>
+template <int RPB, bool NTL>
 __global__ __launch_bounds__(kBlock) void moe_gather_kernel(const MoeRank* ranks,
                                                             const MoeSeg* segs, int E,
                                                             int64_t rows, int64_t idx_limit,
@@ -105,7 +105,10 @@ __global__ __launch_bounds__(kBlock) void moe_gather_kernel(const MoeRank* ranks
     u32x4 v[RPB];
 #pragma unroll
     for (int j = 0; j < RPB; j++)
-      if (from[j]) v[j] = from[j][c];
+      if (from[j]) {
+        if constexpr (NTL) v[j] = __builtin_nontemporal_load(from[j] + c);
+        else v[j] = from[j][c];
+      }
 #pragma unroll
     for (int j = 0; j < RPB; j++)
       if (to[j]) to[j][c] = v[j];
@@ -236,7 +239,7 @@ hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, i
   return hipGetLastError();
 }
 
-template <int RPB>
+template <int RPB, bool NTL>
 hipError_t launch_gather_rpb(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
                              int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -244,18 +247,28 @@ hipError_t launch_gather_rpb(int combine, const MoeRank* ranks, const MoeSeg* se
   const int64_t grid = per_rank * R;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (start && stop)
-    hipExtLaunchKernelGGL(moe_gather_kernel<RPB>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+    hipExtLaunchKernelGGL(moe_gather_kernel<RPB, NTL>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
                           start, stop, 0, ranks, segs, E, rows_per_rank, idx_limit, row_bytes >> 4,
                           per_rank, combine);
   else
-    moe_gather_kernel<RPB><<<(unsigned)grid, kBlock, 0, stream>>>(
+    moe_gather_kernel<RPB, NTL><<<(unsigned)grid, kBlock, 0, stream>>>(
         ranks, segs, E, rows_per_rank, idx_limit, row_bytes >> 4, per_rank, combine);
   return hipGetLastError();
 }
 
+template <int RPB>
+hipError_t launch_gather_nt(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
+                            int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
+                            bool nt_load, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  return nt_load ? launch_gather_rpb<RPB, true>(combine, ranks, segs, R, E, rows_per_rank, idx_limit,
+                                                row_bytes, stream, start, stop)
+                 : launch_gather_rpb<RPB, false>(combine, ranks, segs, R, E, rows_per_rank,
+                                                 idx_limit, row_bytes, stream, start, stop);
+}
+
 hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* segs, int R, int E,
                              int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
-                             hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                             bool nt_load, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (R <= 0 || E <= 0 || rows_per_rank <= 0 || row_bytes <= 0) return hipSuccess;
   // rows per workgroup: overridable for tuning sweeps
   static const int rpb = [] {
@@ -265,14 +278,14 @@ hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* se
   }();
   switch (rpb) {
     case 4:
-      return launch_gather_rpb<4>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
-                                  stream, start, stop);
+      return launch_gather_nt<4>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
+                                 nt_load, stream, start, stop);
     case 16:
-      return launch_gather_rpb<16>(combine, ranks, segs, R, E, rows_per_rank, idx_limit,
-                                   row_bytes, stream, start, stop);
+      return launch_gather_nt<16>(combine, ranks, segs, R, E, rows_per_rank, idx_limit,
+                                  row_bytes, nt_load, stream, start, stop);
     default:
-      return launch_gather_rpb<8>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
-                                  stream, start, stop);
+      return launch_gather_nt<8>(combine, ranks, segs, R, E, rows_per_rank, idx_limit, row_bytes,
+                                 nt_load, stream, start, stop);
   }
 }
 
