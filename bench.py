@@ -863,7 +863,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.bf16_acc == "per_hop" else None,
-                     "kernel": "pieces_kernel<kReduceBf16, 2, false, 8>: one reduce-scatter hop, all 8 ranks"
+                     "kernel": "pieces_kernel<kReduceBf16, 2, 2, 8>: one reduce-scatter hop, all 8 ranks, incoming operand loaded non-temporally"
                                if args.bf16_acc == "per_hop" else
                                "partial_kernel<kFirst/kMid/kLast*, 16>: the reduce-scatter hops with fp32 partials",
                      "launches": red["launches"],
