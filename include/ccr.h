@@ -169,8 +169,12 @@ typedef struct ccr_ctx *ccr_ctx_t;
  * (kernel|sdma), CCR_CU_BUDGET, CCR_SLICES, CCR_OVERLAP, CCR_STAGING_CHUNK,
  * CCR_STAGING_SLOTS, CCR_BF16_ACC (per_hop|fp32_partials), CCR_DMA_STRIPE,
  * CCR_DMA_CHUNK, CCR_DMA_SYNC (host_func|stream_flags), CCR_DMA_ENGINES,
- * CCR_GRAPH_CACHE (0|1).  HOCCL §4 switches backends by an environment variable;
- * this mirrors that. */
+ * CCR_GRAPH_CACHE (0|1), CCR_DMA_DEADLINE_US.  HOCCL §4 switches backends by an
+ * environment variable; this mirrors that.  (Read once per process and not part
+ * of the configuration: CCR_NONTEMPORAL forces the streaming kernels' load mode,
+ * 0 every access temporal, 1 every load and store non-temporal, 2 the incoming
+ * operand's load non-temporal; unset, each call takes 2 when the buffers it
+ * touches exceed the 256 MB last-level cache and 0 otherwise.) */
 ccr_status_t ccr_config_default(ccr_config_t *cfg);
 
 /* Create a context on HIP device `device`.  cfg NULL = ccr_config_default().
