@@ -487,6 +487,33 @@ bool any_engine_placement() {
   return !(place && strcmp(place, "static") == 0);
 }
 
+// Engines for a staged transfer of `chunks` chunks under the context's
+// deadline, once a staged job has shown its fixed cost per chunk step: a
+// transfer takes about chunks x (step cost + chunk / (stripe x rate)), its
+// fills and drains each striped over `stripe` engines of their own (twice
+// that when there are too few engines for both and they share them).  The
+// fewest engines whose time fits, or every allowed one when none does; never
+// fewer than ccr_dma_pace's count for the same bytes.
+int staged_engines(ccr_ctx* ctx, int64_t chunks) {
+  const ccr_config_t& c = ctx->cfg;
+  const int n = ctx->dma->engine_count();
+  const int emax = c.dma_engines > 0 ? std::min(c.dma_engines, n) : n;
+  const double rate = ctx->dma->engine_gbs(), step = ctx->dma->staged_step_us();
+  int e = emax;
+  for (int k = 1; k <= emax && rate > 0; k++) {
+    const int stripe = c.dma_stripe > 0 ? std::min(c.dma_stripe, k) : std::max(1, k / 2);
+    const double share = k >= 2 * stripe ? 1.0 : 2.0;
+    const double t_us =
+        (double)chunks * share * (step + (double)c.staging_chunk_bytes / (stripe * rate * 1e3));
+    if (t_us <= (double)c.dma_deadline_us) {
+      e = k;
+      break;
+    }
+  }
+  ctx->last_dma_engines = e;
+  return e;
+}
+
 ccr_status_t dma_submit(ccr_ctx* ctx, std::vector<DmaCopy> copies, hipStream_t s,
                         int max_engines = 0) {
   std::string err;
@@ -1182,6 +1209,8 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
     plan.slots = ctx->cfg.staging_slots;
     plan.slot_mem = ctx->staging;
     plan.engines = dma_engine_limit(ctx, 2 * (int64_t)n * nbytes);  // a fill and a drain per byte
+    if (ctx->cfg.dma_deadline_us > 0 && ctx->dma->staged_step_us() > 0)
+      plan.engines = staged_engines(ctx, (int64_t)n * ceil_div(nbytes, ctx->cfg.staging_chunk_bytes));
     plan.stripe = ctx->cfg.dma_stripe > 0 ? ctx->cfg.dma_stripe : std::max(1, plan.engines / 2);
     std::string err;
     if (!ctx->dma->submit_staged(plan, caller, (DmaSync)ctx->cfg.dma_sync, &err))

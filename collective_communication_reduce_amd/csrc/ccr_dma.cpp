@@ -209,6 +209,20 @@ bool DmaProxy::start(int device, std::string* err) {
   return true;
 }
 
+// A staged job moves chunk after chunk through its slots; beyond its bytes
+// at the engines' rate, each chunk step costs a fixed time (copy issue and
+// completion, the slot hand-over).  Keep that per-step cost of the last
+// completed job, for pacing staged transfers by a deadline.
+void DmaProxy::note_staged(const Job& j, double elapsed_s) {
+  const StagedPlan& p = j.plan;
+  const int n_eng = p.engines > 0 ? std::min(p.engines, (int)engines_.size()) : (int)engines_.size();
+  const int stripe = std::max(1, std::min(p.stripe, n_eng));
+  if (!(engine_gbs_ > 0) || j.total_chunks <= 0) return;
+  const double step_us = elapsed_s * 1e6 / (double)j.total_chunks;
+  const double copy_us = (double)p.chunk / ((double)stripe * engine_gbs_ * 1e3);
+  staged_step_us_.store(std::max(0.0, step_us - copy_us));
+}
+
 // One engine's device-to-device rate, for pacing calls by a deadline: a
 // 16 MiB copy on the first usable engine (already warm), nothing else
 // running.  Left at 0 (no pacing) if the copy cannot be made or timed.
@@ -592,6 +606,7 @@ void DmaProxy::loop() {
         }
       } else if (j.state == Job::kRunning) {
         if (j.aborted || advance(j)) {
+          if (j.kind == Job::kStaged && !j.aborted && !j.failed) note_staged(j, seconds_since(j.t0));
           if (const int d = finish_delay_us_.load(); d > 0)
             std::this_thread::sleep_for(std::chrono::microseconds(d));
           {

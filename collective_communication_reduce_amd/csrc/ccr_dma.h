@@ -99,6 +99,9 @@ class DmaProxy {
   // One engine's device-to-device copy rate measured at start (GB/s; 0 if
   // it could not be measured).
   double engine_gbs() const { return engine_gbs_; }
+  // Fixed time per chunk step of the last completed staged job, beyond its
+  // bytes at engine_gbs() (microseconds; 0 before any).
+  double staged_step_us() const { return staged_step_us_.load(); }
 
   // Enqueue on `stream` the handshake around a job and hand the job to the
   // proxy.  Returns false (with *err) if no flag pair frees up in time.
@@ -138,11 +141,13 @@ class DmaProxy {
   void put_signal(hsa_signal_t s);
   void note_error(const std::string& e);
   void measure_engine_rate();
+  void note_staged(const Job& j, double elapsed_s);
 
   hsa_agent_t agent_{};
   std::vector<int> engines_;  // HSA SDMA engine indices (bit positions)
   std::vector<int64_t> load_;  // per engine: bytes of copy-job copies issued, not yet seen done
   double engine_gbs_ = 0;     // one engine's measured copy rate
+  std::atomic<double> staged_step_us_{0};  // written by the proxy thread
   uint32_t* flags_ = nullptr;  // pinned host: start flag of pair f at word 2f*stride, finish at (2f+1)*stride
   std::vector<int> free_flags_;
   std::list<Job*> active_;    // owned by the proxy thread

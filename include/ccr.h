@@ -154,7 +154,12 @@ typedef struct {
                                     > 0: the call uses the fewest engines whose
                                     measured rate moves its copy bytes within
                                     that time (ccr_dma_pace; never more than
-                                    dma_engines when that is set).  The rate is
+                                    dma_engines when that is set).  A staged
+                                    ccr_sendrecv, once the context has completed
+                                    one, uses the fewest engines for which
+                                    chunks x (measured cost per chunk step +
+                                    chunk / (stripe x rate)) fits, or all
+                                    allowed engines when none does.  The rate is
                                     the engines' rate with nothing else running,
                                     so under concurrent load the copies can take
                                     longer.  0 (default): dma_engines alone
