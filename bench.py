@@ -385,7 +385,7 @@ def workload_probe(ccr, workloads, name, steps):
         cfg = ccr.Config(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
         with ccr.Context(0, cfg) as ctx:
             for _ in range(steps):
-                ccr.ccr_sendrecv(ctx, mbs, outs)
+                ccr.ccr_sendrecv_batch(ctx, mbs, outs)
             torch.cuda.synchronize()
     else:
         m = workloads.MOE_DISPATCH_BF16
@@ -480,7 +480,7 @@ def workload_timings(ccr, workloads):
     for mode in ("kernel", "sdma"):
         with ccr.Context(0, ccr.Config(copy_mode=mode, staging_chunk_bytes=pw.chunk_bytes,
                                        staging_slots=pw.slots)) as ctx:
-            ts = event_times(lambda: ccr.ccr_sendrecv(ctx, mbs, outs))
+            ts = event_times(lambda: ccr.ccr_sendrecv_batch(ctx, mbs, outs))
         ms = sorted(ts)[len(ts) // 2]
         # every chunk is copied in (fill) and out (drain): 2 reads + 2 writes per byte
         pp[mode] = {"ms": round(ms, 4), **spread(ts),
@@ -629,10 +629,10 @@ def copy_roofline(ccr, nbytes=1 << 30, reps=5):
     a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     with ccr.Context(0) as ctx:
-        ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+        ccr.ccr_alltoall_rows(ctx, [a], [b], [[nbytes // 16]], 16)
         ccr.ccr_profile_enable(ctx, True)
         for _ in range(reps):
-            ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+            ccr.ccr_alltoall_rows(ctx, [a], [b], [[nbytes // 16]], 16)
         st = ccr.ccr_profile_read(ctx, "copy_kernel")
         ccr.ccr_profile_enable(ctx, False)
     del a, b
@@ -647,7 +647,7 @@ def copy_probe(ccr, nbytes, reps):
     b = torch.empty_like(a)
     with ccr.Context(0) as ctx:
         for _ in range(reps):
-            ccr.ccr_alltoall(ctx, [a], [b], [[nbytes // 16]], 16)
+            ccr.ccr_alltoall_rows(ctx, [a], [b], [[nbytes // 16]], 16)
         torch.cuda.synchronize()
     assert torch.equal(a, b)
     log(f"copy probe: {reps} x {nbytes} bytes")
@@ -807,7 +807,7 @@ def main():
         outs = [torch.empty_like(x) for x in mbs]
         stg = dict(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
         pp = guarded("pp_staging_gemm_slowdown", lambda: overlap_runs(
-            ccr, lambda ctx, st: ccr.ccr_sendrecv(ctx, mbs, outs, stream=st),
+            ccr, lambda ctx, st: ccr.ccr_sendrecv_batch(ctx, mbs, outs, stream=st),
             [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
              dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2),
              dict(stg, copy_mode="sdma", dma_deadline_us="window")],
@@ -824,9 +824,9 @@ def main():
                     ccr.ccr_allreduce(c2, bufs)
                     out[f"allreduce_{m}"] = host_call_us(ccr, lambda: ccr.ccr_allreduce(c2, bufs), 20)
                 with ccr.Context(0, ccr.Config(**dict(stg, copy_mode=m))) as c2:
-                    ccr.ccr_sendrecv(c2, mbs[:1], outs[:1])
+                    ccr.ccr_sendrecv_batch(c2, mbs[:1], outs[:1])
                     out[f"sendrecv_16MiB_{m}"] = host_call_us(
-                        ccr, lambda: ccr.ccr_sendrecv(c2, mbs[:1], outs[:1]), 20)
+                        ccr, lambda: ccr.ccr_sendrecv_batch(c2, mbs[:1], outs[:1]), 20)
             return out
         launch = guarded("host_us_per_call", host_costs)
 

@@ -73,8 +73,10 @@ _SIGNATURES = {
     "ccr_allreduce": [_vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_reduce_scatter": [_vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_all_gather": [_vp, _vp, _i32, _i64, _i32, _vp],
-    "ccr_sendrecv": [_vp, _vp, _vp, _i32, _i64, _vp],
-    "ccr_alltoall": [_vp, _vp, _vp, _i32, _vp, _i64, _vp],
+    "ccr_sendrecv": [_vp, _vp, _vp, _i32, _i64, _i32, _vp],
+    "ccr_sendrecv_batch": [_vp, _vp, _vp, _i32, _i64, _vp],
+    "ccr_alltoall": [_vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp],
+    "ccr_alltoall_rows": [_vp, _vp, _vp, _i32, _vp, _i64, _vp],
     "ccr_permute_rows": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "ccr_moe_topk": [_vp, _vp, _vp, _i64, _i32, _i32, _vp],
     "ccr_moe_plan": [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp],
@@ -95,6 +97,7 @@ _SIGNATURES = {
     "ccr_stream_wait": [_vp, _vp, _i32],
     "ccr_dma_hold_finish": [_vp, _i32],
     "ccr_graph_cache_stats": [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
+    "ccr_ctx_streams": [_vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)],
 }
 
 
@@ -348,21 +351,49 @@ def ccr_all_gather(ctx: Context, bufs: Sequence, stream=None):
 
 
 def ccr_sendrecv(ctx: Context, send: Sequence, recv: Sequence, stream=None):
+    """Ring shift: recv[(r + 1) % R] <- send[r] for the R = len(send) ranks."""
+    if len(send) != len(recv) or not send:
+        raise ValueError("send and recv need one buffer per rank")
+    ptrs, n, dt = _ring_args(list(send))
+    rp, rn, rdt = _ring_args(list(recv))
+    if rn != n or rdt != dt:
+        raise ValueError("send and recv buffers need the same element count and dtype")
+    _check(_lib.ccr_sendrecv(ctx.handle, ptrs, rp, len(send), n, dt, _stream(stream)))
+
+
+def ccr_sendrecv_batch(ctx: Context, send: Sequence, recv: Sequence, stream=None):
+    """recv[m] <- send[m] for every transfer m, in order."""
     if len(send) != len(recv):
         raise ValueError("send and recv need the same number of transfers")
     nbytes = send[0].numel() * send[0].element_size() if send else 0
     if any(t.numel() * t.element_size() != nbytes for t in list(send) + list(recv)):
         raise ValueError("every transfer moves the same number of bytes")
-    _check(_lib.ccr_sendrecv(ctx.handle, _ptrs(send), _ptrs(recv), len(send), nbytes,
-                             _stream(stream)))
+    _check(_lib.ccr_sendrecv_batch(ctx.handle, _ptrs(send), _ptrs(recv), len(send), nbytes,
+                                   _stream(stream)))
 
 
-def ccr_alltoall(ctx: Context, send: Sequence, recv: Sequence, counts, row_bytes: int,
-                 stream=None):
+def ccr_alltoall(ctx: Context, send: Sequence, recv: Sequence, counts=None, stream=None):
+    """send[r] holds count elements (its segments in destination order);
+    counts[r][d] elements go from r to d, or count / R each when counts is
+    None; recv[d] gets its segments in source order."""
+    R = len(send)
+    if len(recv) != R:
+        raise ValueError("send and recv need one buffer per rank")
+    ptrs, n, dt = _ring_args(list(send))
+    c = None
+    if counts is not None:
+        c = np.ascontiguousarray(counts, dtype=np.int64).reshape(R, R)
+    _check(_lib.ccr_alltoall(ctx.handle, ptrs, _ptrs(recv), R, n,
+                             c.ctypes.data if c is not None else None, dt, _stream(stream)))
+
+
+def ccr_alltoall_rows(ctx: Context, send: Sequence, recv: Sequence, counts, row_bytes: int,
+                      stream=None):
+    """counts[r][d] rows of row_bytes from rank r to rank d."""
     R = len(send)
     counts = np.ascontiguousarray(counts, dtype=np.int64).reshape(R, R)
-    _check(_lib.ccr_alltoall(ctx.handle, _ptrs(send), _ptrs(recv), R, counts.ctypes.data,
-                             row_bytes, _stream(stream)))
+    _check(_lib.ccr_alltoall_rows(ctx.handle, _ptrs(send), _ptrs(recv), R, counts.ctypes.data,
+                                  row_bytes, _stream(stream)))
 
 
 def ccr_permute_rows(ctx: Context, dst, src, idx, stream=None):
@@ -515,3 +546,10 @@ def ccr_graph_cache_stats(ctx: Context) -> tuple:
     g, r = ctypes.c_int64(), ctypes.c_int64()
     _check(_lib.ccr_graph_cache_stats(ctx.handle, ctypes.byref(g), ctypes.byref(r)))
     return g.value, r.value
+
+
+def ccr_ctx_streams(ctx: Context) -> tuple:
+    """(CU-masked side streams, plain streams) the context holds now."""
+    m, p = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.ccr_ctx_streams(ctx.handle, ctypes.byref(m), ctypes.byref(p)))
+    return m.value, p.value

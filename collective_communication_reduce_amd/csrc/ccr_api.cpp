@@ -98,9 +98,15 @@ struct ccr_ctx {
   int device = 0;
   int num_cus = 0;
   ccr_config_t cfg{};
-  bool masked = false;          // s_a / s_b carry a CU mask
+  bool masked = false;          // a CU budget is set: s_a / s_b carry its mask
+  // Side streams, each created with a CU mask (a hardware queue of its own):
+  // s_a when a CU budget is set (created with the context), or on first use
+  // by the CU-id probe; s_b when a call first needs a second stream (an
+  // overlapped or SDMA all-gather of several slices).  s_cap: a plain stream
+  // the graph cache captures on, created on the first capture.
   hipStream_t s_a = nullptr;    // reduce / fill / exchange side stream
-  hipStream_t s_b = nullptr;    // all-gather (overlap, SDMA handshake) / drain side stream
+  hipStream_t s_b = nullptr;    // all-gather (overlap, SDMA handshake) side stream
+  hipStream_t s_cap = nullptr;
   std::unique_ptr<DmaProxy> dma;  // SDMA engines + CPU proxy, started on first SDMA use
   int last_dma_engines = 0;     // engines the most recent SDMA job was allowed
   int64_t footprint = 0;        // bytes of the buffers the current call touches
@@ -195,28 +201,52 @@ std::vector<uint32_t> cu_mask_for_budget(int budget, int num_cus) {
 }
 
 ccr_status_t destroy_streams(ccr_ctx* ctx) {
-  if (ctx->s_a) HIP_TRY(hipStreamSynchronize(ctx->s_a));
-  if (ctx->s_b) HIP_TRY(hipStreamSynchronize(ctx->s_b));
-  if (ctx->s_a) HIP_TRY(hipStreamDestroy(ctx->s_a));
-  if (ctx->s_b) HIP_TRY(hipStreamDestroy(ctx->s_b));
-  ctx->s_a = ctx->s_b = nullptr;
+  for (hipStream_t* p : {&ctx->s_a, &ctx->s_b, &ctx->s_cap})
+    if (*p) HIP_TRY(hipStreamSynchronize(*p));
+  for (hipStream_t* p : {&ctx->s_a, &ctx->s_b, &ctx->s_cap}) {
+    if (*p) HIP_TRY(hipStreamDestroy(*p));
+    *p = nullptr;
+  }
   ctx->masked = false;
   return CCR_OK;
 }
 
-// The side streams are always created with a CU mask (all CUs when there is
-// no budget): a CU-masked stream gets a hardware queue of its own.  Plain
+// A CU-masked side stream: the lowest cu_budget CUs, or all CUs without a
+// budget.  A CU-masked stream gets a hardware queue of its own.  Plain
 // streams share the runtime's few hardware queues round-robin, and a
 // handshake wait or a join parked in a shared in-order queue would stall
-// unrelated work (a concurrent GEMM) queued behind it.
-ccr_status_t make_streams(ccr_ctx* ctx) {
-  CCR_TRY(destroy_streams(ctx));
+// unrelated work (a concurrent GEMM) queued behind it.  Every such queue
+// counts against the GPU's hardware scheduler (with about twenty of them,
+// even idle, a lone GEMM ran 1.65x slower on MI355X), so the side streams
+// are made only when a call needs them.
+ccr_status_t masked_stream(ccr_ctx* ctx, hipStream_t* s) {
+  if (*s) return CCR_OK;
   const int budget = ctx->cfg.cu_budget;
   const bool limited = budget > 0 && budget < ctx->num_cus;
   std::vector<uint32_t> mask = cu_mask_for_budget(limited ? budget : ctx->num_cus, ctx->num_cus);
-  HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_a, (uint32_t)mask.size(), mask.data()));
-  HIP_TRY(hipExtStreamCreateWithCUMask(&ctx->s_b, (uint32_t)mask.size(), mask.data()));
-  ctx->masked = limited;
+  HIP_TRY(hipExtStreamCreateWithCUMask(s, (uint32_t)mask.size(), mask.data()));
+  return CCR_OK;
+}
+
+ccr_status_t side_a(ccr_ctx* ctx, hipStream_t* out) {
+  CCR_TRY(masked_stream(ctx, &ctx->s_a));
+  *out = ctx->s_a;
+  return CCR_OK;
+}
+
+ccr_status_t side_b(ccr_ctx* ctx, hipStream_t* out) {
+  CCR_TRY(masked_stream(ctx, &ctx->s_b));
+  *out = ctx->s_b;
+  return CCR_OK;
+}
+
+// Streams for the context's configuration: with a CU budget, the budgeted
+// stream every call runs on is made now, so calls need not create it.
+ccr_status_t make_streams(ccr_ctx* ctx) {
+  CCR_TRY(destroy_streams(ctx));
+  const int budget = ctx->cfg.cu_budget;
+  ctx->masked = budget > 0 && budget < ctx->num_cus;
+  if (ctx->masked) CCR_TRY(masked_stream(ctx, &ctx->s_a));
   return CCR_OK;
 }
 
@@ -246,6 +276,21 @@ ccr_status_t refuse_capture(hipStream_t s, const char* what) {
   HIP_TRY(hipStreamIsCapturing(s, &st));
   if (st != hipStreamCaptureStatusNone)
     return fail(CCR_ERR_UNSUPPORTED, "%s cannot be captured into a graph", what);
+  return CCR_OK;
+}
+
+// The stream a call's kernels run on: the budgeted side stream when a CU
+// budget is set, else the caller's.  A budgeted call is refused while the
+// caller's stream is capturing: a graph replay runs the captured kernels on
+// the replaying stream's hardware queue, without the budget's CU mask (a
+// probe captured with a 16-CU budget reached all 256 CUs when replayed).
+ccr_status_t work_stream(ccr_ctx* ctx, hipStream_t caller, hipStream_t* s) {
+  if (!ctx->masked) {
+    *s = caller;
+    return CCR_OK;
+  }
+  CCR_TRY(refuse_capture(caller, "a call with a CU budget (a replay would run without the CU mask)"));
+  *s = ctx->s_a;
   return CCR_OK;
 }
 
@@ -363,6 +408,16 @@ LaunchTuning tuning() {
   return t;
 }
 
+// Load mode of a call's first reduce-scatter hop, whose operands were last
+// written the longest time before (-1: the call's mode, as every other hop).
+int first_hop_nontemporal() {
+  static const int m = [] {
+    const char* e = getenv("CCR_FIRST_HOP_NT");
+    return e && *e ? atoi(e) : -1;
+  }();
+  return m;
+}
+
 // The MI355X's last-level cache (MALL, Infinity Cache) in front of HBM.
 constexpr int64_t kMallBytes = int64_t(256) << 20;
 
@@ -430,8 +485,10 @@ int64_t payload(const Piece* p, size_t n) {
 
 // A kernel launch; when profiling, its start/stop events are stamped by the
 // dispatch itself (hipExtLaunchKernelGGL), so they time the kernel alone.
-ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hipStream_t s) {
-  const LaunchTuning tune = call_tuning(ctx);
+ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hipStream_t s,
+                          int nt_override = -1) {
+  LaunchTuning tune = call_tuning(ctx);
+  if (nt_override >= 0) tune.nontemporal = nt_override;
   if (!ctx->prof_on) {
     HIP_TRY(launch_pieces(kind, p, n, tune, s));
     return CCR_OK;
@@ -747,7 +804,13 @@ ccr_status_t run_ring_graph(ccr_ctx* ctx, void* const* bufs, int R, int64_t coun
   if (!g->exec && g->uses >= 0 && ++g->uses >= 2) {
     // A capture that the runtime refuses or cannot instantiate leaves this
     // key to eager launches for good (uses < 0); the call itself goes on.
-    hipStream_t cs = ctx->s_a;
+    if (!ctx->s_cap && hipStreamCreateWithFlags(&ctx->s_cap, hipStreamNonBlocking) != hipSuccess) {
+      (void)hipGetLastError();
+      ctx->s_cap = nullptr;
+      g->uses = -1;
+      return CCR_OK;
+    }
+    hipStream_t cs = ctx->s_cap;
     hipGraph_t graph = nullptr;
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
       (void)hipGetLastError();
@@ -836,12 +899,14 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
   // element sees the same operations in the same order.
   const bool pipelined = which == kWhichAllreduce && (ctx->cfg.overlap || sdma);
   const int S = pipelined ? ctx->cfg.slices : 1;
-  hipStream_t rs = ctx->masked ? ctx->s_a : caller;
+  hipStream_t rs;
+  CCR_TRY(work_stream(ctx, caller, &rs));
   // A second stream only when there is something to overlap: with a single
   // slice the all-gather (kernel copies or the SDMA job's gate) follows the
   // reduce-scatter on its stream, which saves two cross-stream waits (each
   // ~27 us of host time on this runtime when the work is still running).
-  hipStream_t ag = (S > 1 && (ctx->cfg.overlap || sdma)) ? ctx->s_b : rs;
+  hipStream_t ag = rs;
+  if (S > 1 && (ctx->cfg.overlap || sdma)) CCR_TRY(side_b(ctx, &ag));
   const size_t ev_fork = 0, ev_join_rs = 1, ev_join_ag = 2, ev_slice0 = 3;
   CCR_TRY(events(ctx, ev_slice0 + (size_t)S));
   if (rs != caller || ag != caller) {
@@ -898,7 +963,8 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
         }
         int n;
         to_pieces(&n, forward);
-        CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs));
+        CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs,
+                             k == 0 ? first_hop_nontemporal() : -1));
       }
     }
     if (which != kWhichRS && sdma) {
@@ -1049,7 +1115,17 @@ ccr_status_t ccr_ctx_create(int device, const ccr_config_t* cfg, ccr_ctx_t* out)
 ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
   if (!ctx) return CCR_OK;
   (void)hipSetDevice(ctx->device);
-  ctx->dma.reset();  // drains outstanding DMA operations, stops the proxy
+  // Stop the DMA proxy: wait for its jobs (CCR_DESTROY_TIMEOUT_MS, default
+  // 10 s), then abandon those whose streams have not reached them (each such
+  // stream is released without the copies, whenever it gets there), then
+  // wait as long again for copies that are running.
+  DmaClose how = DmaClose::kClean;
+  if (ctx->dma) {
+    const double t = (double)env_int("CCR_DESTROY_TIMEOUT_MS", 10000) * 1e-3;
+    how = ctx->dma->close(t > 0 ? t : 0.0);
+    if (how != DmaClose::kInFlight) ctx->dma.reset();
+    else (void)ctx->dma.release();  // its engines may still complete copies: keep its state
+  }
   flush_graphs(ctx);
   ccr_status_t st = destroy_streams(ctx);
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
@@ -1058,7 +1134,8 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
     (void)hipEventDestroy(t.stop);
   }
   for (hipEvent_t e : ctx->timing_pool) (void)hipEventDestroy(e);
-  if (ctx->staging) (void)hipFree(ctx->staging);
+  // An SDMA staging copy may still write the slots if the proxy gave up.
+  if (ctx->staging && how != DmaClose::kInFlight) (void)hipFree(ctx->staging);
   if (ctx->d_ecnt) (void)hipFree(ctx->d_ecnt);
   if (ctx->partials) (void)hipFree(ctx->partials);
   if (ctx->h_pinned) (void)hipHostFree(ctx->h_pinned);
@@ -1069,6 +1146,12 @@ ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx) {
     if (t.done) (void)hipEventDestroy(t.done);
   }
   delete ctx;
+  if (how == DmaClose::kAbandoned)
+    return fail(CCR_ERR_TIMEOUT, "SDMA operations whose streams had not reached them were abandoned "
+                                 "(their streams go on without the copies)");
+  if (how == DmaClose::kInFlight)
+    return fail(CCR_ERR_TIMEOUT, "SDMA copies still running at shutdown; their streams were released "
+                                 "and the memory they write is kept");
   return st;
 }
 
@@ -1077,8 +1160,8 @@ ccr_status_t ccr_ctx_set_config(ccr_ctx_t ctx, const ccr_config_t* cfg) {
   if (!cfg) return fail(CCR_ERR_INVALID_ARG, "cfg is NULL");
   CCR_TRY(check_config(cfg));
   const bool restream = cfg->cu_budget != ctx->cfg.cu_budget;
-  HIP_TRY(hipStreamSynchronize(ctx->s_a));
-  HIP_TRY(hipStreamSynchronize(ctx->s_b));
+  for (hipStream_t x : {ctx->s_a, ctx->s_b})
+    if (x) HIP_TRY(hipStreamSynchronize(x));
   flush_graphs(ctx);
   ctx->cfg = *cfg;
   if (restream) CCR_TRY(make_streams(ctx));
@@ -1174,12 +1257,19 @@ ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void* const* bufs, int R, int64_t cou
   return run_ring(ctx, bufs, R, count, dtype, kWhichAG, static_cast<hipStream_t>(stream));
 }
 
-ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* recv, int n,
-                          int64_t nbytes, void* stream) {
-  CCR_MARK("ccr_sendrecv");
+
+}  // extern "C"
+
+namespace {
+
+// Transfers m = 0..n-1, each nbytes from send[m] to recv[m], in order,
+// through the context's staging slots (the batch and ring-shift forms of
+// the staged send/recv).
+ccr_status_t run_sendrecv(ccr_ctx* ctx, const void* const* send, void* const* recv, int n,
+                          int64_t nbytes, hipStream_t caller) {
   CCR_TRY(check_ctx(ctx));
   if (n < 0 || nbytes < 0) return fail(CCR_ERR_INVALID_ARG, "n or nbytes < 0");
-  if (nbytes % 16 != 0) return fail(CCR_ERR_INVALID_ARG, "nbytes %lld is not a multiple of 16", (long long)nbytes);
+  if (nbytes % 16 != 0) return fail(CCR_ERR_INVALID_ARG, "%lld bytes per transfer is not a multiple of 16", (long long)nbytes);
   if (n == 0 || nbytes == 0) return CCR_OK;
   if (!send || !recv) return fail(CCR_ERR_INVALID_ARG, "send or recv is NULL");
   std::vector<Range> ranges;
@@ -1192,8 +1282,7 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
   ctx->footprint = 2 * (int64_t)n * nbytes + ctx->cfg.staging_chunk_bytes * ctx->cfg.staging_slots;
-  hipStream_t caller = static_cast<hipStream_t>(stream);
-  CCR_TRY(refuse_capture(caller, "ccr_sendrecv (context staging slots)"));
+  CCR_TRY(refuse_capture(caller, "a staged send/recv (context staging slots)"));
   CCR_TRY(ensure_staging(ctx));
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
     // One DMA job: the proxy runs the slot state machine itself, each fill
@@ -1230,7 +1319,8 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
   // compute-unit copies sharing HBM, so running them on two streams would
   // gain nothing on one GPU -- and a cross-stream wait costs ~27 us of host
   // time on this runtime.
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   const int P = ctx->cfg.staging_slots;
   const int64_t C = ctx->cfg.staging_chunk_bytes;
@@ -1265,9 +1355,11 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* r
   return CCR_OK;
 }
 
-ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
-                          const int64_t* counts, int64_t row_bytes, void* stream) {
-  CCR_MARK("ccr_alltoall");
+
+// All-to-all of row segments: counts[r*R + d] rows of row_bytes from rank r
+// to rank d; send[r] in destination order, recv[d] in source order.
+ccr_status_t run_alltoall_rows(ccr_ctx* ctx, const void* const* send, void* const* recv, int R,
+                               const int64_t* counts, int64_t row_bytes, hipStream_t caller) {
   CCR_TRY(check_ctx(ctx));
   if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
   if (!send || !recv || !counts) return fail(CCR_ERR_INVALID_ARG, "send, recv or counts is NULL");
@@ -1297,14 +1389,86 @@ ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* r
   CCR_TRY(check_disjoint(ranges, "send/recv"));
   ctx->footprint = 0;
   for (int r = 0; r < R; r++) ctx->footprint += (sent[(size_t)r] + got[(size_t)r]) * row_bytes;
-  hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
-    CCR_TRY(refuse_capture(caller, "ccr_alltoall with SDMA copies"));
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+    CCR_TRY(refuse_capture(caller, "an all-to-all with SDMA copies"));
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   CCR_TRY(run_alltoall(ctx, send, recv, R, counts, row_bytes, s));
   CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
+                          int64_t count, int dtype, void* stream) {
+  CCR_MARK("ccr_sendrecv");
+  CCR_TRY(check_ctx(ctx));
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (count < 0) return fail(CCR_ERR_INVALID_ARG, "count %lld < 0", (long long)count);
+  const int esize = dtype_size(dtype);
+  if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
+  if (count == 0) return CCR_OK;
+  if (count * esize % 16 != 0)
+    return fail(CCR_ERR_INVALID_ARG, "count %lld is not a whole number of 16-byte vectors",
+                (long long)count);
+  if (!send || !recv) return fail(CCR_ERR_INVALID_ARG, "send or recv is NULL");
+  // rank r's transfer lands in the buffer of its ring successor
+  std::vector<void*> to((size_t)R);
+  for (int r = 0; r < R; r++) to[(size_t)r] = recv[(r + 1) % R];
+  return run_sendrecv(ctx, send, to.data(), R, count * esize, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_sendrecv_batch(ccr_ctx_t ctx, const void* const* send, void* const* recv, int n,
+                                int64_t nbytes, void* stream) {
+  CCR_MARK("ccr_sendrecv_batch");
+  return run_sendrecv(ctx, send, recv, n, nbytes, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
+                          int64_t count, const int64_t* counts, int dtype, void* stream) {
+  CCR_MARK("ccr_alltoall");
+  CCR_TRY(check_ctx(ctx));
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (count < 0) return fail(CCR_ERR_INVALID_ARG, "count %lld < 0", (long long)count);
+  const int esize = dtype_size(dtype);
+  if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
+  const int64_t V = 16 / esize;  // elements per 16-byte vector
+  // segments as rows of one 16-byte vector each
+  std::vector<int64_t> rows((size_t)R * R);
+  if (!counts) {
+    if (count % ((int64_t)R * V) != 0)
+      return fail(CCR_ERR_INVALID_ARG,
+                  "count %lld does not split into %d segments of whole 16-byte vectors", (long long)count, R);
+    std::fill(rows.begin(), rows.end(), count / R / V);
+  } else {
+    for (int r = 0; r < R; r++) {
+      int64_t sent = 0;
+      for (int d = 0; d < R; d++) {
+        const int64_t c = counts[(size_t)r * R + d];
+        if (c < 0) return fail(CCR_ERR_INVALID_ARG, "counts[%d][%d] < 0", r, d);
+        if (c % V != 0)
+          return fail(CCR_ERR_INVALID_ARG, "counts[%d][%d] = %lld is not a whole number of 16-byte vectors",
+                      r, d, (long long)c);
+        rows[(size_t)r * R + d] = c / V;
+        sent += c;
+      }
+      if (sent != count)
+        return fail(CCR_ERR_INVALID_ARG, "rank %d sends %lld elements, not count = %lld", r,
+                    (long long)sent, (long long)count);
+    }
+  }
+  return run_alltoall_rows(ctx, send, recv, R, rows.data(), 16, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_alltoall_rows(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,
+                               const int64_t* counts, int64_t row_bytes, void* stream) {
+  CCR_MARK("ccr_alltoall_rows");
+  return run_alltoall_rows(ctx, send, recv, R, counts, row_bytes, static_cast<hipStream_t>(stream));
 }
 
 ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void* dst, const void* src, const int32_t* d_idx,
@@ -1324,7 +1488,8 @@ ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void* dst, const void* src, const i
                              reinterpret_cast<uintptr_t>(src) + (uintptr_t)(nsrc * row_bytes), 1}};
   CCR_TRY(check_disjoint(ranges, "dst/src"));
   hipStream_t caller = static_cast<hipStream_t>(stream);
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   HIP_TRY(launch_permute_rows(static_cast<char*>(dst), static_cast<const char*>(src), d_idx, nrows,
                               nsrc, row_bytes, s));
@@ -1514,7 +1679,8 @@ ccr_status_t ccr_moe_dispatch(ccr_ctx_t ctx, const void* const* x, const int32_t
   hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
     CCR_TRY(refuse_capture(caller, "ccr_moe_dispatch with SDMA copies"));
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   // pack: send[r] row j = x[r] row src_tok[r][j]
   for (int r = 0; r < R; r++)
@@ -1559,7 +1725,8 @@ ccr_status_t ccr_moe_combine(ccr_ctx_t ctx, const void* const* exp, const int32_
   hipStream_t caller = static_cast<hipStream_t>(stream);
   if (ctx->cfg.copy_mode == CCR_COPY_SDMA)
     CCR_TRY(refuse_capture(caller, "ccr_moe_combine with SDMA copies"));
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   // inverse unpack: expert-major rows back to source-segment order
   std::vector<Piece> p;
@@ -1634,7 +1801,8 @@ ccr_status_t moe_gather(ccr_ctx* ctx, int combine, const MoeShape& m, const int6
       }
   }
   CCR_TRY(refuse_capture(caller, "a fused MoE call (segment table copied from host memory)"));
-  hipStream_t s = ctx->masked ? ctx->s_a : caller;
+  hipStream_t s;
+  CCR_TRY(work_stream(ctx, caller, &s));
   CCR_TRY(order_after(ctx, 0, caller, s));
   ccr_ctx::TableSlot* slot = nullptr;
   CCR_TRY(upload_table(ctx, tab.data(), (int64_t)tab.size(), s, &slot));
@@ -1750,6 +1918,13 @@ ccr_status_t ccr_profile_intervals(ccr_ctx_t ctx, int kind, void* ref_event, dou
     k++;
   }
   *n = k;
+  return CCR_OK;
+}
+
+ccr_status_t ccr_ctx_streams(ccr_ctx_t ctx, int32_t* masked, int32_t* plain) {
+  if (!ctx) return fail(CCR_ERR_INVALID_ARG, "ctx is NULL");
+  if (masked) *masked = (ctx->s_a ? 1 : 0) + (ctx->s_b ? 1 : 0);
+  if (plain) *plain = ctx->s_cap ? 1 : 0;
   return CCR_OK;
 }
 
@@ -1869,9 +2044,12 @@ ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t* out, int nblocks, void* st
   if (nblocks == 0) return CCR_OK;
   CCR_TRY(check_dev_ptr(ctx, out, (int64_t)nblocks * 12, "out", 0));
   hipStream_t caller = static_cast<hipStream_t>(stream);
-  CCR_TRY(order_after(ctx, 0, caller, ctx->s_a));
-  HIP_TRY(launch_probe_cu_ids(out, nblocks, ctx->s_a));
-  CCR_TRY(order_after(ctx, 1, ctx->s_a, caller));
+  hipStream_t s;
+  if (ctx->masked) CCR_TRY(work_stream(ctx, caller, &s));
+  else CCR_TRY(side_a(ctx, &s));
+  CCR_TRY(order_after(ctx, 0, caller, s));
+  HIP_TRY(launch_probe_cu_ids(out, nblocks, s));
+  CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
 }
 

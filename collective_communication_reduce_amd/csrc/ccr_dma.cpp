@@ -14,18 +14,34 @@
 namespace ccr {
 namespace {
 
-constexpr int kFlags = 64;                 // flag pairs: operations in flight at once
-constexpr int kFlagStride = 32;            // words between flags (one 128-byte line each)
-constexpr uint32_t kStartValue = 0x53544152u;
-constexpr uint32_t kFinishValue = 0x46494e49u;
+constexpr int kFlagSlots = 256;            // flag-word slots in the process (jobs in flight at once)
+constexpr int kFlagStride = 32;            // words between flag words (one 128-byte line each)
 // Engines gfx950 offers for device-to-device copies when the runtime cannot
 // report them itself (engines 0 and 1 serve host transfers).
 constexpr uint32_t kFallbackEngineMask = 0xfffcu;
 
 using clk = std::chrono::steady_clock;
 
-uint32_t load_flag(const uint32_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
-void store_flag(uint32_t* p, uint32_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+// The process's flag words: coherent pinned host memory, allocated on first
+// use and kept until the process ends (a stream may read a slot's done word
+// long after the proxy that used the slot is gone), shared by every proxy.
+FlagWords* flag_words(std::string* err) {
+  static std::mutex mu;
+  static FlagWords* pool = nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (pool) return pool;
+  uint32_t* mem = nullptr;
+  const size_t bytes = sizeof(uint32_t) * kFlagStride * 2 * kFlagSlots;
+  if (hipHostMalloc(reinterpret_cast<void**>(&mem), bytes, hipHostMallocCoherent | hipHostMallocMapped) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    *err = "hipHostMalloc of the flag words failed";
+    return nullptr;
+  }
+  memset(mem, 0, bytes);
+  pool = new FlagWords(mem, kFlagSlots, kFlagStride);
+  return pool;
+}
 
 double seconds_since(clk::time_point t) {
   return std::chrono::duration<double>(clk::now() - t).count();
@@ -68,14 +84,13 @@ int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
 struct DmaProxy::Job {
   enum Kind { kCopies, kStaged } kind = kCopies;
-  enum State { kQueued, kRunning, kFinishing } state = kQueued;
+  enum State { kQueued, kRunning } state = kQueued;
   DmaSync sync = DmaSync::kHostFunc;
-  DmaProxy* owner = nullptr;
-  // kHostFunc gate: 0 not reached, 1 stream at the gate (start request),
-  // 2 copies done (finish), 3 gate returned (final acknowledgement)
-  std::atomic<int> gate{0};
-  int flag = -1;  // kStreamFlags: flag pair
-  bool aborted = false;  // handshake only partly enqueued: release without copying
+  GateBlock* gate = nullptr;  // kHostFunc: shared with the stream's host function
+  FlagWords* flags = nullptr;  // kStreamFlags: the slot and sequence number
+  int flag = -1;
+  uint32_t seq = 0;
+  bool aborted = false;  // hand-over only partly enqueued: release without copying
   bool failed = false;   // an issue call failed: stop issuing, drain what was issued
   clk::time_point t0;
   int64_t bytes = 0, ncopies = 0;
@@ -100,18 +115,34 @@ struct DmaProxy::Job {
   std::vector<SlotEvent> log;
 };
 
-DmaProxy::~DmaProxy() {
-  if (!started_) return;
-  const bool clean = drain(10.0);
+DmaProxy::~DmaProxy() { (void)close(10.0); }
+
+DmaClose DmaProxy::close(double timeout_s) {
+  if (!started_ || closed_) return DmaClose::kClean;
+  closed_ = true;
+  DmaClose how = DmaClose::kClean;
+  if (!drain(timeout_s)) {
+    // Streams that never reached their jobs (e.g. held behind other work):
+    // drop those jobs, releasing each stream for whenever it gets there.
+    abandon_queued_.store(true);
+    if (!drain(timeout_s)) {
+      std::lock_guard<std::mutex> lk(mu_);
+      give_up_ = true;
+      how = DmaClose::kInFlight;
+    }
+  }
   {
     std::lock_guard<std::mutex> lk(mu_);
     stop_ = true;
+    if (how == DmaClose::kClean && abandoned_ > 0) how = DmaClose::kAbandoned;
   }
   cv_.notify_all();
   if (thread_.joinable()) thread_.join();
+  // Signals of copies still in flight belong to jobs that were given up
+  // (leaked with them); the pool holds only completed ones.
   for (hsa_signal_t s : signal_pool_) hsa_signal_destroy(s);
-  // A stream may still be waiting on an unreleased flag: keep the memory then.
-  if (clean && flags_) (void)hipHostFree(flags_);
+  signal_pool_.clear();
+  return how;
 }
 
 void DmaProxy::note_error(const std::string& e) {
@@ -195,15 +226,6 @@ bool DmaProxy::start(int device, std::string* err) {
   }
   load_.assign(engines_.size(), 0);
   measure_engine_rate();
-
-  if (hipHostMalloc(reinterpret_cast<void**>(&flags_), sizeof(uint32_t) * kFlagStride * 2 * kFlags,
-                    hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
-    (void)hipGetLastError();
-    *err = "hipHostMalloc of the flag pool failed";
-    return false;
-  }
-  memset(flags_, 0, sizeof(uint32_t) * kFlagStride * 2 * kFlags);
-  for (int f = kFlags - 1; f >= 0; f--) free_flags_.push_back(f);
   thread_ = std::thread(&DmaProxy::loop, this);
   started_ = true;
   return true;
@@ -260,80 +282,51 @@ void DmaProxy::measure_engine_rate() {
   }
 }
 
-bool DmaProxy::take_flag(int* f, std::string* err) {
-  std::unique_lock<std::mutex> lk(mu_);
-  if (!freed_.wait_for(lk, std::chrono::seconds(30), [&] { return !free_flags_.empty(); })) {
-    *err = "no free start/finish flag pair within 30 s (DMA operations are not completing)";
-    return false;
-  }
-  *f = free_flags_.back();
-  free_flags_.pop_back();
-  return true;
-}
-
-// The stream side of the handshake: raise start, wait for the proxy's
-// acknowledgement (start back to 0), wait for finish, acknowledge it.
-bool DmaProxy::enqueue_handshake(int f, hipStream_t s, std::string* err) {
-  uint32_t* st = flags_ + (size_t)(2 * f) * kFlagStride;
-  uint32_t* fi = flags_ + (size_t)(2 * f + 1) * kFlagStride;
-  hipError_t e = hipStreamWriteValue32(s, st, kStartValue, 0);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    *err = std::string("hipStreamWriteValue32 failed: ") + hipGetErrorString(e);
-    return false;
-  }
-  e = hipStreamWaitValue32(s, st, 0, hipStreamWaitValueEq, 0xffffffffu);
-  if (e == hipSuccess) e = hipStreamWaitValue32(s, fi, kFinishValue, hipStreamWaitValueEq, 0xffffffffu);
-  if (e == hipSuccess) e = hipStreamWriteValue32(s, fi, 0, 0);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    *err = std::string("stream flag operation failed: ") + hipGetErrorString(e);
-    return false;  // start was enqueued: caller still hands the job over, marked aborted
-  }
-  return true;
-}
-
 // The host-function gate: runs on the runtime's callback thread when the
-// stream reaches it, and holds the stream until the proxy is done.
-void DmaProxy::gate(void* p) {
-  Job* j = static_cast<Job*>(p);
-  DmaProxy* self = j->owner;
-  std::unique_lock<std::mutex> lk(self->gate_mu_);
-  j->gate.store(1);
-  self->cv_.notify_one();
-  self->gate_cv_.wait(lk, [&] { return j->gate.load() == 2; });
-  j->gate.store(3);
-}
+// stream reaches it and holds the stream until the proxy releases it (or
+// returns at once for a job the proxy has abandoned).
+void DmaProxy::gate(void* p) { (void)GateBlock::arrive_and_wait(static_cast<GateBlock*>(p)); }
 
 bool DmaProxy::submit(Job* j, hipStream_t stream, std::string* err) {
-  j->owner = this;
   if (j->sync == DmaSync::kHostFunc) {
-    const hipError_t e = hipLaunchHostFunc(stream, &DmaProxy::gate, j);
+    j->gate = GateBlock::make();
+    const hipError_t e = hipLaunchHostFunc(stream, &DmaProxy::gate, j->gate);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       *err = std::string("hipLaunchHostFunc failed: ") + hipGetErrorString(e);
+      (void)GateBlock::abandon(j->gate);  // the job's reference
+      (void)GateBlock::arrive_and_wait(j->gate);  // the callback's, which will never run
       delete j;
       return false;
     }
   } else {
-    int f;
-    if (!take_flag(&f, err)) {
+    j->flags = flag_words(err);
+    if (!j->flags) {
       delete j;
       return false;
     }
-    j->flag = f;
-    std::string e2;
-    if (!enqueue_handshake(f, stream, &e2)) {
-      if (e2.rfind("hipStreamWriteValue32", 0) == 0) {  // nothing enqueued
-        delete j;
-        std::lock_guard<std::mutex> lk(mu_);
-        free_flags_.push_back(f);
-        *err = e2;
-        return false;
-      }
-      j->aborted = true;  // the stream will raise start: release it without copying
-      note_error(e2);
-      *err = e2;
+    if (!j->flags->take(&j->flag, &j->seq, std::chrono::seconds(30))) {
+      *err = "no free flag slot within 30 s (DMA operations are not completing)";
+      delete j;
+      return false;
+    }
+    hipError_t e = hipStreamWriteValue32(stream, j->flags->req(j->flag), j->seq, 0);
+    if (e != hipSuccess) {  // nothing enqueued
+      (void)hipGetLastError();
+      *err = std::string("hipStreamWriteValue32 failed: ") + hipGetErrorString(e);
+      j->flags->complete(j->flag, j->seq);
+      delete j;
+      return false;
+    }
+    e = hipStreamWaitValue32(stream, j->flags->done(j->flag), j->seq, hipStreamWaitValueGte,
+                             0xffffffffu);
+    if (e != hipSuccess) {
+      // the request is enqueued: hand the job over marked aborted, so the
+      // proxy answers the request without copying
+      (void)hipGetLastError();
+      *err = std::string("hipStreamWaitValue32 failed: ") + hipGetErrorString(e);
+      j->aborted = true;
+      note_error(*err);
     }
   }
   const bool aborted = j->aborted;
@@ -450,7 +443,7 @@ bool DmaProxy::start_copy(Job& j, int32_t i) {
 // makes its engine wait on the signal itself, and with chains on many
 // engines at once that waiting slowed a concurrent GEMM by 2x and the
 // copies themselves by two orders of magnitude on gfx950.
-bool DmaProxy::begin(Job& j) {
+void DmaProxy::begin(Job& j) {
   if (j.kind == Job::kCopies) {
     const size_t n = j.copies.size();
     j.sig.assign(n, hsa_signal_t{0});
@@ -461,7 +454,7 @@ bool DmaProxy::begin(Job& j) {
       if (a >= (int32_t)i) {  // a copy can only wait for an earlier one
         j.failed = true;
         note_error("an SDMA copy waits for a later copy of its job");
-        return true;
+        return;
       }
       if (a >= 0) j.kid_start[(size_t)a + 1]++;
     }
@@ -472,10 +465,9 @@ bool DmaProxy::begin(Job& j) {
       if (const int32_t a = j.copies[i].after; a >= 0) j.kids[(size_t)fill[(size_t)a]++] = (int32_t)i;
     for (size_t i = 0; i < n && !j.failed; i++)
       if (j.copies[i].after < 0) start_copy(j, (int32_t)i);
-    return true;
+    return;
   }
   j.slots.assign((size_t)j.plan.slots, Job::Slot());
-  return true;
 }
 
 // Progress a running job; true once every issued copy has completed and
@@ -568,6 +560,32 @@ bool DmaProxy::advance(Job& j) {
   return j.done_chunks == j.total_chunks;
 }
 
+// Has the job's stream reached the communication point?
+bool DmaProxy::arrived(Job& j) {
+  return j.sync == DmaSync::kStreamFlags ? j.flags->requested(j.flag, j.seq) : j.gate->state() == 1;
+}
+
+// Drop a job whose stream has not arrived (shutdown); false if it has.
+bool DmaProxy::try_abandon(Job& j) {
+  if (j.sync == DmaSync::kStreamFlags) {
+    if (j.flags->requested(j.flag, j.seq)) return false;
+    j.flags->abandon(j.flag);  // the stream passes whenever it gets there; slot retired
+    return true;
+  }
+  return GateBlock::abandon(j.gate);
+}
+
+// Let the job's stream go on.  `abandoned`: its copies may not have run
+// (shutdown), so a flag slot is retired rather than reused.
+void DmaProxy::release(Job& j, bool abandoned) {
+  if (j.sync == DmaSync::kStreamFlags) {
+    if (abandoned) j.flags->abandon(j.flag);
+    else j.flags->complete(j.flag, j.seq);
+  } else {
+    GateBlock::release(j.gate);
+  }
+}
+
 void DmaProxy::loop() {
   int idle = 0;  // polls in a row without progress
   for (;;) {
@@ -577,68 +595,71 @@ void DmaProxy::loop() {
         active_.push_back(incoming_.front());
         incoming_.pop_front();
       }
+      if (give_up_) {
+        // Shutdown after the timeouts: release every stream still held.
+        // Jobs with copies in flight are leaked with their signals (an
+        // engine may still complete them).
+        for (Job* j : active_) {
+          if (j->state == Job::kQueued) {
+            if (try_abandon(*j)) {
+              abandoned_++;
+              delete j;
+              continue;
+            }
+          }
+          release(*j, true);
+        }
+        active_.clear();
+        pending_ = 0;
+        freed_.notify_all();
+        return;
+      }
       if (active_.empty()) {
         if (stop_) return;
         cv_.wait_for(lk, std::chrono::milliseconds(20));
         continue;
       }
-      if (stop_ && pending_ > 0) {
-        // Shutting down with operations whose streams never arrived: stop
-        // polling (their flags stay allocated) rather than spin forever.
-        bool any_started = false;
-        for (Job* j : active_) any_started |= j->state != Job::kQueued;
-        if (!any_started) return;
-      }
     }
+    const bool abandon = abandon_queued_.load();
     bool progress = false;
     for (auto it = active_.begin(); it != active_.end();) {
       Job& j = **it;
-      const bool flags = j.sync == DmaSync::kStreamFlags;
-      uint32_t* st = flags ? flags_ + (size_t)(2 * j.flag) * kFlagStride : nullptr;
-      uint32_t* fi = flags ? flags_ + (size_t)(2 * j.flag + 1) * kFlagStride : nullptr;
+      bool finished = false;
       if (j.state == Job::kQueued) {
-        if (flags ? load_flag(st) == kStartValue : j.gate.load() == 1) {
-          if (flags) store_flag(st, 0);  // acknowledge the start request
+        if (arrived(j)) {
           j.t0 = clk::now();
           if (!j.aborted) begin(j);
           j.state = Job::kRunning;
           progress = true;
+        } else if (abandon && try_abandon(j)) {
+          std::lock_guard<std::mutex> lk(mu_);
+          abandoned_++;
+          finished = true;
         }
-      } else if (j.state == Job::kRunning) {
-        if (j.aborted || advance(j)) {
-          if (j.kind == Job::kStaged && !j.aborted && !j.failed) note_staged(j, seconds_since(j.t0));
-          if (const int d = finish_delay_us_.load(); d > 0)
-            std::this_thread::sleep_for(std::chrono::microseconds(d));
-          {
-            std::lock_guard<std::mutex> lk(mu_);
-            if (!j.aborted && !j.failed) {
-              stats_.jobs++;
-              stats_.copies += j.kind == Job::kCopies ? (int64_t)j.sig.size() : j.ncopies;
-              stats_.bytes += 2 * j.bytes;
-              stats_.ms += 1e3 * seconds_since(j.t0);
-            }
-            if (j.kind == Job::kStaged) slot_log_ = j.log;
-          }
-          for (hsa_signal_t s : j.sig)
-            if (s.handle) put_signal(s);
-          j.sig.clear();
-          if (flags) {
-            store_flag(fi, kFinishValue);  // release the stream
-          } else {
-            {
-              std::lock_guard<std::mutex> lk(gate_mu_);
-              j.gate.store(2);
-            }
-            gate_cv_.notify_all();
-          }
-          j.state = Job::kFinishing;
-          progress = true;
-        }
-      } else if (flags ? load_flag(fi) == 0 : j.gate.load() == 3) {
-        // the stream acknowledged the finish: the job (and its flag pair) is free
+      }
+      if (!finished && j.state == Job::kRunning && (j.aborted || advance(j))) {
+        if (j.kind == Job::kStaged && !j.aborted && !j.failed) note_staged(j, seconds_since(j.t0));
+        if (const int d = finish_delay_us_.load(); d > 0)
+          std::this_thread::sleep_for(std::chrono::microseconds(d));
         {
           std::lock_guard<std::mutex> lk(mu_);
-          if (flags) free_flags_.push_back(j.flag);
+          if (!j.aborted && !j.failed) {
+            stats_.jobs++;
+            stats_.copies += j.kind == Job::kCopies ? (int64_t)j.sig.size() : j.ncopies;
+            stats_.bytes += 2 * j.bytes;
+            stats_.ms += 1e3 * seconds_since(j.t0);
+          }
+          if (j.kind == Job::kStaged) slot_log_ = j.log;
+        }
+        for (hsa_signal_t x : j.sig)
+          if (x.handle) put_signal(x);
+        j.sig.clear();
+        release(j, false);
+        finished = true;
+      }
+      if (finished) {
+        {
+          std::lock_guard<std::mutex> lk(mu_);
           pending_--;
         }
         freed_.notify_all();

@@ -115,4 +115,5 @@ hipError_t launch_moe_plan(const int32_t* topk, int64_t T, int E, int K, int elo
 // One wave64 workgroup per block; writes (XCC id, SE id, CU id) per block.
 hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream);
 
+
 }  // namespace ccr

@@ -30,8 +30,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // The pieces of one launch, by value in the kernel arguments.  NP slots: a
-// launch of up to 8 or 16 pieces (one ring hop of R <= 16 ranks) uses the
-// small table, because a launch's host cost grows with its argument block
+// launch of up to 8, 16 or 32 pieces (one ring hop of R <= 32 ranks) uses a
+// smaller table, because a launch's host cost grows with its argument block
 // (on gfx950, ~2.3 us for 32 bytes, ~4.7 us for the 2.6 KB of 64 slots).
 template <int NP>
 struct PieceArgs {
@@ -126,6 +126,19 @@ constexpr int tail_unit_bytes() {
   return is_f32<K>() ? 4 : 2;
 }
 
+// Piece of workgroup tile b: the number of pieces after the first whose
+// first tile is <= b.  Unused slots hold the total tile count (> b), so the
+// count runs over the whole table with no bound on n: the table's entries
+// are independent scalar loads issued together, instead of the dependent
+// chain of loads a binary search makes every workgroup wait through.
+template <int NP>
+__device__ __forceinline__ int piece_of(const int32_t* tile_start, int b) {
+  int lo = 0;
+#pragma unroll
+  for (int i = 1; i < NP; i++) lo += tile_start[i] <= b ? 1 : 0;
+  return lo;
+}
+
 // One tile = kBlock * U consecutive 16-byte vectors of one piece.  Thread t
 // handles vectors first + u * kBlock + t, u < U, so every load instruction
 // of a wave covers 1 KiB of contiguous memory.  All loads of a tile are
@@ -138,16 +151,14 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
   // 2 = only the incoming operand's load non-temporal (it is read once and
   // is dead afterwards, so it need not displace the result, which the next
   // hop reads, from the caches)
+  // 3 = both loads non-temporal, the store temporal (the local operand is
+  // overwritten by the result, and only the result is read again)
   constexpr bool NT = NTM == 1;
   constexpr bool NTI = NTM != 0;
-  const int ntiles = a.tile_start[a.n];
+  constexpr bool NTL = NTM == 1 || NTM == 3;
+  const int ntiles = a.tile_start[NP];
   for (int b = blockIdx.x; b < ntiles; b += gridDim.x) {
-    int lo = 0, hi = a.n;  // tile_start[lo] <= b < tile_start[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tile_start[mid] <= b) lo = mid;
-      else hi = mid;
-    }
+    const int lo = piece_of<NP>(a.tile_start, b);  // tile_start[lo] <= b < tile_start[lo + 1]
     char* const dst = a.p[lo].dst;
     char* const dst2 = a.p[lo].dst2;
     const char* const src = a.p[lo].src;
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
         in[u] = load16<NTI>(s16 + v0 + u * kBlock);
-        if constexpr (K != HopKind::kCopy) loc[u] = load16<NT>(d16 + v0 + u * kBlock);
+        if constexpr (K != HopKind::kCopy) loc[u] = load16<NTL>(d16 + v0 + u * kBlock);
       }
 #pragma unroll
       for (int u = 0; u < U; u++) {
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void pieces_kernel(PieceArgs<NP> a) {
         const int64_t v = v0 + u * kBlock;
         if (v < nvec) {
           u32x4 loc = {0, 0, 0, 0};
-          if constexpr (K != HopKind::kCopy) loc = load16<NT>(d16 + v);
+          if constexpr (K != HopKind::kCopy) loc = load16<NTL>(d16 + v);
           const u32x4 r = apply16<K>(loc, load16<NTI>(s16 + v));
           if constexpr (K == HopKind::kDrainFill) store16<NT>(f16 + v, loc);
           store16<NT>(d16 + v, r);
@@ -219,19 +230,24 @@ hipError_t launch_kind(const PieceArgs<kMaxPieces>& a, int ntm, hipStream_t s, T
   switch (ntm) {
     case 1: return launch_one<K, U, 1>(a, s, t, g);
     case 2: return launch_one<K, U, 2>(a, s, t, g);
+    case 3: return launch_one<K, U, 3>(a, s, t, g);
     default: return launch_one<K, U, 0>(a, s, t, g);
   }
 }
 
 // Every tuning variant exists for the full table; the small tables exist for
-// 2 vectors per operand per thread with temporal accesses or a non-temporal
-// incoming load.
+// 2 vectors per operand per thread with temporal accesses or non-temporal
+// loads (incoming only, or both operands).
 template <HopKind K, int NP>
 hipError_t launch_unroll(const PieceArgs<NP>& a, int unroll, int nt, hipStream_t s, Timing t,
                          int g) {
   if constexpr (NP != kMaxPieces) {
     (void)unroll;
-    return nt == 2 ? launch_one<K, 2, 2>(a, s, t, g) : launch_one<K, 2, 0>(a, s, t, g);
+    switch (nt) {
+      case 2: return launch_one<K, 2, 2>(a, s, t, g);
+      case 3: return launch_one<K, 2, 3>(a, s, t, g);
+      default: return launch_one<K, 2, 0>(a, s, t, g);
+    }
   } else {
     switch (unroll) {
       case 1: return launch_kind<K, 1>(a, nt, s, t, g);
@@ -328,12 +344,7 @@ __device__ __forceinline__ void partial_one(const PartialPiece& pc, int64_t i) {
 template <PartialKind K, int NP>
 __global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
   const int b = blockIdx.x;
-  int lo = 0, hi = a.n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tile_start[mid] <= b) lo = mid;
-    else hi = mid;
-  }
+  const int lo = piece_of<NP>(a.tile_start, b);
   const PartialPiece pc = a.p[lo];
   const int64_t ngroups = pc.n >> 3;
   const int64_t tile = b - a.tile_start[lo];
@@ -397,7 +408,7 @@ hipError_t launch_pieces_np(HopKind kind, const Piece* pieces, int n, LaunchTuni
   }
   for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
-  const int nt = tune.nontemporal == 1 || tune.nontemporal == 2 ? tune.nontemporal : 0;
+  const int nt = tune.nontemporal >= 1 && tune.nontemporal <= 3 ? tune.nontemporal : 0;
   const Timing t{start, stop};
   const int g = tune.grid;
   switch (kind) {
@@ -424,6 +435,8 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
     return launch_pieces_np<8>(kind, pieces, n, tune, unroll, stream, start, stop);
   if (small_ok && n <= 16)
     return launch_pieces_np<16>(kind, pieces, n, tune, unroll, stream, start, stop);
+  if (small_ok && n <= 32)
+    return launch_pieces_np<32>(kind, pieces, n, tune, unroll, stream, start, stop);
   return launch_pieces_np<kMaxPieces>(kind, pieces, n, tune, unroll, stream, start, stop);
 }
 

@@ -50,14 +50,17 @@
  *     work around it.
  *   - HIP graphs: a call made of kernel launches only can be captured on a
  *     capturing stream and replayed (the ring collectives with kernel copies
- *     and per-hop bf16, with or without CU budget, slices or overlap;
- *     ccr_alltoall, ccr_moe_dispatch and ccr_moe_combine with kernel copies;
- *     ccr_permute_rows; ccr_moe_topk).  A replay reuses the device pointers
- *     given at capture time.  Calls that would depend on context scratch
- *     that may be reallocated, on host memory copied at launch, or on the
- *     DMA proxy (SDMA copies, fp32 partials, ccr_sendrecv, ccr_moe_plan,
- *     the fused MoE calls) return CCR_ERR_UNSUPPORTED while `stream` is
- *     capturing, and enqueue nothing.
+ *     and per-hop bf16, with or without slices or overlap; ccr_alltoall,
+ *     ccr_alltoall_rows, ccr_moe_dispatch and ccr_moe_combine with kernel
+ *     copies; ccr_permute_rows; ccr_moe_topk).  A replay reuses the device
+ *     pointers given at capture time.  Calls that would depend on context
+ *     scratch that may be reallocated, on host memory copied at launch, or
+ *     on the DMA proxy (SDMA copies, fp32 partials, ccr_sendrecv,
+ *     ccr_sendrecv_batch, ccr_moe_plan, the fused MoE calls) return
+ *     CCR_ERR_UNSUPPORTED while `stream` is capturing, and enqueue nothing;
+ *     so does every call of a context with a CU budget, because a replay
+ *     runs the captured kernels on the replaying stream's hardware queue,
+ *     without the budget's CU mask.
  */
 #ifndef CCR_H
 #define CCR_H
@@ -90,16 +93,21 @@ typedef enum { CCR_F32 = 0, CCR_BF16 = 1 } ccr_dtype_t;
  * acknowledgement); see ccr_dma_sync_t. */
 typedef enum { CCR_COPY_KERNEL = 0, CCR_COPY_SDMA = 1 } ccr_copy_mode_t;
 
-/* How an SDMA operation is tied to the stream.
- * HOST_FUNC (default): a hipLaunchHostFunc gate; the gate hands the
- *   operation to the proxy and returns when the copies are done, and the
- *   stream waits on the gate's completion without any GPU-side polling.
- * STREAM_FLAGS: the flag handshake of HOCCL Listing 1 on host flags with
- *   hipStreamWriteValue32 / hipStreamWaitValue32 (the stream raises start,
- *   waits for the proxy to reset it, waits for finish, resets it).  This
- *   HIP runtime executes those as kernels, and a stream waiting in
- *   hipStreamWaitValue32 for the length of a DMA slows concurrent compute
- *   by tens of percent, so it is kept for comparison only. */
+/* How an SDMA operation is tied to the stream (HOCCL §3.2: the CPU takes
+ * over when the stream reaches the communication point, and the stream
+ * continues once the copies are done).
+ * HOST_FUNC (default): a hipLaunchHostFunc gate; the gate announces that
+ *   the stream has arrived and returns when the proxy releases it after
+ *   the copies, and the stream waits on the gate's completion without any
+ *   GPU-side polling.
+ * STREAM_FLAGS: stream memory operations on words in coherent host memory:
+ *   the stream writes the operation's sequence number into a request word
+ *   (hipStreamWriteValue32) and waits until the proxy's done word reaches
+ *   it (hipStreamWaitValue32, >=); numbers only grow, so nothing is reset
+ *   and nothing is acknowledged.  This HIP runtime executes those operations
+ *   as kernels, and a stream waiting in hipStreamWaitValue32 for the length
+ *   of a DMA slows concurrent compute by tens of percent, so it is kept for
+ *   comparison only. */
 typedef enum { CCR_DMA_SYNC_HOST_FUNC = 0, CCR_DMA_SYNC_STREAM_FLAGS = 1 } ccr_dma_sync_t;
 
 /* bf16 reduce-scatter accumulation.  PER_HOP: every hop computes
@@ -183,13 +191,25 @@ typedef struct ccr_ctx *ccr_ctx_t;
 ccr_status_t ccr_config_default(ccr_config_t *cfg);
 
 /* Create a context on HIP device `device`.  cfg NULL = ccr_config_default().
- * The context owns its side streams (CU-masked when cu_budget is set),
- * events, staging slots, small device scratch and -- from the first SDMA
- * use on -- the DMA proxy thread, its flag pool and its engine list (every
- * engine is warmed with a small copy when the proxy starts).  Makes
+ * The context owns its side streams, events, staging slots, small device
+ * scratch and -- from the first SDMA use on -- the DMA proxy thread and its
+ * engine list (every engine is warmed with a small copy when the proxy
+ * starts).  Side streams are CU-masked streams, each with a hardware queue
+ * of its own (HOCCL §3.2: the stream manager runs communication on streams
+ * of its own): the budgeted stream is made with the context when cu_budget
+ * is set; a second one only when a call first overlaps an all-gather with
+ * the next slice's reduce-scatter (overlap, or SDMA copies with slices > 1).
+ * A context that needs neither holds no hardware queue of its own.  Makes
  * `device` current on the calling thread. */
 ccr_status_t ccr_ctx_create(int device, const ccr_config_t *cfg, ccr_ctx_t *out);
-/* Waits for the context's streams, then frees everything it owns. */
+/* Waits for the context's streams and SDMA operations, then frees
+ * everything it owns.  An SDMA operation whose stream has not reached it
+ * within CCR_DESTROY_TIMEOUT_MS (environment, default 10000) is abandoned:
+ * its stream, when it gets there, goes on without the copies, and the call
+ * returns CCR_ERR_TIMEOUT.  Copies still running after as long again are
+ * left to finish: their streams are released, the memory they may write
+ * (the staging slots) is kept, and CCR_ERR_TIMEOUT is returned.  The
+ * context is gone in every case. */
 ccr_status_t ccr_ctx_destroy(ccr_ctx_t ctx);
 /* Replace the configuration.  Synchronises the context's streams first. */
 ccr_status_t ccr_ctx_set_config(ccr_ctx_t ctx, const ccr_config_t *cfg);
@@ -273,8 +293,14 @@ ccr_status_t ccr_schedule_stages(const int64_t *C, int G, const int32_t *node,
 
 /* ----------------------------------------------------------------------
  * Ring collectives, in place over R virtual ranks.
- * bufs: host array of R device pointers, each to `count` elements of dtype;
- * the R buffers must not overlap.  1 <= R <= 64.
+ * bufs: host array of R device pointers, each to `count` elements of dtype
+ * (CCR_F32 or CCR_BF16); the R buffers must not overlap.  1 <= R <= 64.
+ *
+ * HOCCL composes every collective from point-to-point flows (§3.4,
+ * Collective Scheduler, Fig. 6) and runs the reductions on the GPU cores
+ * (§5 Limitations: reduction operators need core-side execution); the
+ * pages describe no ring, so the ring here is the textbook one named at
+ * the top of this file, each hop a pass over every rank's chunk.
  *
  * ccr_allreduce: every rank ends with the element-wise sum over all ranks.
  *   Element i of chunk c is reduced in the order the partial travels round
@@ -284,7 +310,13 @@ ccr_status_t ccr_schedule_stages(const int64_t *C, int G, const int32_t *node,
  * ccr_reduce_scatter: afterwards chunk r of bufs[r] holds the reduced chunk
  *   r; the other chunks hold partial sums.
  * ccr_all_gather: on entry chunk r of bufs[r] is rank r's contribution;
- *   afterwards every buffer holds all R chunks.  A pure copy.
+ *   afterwards every buffer holds all R chunks.  A pure copy (HOCCL §6.2,
+ *   Fig. 8a-b measures AllGather as a DMA copy workload).
+ * Errors: CCR_ERR_INVALID_ARG for a NULL or misaligned pointer, a buffer
+ * that does not hold count elements, overlapping ranks, R or dtype out of
+ * range; CCR_ERR_UNSUPPORTED for a call that cannot be captured while
+ * `stream` is capturing (see the conventions above); CCR_ERR_HIP / OOM for
+ * runtime failures.  Nothing is enqueued when an error is returned.
  * ---------------------------------------------------------------------- */
 ccr_status_t ccr_allreduce(ccr_ctx_t ctx, void *const *bufs, int R, int64_t count,
                            int dtype, void *stream);
@@ -295,36 +327,66 @@ ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void *const *bufs, int R, int64_t cou
 
 /* ----------------------------------------------------------------------
  * Point-to-point transfers through the context's staging pool (HOCCL
- * §3.3.1 DMA-RNIC chunk pipelining; slot states of Fig. 4).  Transfer m
- * copies nbytes from send[m] to recv[m], chunk by chunk: chunk i is copied
- * into slot i mod staging_slots (filling) and out of it (draining), and a
- * slot is refilled only after it has drained.  SDMA copies: the DMA proxy
- * runs each slot's state machine, fills and drains on different engines, so
- * they overlap.  Kernel copies: rounds of staging_slots chunks on one
- * stream; one launch drains each slot's chunk of the previous round to the
- * receiver and refills the slot with this round's chunk (each thread reads
- * its part of the slot before overwriting it), so a transfer of T chunks
- * takes ceil(T / staging_slots) + 1 launches (both stages share the compute
- * units and HBM, so running them apart would overlap nothing).
- * Transfers run in order m = 0..n-1.  send/recv: host arrays of n device
- * pointers; the 2n ranges must not overlap.  nbytes must be a multiple of 16.
+ * §3.3.1 DMA-RNIC chunk pipelining; the slot states of Fig. 4).  A transfer
+ * is cut into staging_chunk_bytes chunks; chunk i (counted over all of the
+ * call's transfers in order) is copied into slot i mod staging_slots
+ * (filling) and out of it (draining), and a slot is refilled only after it
+ * has drained.  SDMA copies: the DMA proxy runs each slot's state machine,
+ * fills and drains on different engines, so they overlap.  Kernel copies:
+ * rounds of staging_slots chunks on one stream; one launch drains each
+ * slot's chunk of the previous round to the receiver and refills the slot
+ * with this round's chunk (each thread reads its part of the slot before
+ * overwriting it), so a transfer of T chunks takes ceil(T / staging_slots)
+ * + 1 launches (both stages share the compute units and HBM, so running
+ * them apart would overlap nothing).  The buffers of one call must not
+ * overlap.  The staging slots are context scratch (see the conventions).
+ *
+ * ccr_sendrecv: the ring shift over R ranks (HOCCL §3.4 group Send/Recv):
+ *   recv[(r + 1) % R] <- send[r] for every r, `count` elements of dtype
+ *   each, transfers in the order r = 0..R-1.  R = 2 is a pipeline pair
+ *   exchanging in both directions.  send, recv: host arrays of R device
+ *   pointers.  count * element size must be a multiple of 16.
+ * ccr_sendrecv_batch: n transfers in one direction, recv[m] <- send[m],
+ *   nbytes each (a multiple of 16), in the order m = 0..n-1: the micro-
+ *   batches one pipeline stage sends the next.
+ * Errors as for the ring collectives; CCR_ERR_OOM when the staging pool
+ * cannot be allocated (nothing is enqueued; a smaller pool works again).
  * ---------------------------------------------------------------------- */
-ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void *const *send, void *const *recv, int n,
-                          int64_t nbytes, void *stream);
+ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void *const *send, void *const *recv, int R,
+                          int64_t count, int dtype, void *stream);
+ccr_status_t ccr_sendrecv_batch(ccr_ctx_t ctx, const void *const *send, void *const *recv, int n,
+                                int64_t nbytes, void *stream);
 
 /* ----------------------------------------------------------------------
- * All-to-all of row segments over R ranks (HOCCL §6.2 / Fig. 8c-d
- * All-to-All).  counts: host array, counts[r*R + d] = rows rank r sends to
- * rank d.  send[r] holds its segments contiguously in destination order;
- * recv[d] receives its segments contiguously in source order.  row_bytes
- * must be a multiple of 16.
+ * All-to-all over R ranks (HOCCL §6.2, Fig. 8c-d All-to-All; §2.1: the
+ * expert-parallel dispatch and combine are all-to-all traffic).  Every
+ * (source, destination) segment is its own flow; with SDMA copies the
+ * flows are cut into chunks interleaved by size (§3.4).
+ *
+ * ccr_alltoall: send[r] holds `count` elements of dtype, its segments for
+ *   d = 0..R-1 contiguous in destination order; recv[d] receives its
+ *   segments contiguously in source order r = 0..R-1.  counts: host int64
+ *   [R*R], counts[r*R + d] = elements r sends to d (each row summing to
+ *   count), or NULL for count / R to every rank.  Every segment must be a
+ *   whole number of 16-byte vectors, and recv[d] must hold the elements it
+ *   receives (count, when counts is NULL).
+ * ccr_alltoall_rows: the same exchange counted in rows of row_bytes (a
+ *   multiple of 16): counts[r*R + d] rows from r to d (the form the MoE
+ *   calls use, rows being tokens).
+ * Errors as for the ring collectives, and CCR_ERR_INVALID_ARG for a negative
+ * count, a row of counts that does not sum to count, or a ragged segment.
  * ---------------------------------------------------------------------- */
 ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void *const *send, void *const *recv, int R,
-                          const int64_t *counts, int64_t row_bytes, void *stream);
+                          int64_t count, const int64_t *counts, int dtype, void *stream);
+ccr_status_t ccr_alltoall_rows(ccr_ctx_t ctx, const void *const *send, void *const *recv, int R,
+                               const int64_t *counts, int64_t row_bytes, void *stream);
 
-/* dst row i = src row d_idx[i], for i < nrows.  d_idx: device int32, each
- * entry in [0, nsrc); an out-of-range entry leaves that dst row unwritten
- * (the indices live on the device, so no error is returned for it). */
+/* dst row i = src row d_idx[i], for i < nrows (the row gather of the MoE
+ * pack and unpack: tokens placed by destination and expert before the
+ * all-to-all, HOCCL §2.1).  d_idx: device int32, each entry in [0, nsrc);
+ * nsrc, the rows src holds, bounds the indices, and an out-of-range entry
+ * leaves that dst row unwritten (the indices live on the device, so no
+ * error is returned for it).  dst must not overlap src. */
 ccr_status_t ccr_permute_rows(ccr_ctx_t ctx, void *dst, const void *src, const int32_t *d_idx,
                               int64_t nrows, int64_t nsrc, int64_t row_bytes, void *stream);
 
@@ -431,7 +493,7 @@ int32_t ccr_dma_pace(int64_t bytes, int64_t deadline_us, double engine_gbs, int3
 ccr_status_t ccr_dma_rate(ccr_ctx_t ctx, double *engine_gbs, int32_t *last_engines);
 
 /* Fault injection for watchdog tests: the DMA proxy holds every
- * operation's finish flag for `us` microseconds after its copies complete
+ * operation's release for `us` microseconds after its copies complete
  * (0 = off).  The stream is always released in the end. */
 ccr_status_t ccr_dma_hold_finish(ccr_ctx_t ctx, int us);
 
@@ -446,6 +508,11 @@ const char *ccr_version(void);
  * [3*nblocks].  Used to show which compute units a CU budget leaves to the
  * collective. */
 ccr_status_t ccr_probe_cu_ids(ccr_ctx_t ctx, int32_t *out, int nblocks, void *stream);
+/* Streams the context holds now: *masked = CU-masked side streams (each
+ * with a hardware queue of its own), *plain = plain streams (sharing the
+ * runtime's queue pool; the graph cache's capture stream).  Host only;
+ * either pointer may be NULL. */
+ccr_status_t ccr_ctx_streams(ccr_ctx_t ctx, int32_t *masked, int32_t *plain);
 /* The context's graph cache (ccr_config_t.graph_cache): *graphs = captured
  * graphs it holds now, *replays = ring calls served by a replay since the
  * context was created.  Host only; either pointer may be NULL. */

@@ -64,6 +64,7 @@ def lib():
         L.orc_ring_reduce_scatter.argtypes = [vp, vp, i32, i64, i32, i32]
         L.orc_ring_all_gather.argtypes = [vp, i32, i64, i32, i32]
         L.orc_ring_allreduce.argtypes = [vp, vp, i32, i64, i32, i32]
+        L.orc_ring_allreduce_range.argtypes = [vp, vp, i32, i64, i32, i32, i64, i64]
         L.orc_ring_step.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i32]
         L.orc_fold.argtypes = [vp, i32, i64, i32, vp]
         L.orc_fold_at.argtypes = [vp, i32, i64, i32, vp, i64, vp]
@@ -178,6 +179,36 @@ def ring_allreduce(bufs, S: int = 1, bf16_acc: str = "per_hop", inplace: bool = 
     return bufs
 
 
+def ring_allreduce_range(bufs, lo: int, hi: int, S: int = 1, bf16_acc: str = "per_hop",
+                         part=None):
+    """In place: the ring all-reduce of ``ring_allreduce`` on elements
+    [lo, hi) of every buffer only (every hop, in the same order).  Element
+    results depend on no other element, so disjoint ranges covering the
+    buffers give exactly the unsplit result, in any order or at once."""
+    bufs, n, dt = _prep(bufs)
+    code = _code(dt, bf16_acc)
+    if code == BF16_P32 and part is None:
+        raise ValueError("fp32 partials need the R partial buffers")
+    _check(lib().orc_ring_allreduce_range(_ptrs(bufs), _ptrs(part) if part else None, len(bufs),
+                                          n, S, code, lo, hi))
+    return bufs
+
+
+def ring_allreduce_threads(bufs, threads: int, S: int = 1, bf16_acc: str = "per_hop"):
+    """``ring_allreduce`` with the element range cut into ``threads`` equal
+    parts, each run by ``ring_allreduce_range`` on a thread of its own (the C
+    call releases Python's lock).  Returns new buffers."""
+    from concurrent.futures import ThreadPoolExecutor
+    bufs, n, dt = _prep([b.copy() for b in bufs])
+    part = [np.zeros(n, np.float32) for _ in bufs] if _code(dt, bf16_acc) == BF16_P32 else None
+    T = max(1, int(threads))
+    cuts = [n * t // T for t in range(T + 1)]
+    with ThreadPoolExecutor(T) as ex:
+        list(ex.map(lambda t: ring_allreduce_range(bufs, cuts[t], cuts[t + 1], S, bf16_acc, part),
+                    range(T)))
+    return bufs
+
+
 def fold(xs, bf16_acc: str = "per_hop"):
     """Closed form of the ring result (one buffer, identical on every rank)."""
     xs, n, dt = _prep(xs)
@@ -212,6 +243,16 @@ def staged_copy(srcs, chunk_bytes: int, nslots: int):
     if nev < 0:
         raise ValueError("illegal staging slot transition")
     return dsts, ev[:nev]
+
+
+def ring_sendrecv(sends, chunk_bytes: int, nslots: int):
+    """The ring shift through the staging pool: transfer r carries send[r]
+    to rank (r + 1) mod R, the transfers in order r = 0..R-1 (HOCCL §3.4,
+    Fig. 6: a collective described as a group of Send/Recv pairs).  Returns
+    (recvs, events) with recvs[q] the bytes rank q received."""
+    R = len(sends)
+    dsts, ev = staged_copy(sends, chunk_bytes, nslots)
+    return [dsts[(q - 1) % R] for q in range(R)], ev
 
 
 def alltoall(sends, counts, row_bytes: int):

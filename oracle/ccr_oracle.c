@@ -66,13 +66,18 @@ void orc_slice_bounds(int64_t clo, int64_t chi, int S, int vec, int s,
     *hi = clo + min64(len, (int64_t)(s + 1) * sl);
 }
 
-/* Element range touched by slice s of chunk c. */
+/* Element range touched by slice s of chunk c, restricted to the window
+ * [wlo, whi) of element indices (the whole buffer, [0, n), except in the
+ * range entry point below: every element's operations depend on no other
+ * element, so a window sees exactly the operations of the full run). */
 static void piece(int64_t n, int R, int S, int vec, int c, int s,
-                  int64_t *lo, int64_t *hi)
+                  int64_t wlo, int64_t whi, int64_t *lo, int64_t *hi)
 {
     int64_t clo, chi;
     orc_chunk_bounds(n, R, vec, c, &clo, &chi);
     orc_slice_bounds(clo, chi, S, vec, s, lo, hi);
+    if (*lo < wlo) *lo = wlo;
+    if (*hi > whi) *hi = whi;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -115,36 +120,38 @@ void orc_bf16_to_f32_array(const uint16_t *in, float *out, int64_t n)
 /* not depend on S; S only changes which elements a hop moves at a time.     */
 /* ------------------------------------------------------------------------ */
 
-static void rs_step_f32(float *const *b, int R, int64_t n, int S, int s, int k)
+static void rs_step_f32(float *const *b, int R, int64_t n, int S, int s, int k,
+                        int64_t wlo, int64_t whi)
 {
     for (int q = 0; q < R; q++) {
         int c = mod(q - k - 2, R), p = mod(q - 1, R);
         int64_t lo, hi;
-        piece(n, R, S, 4, c, s, &lo, &hi);
+        piece(n, R, S, 4, c, s, wlo, whi, &lo, &hi);
         for (int64_t i = lo; i < hi; i++) b[q][i] = b[q][i] + b[p][i];
     }
 }
 
 static void ag_step(void *const *b, int R, int64_t n, int S, int s, int k,
-                    int esize)
+                    int esize, int64_t wlo, int64_t whi)
 {
     int vec = 16 / esize;
     for (int q = 0; q < R; q++) {
         int c = mod(q - k - 1, R), p = mod(q - 1, R);
         int64_t lo, hi;
-        piece(n, R, S, vec, c, s, &lo, &hi);
+        piece(n, R, S, vec, c, s, wlo, whi, &lo, &hi);
         if (hi > lo)
             memcpy((char *)b[q] + lo * esize, (char *)b[p] + lo * esize,
                    (size_t)(hi - lo) * esize);
     }
 }
 
-static void rs_step_bf16(uint16_t *const *b, int R, int64_t n, int S, int s, int k)
+static void rs_step_bf16(uint16_t *const *b, int R, int64_t n, int S, int s, int k,
+                         int64_t wlo, int64_t whi)
 {
     for (int q = 0; q < R; q++) {
         int c = mod(q - k - 2, R), p = mod(q - 1, R);
         int64_t lo, hi;
-        piece(n, R, S, 8, c, s, &lo, &hi);
+        piece(n, R, S, 8, c, s, wlo, whi, &lo, &hi);
         for (int64_t i = lo; i < hi; i++)
             b[q][i] = orc_f32_to_bf16(orc_bf16_to_f32(b[q][i]) +
                                       orc_bf16_to_f32(b[p][i]));
@@ -155,12 +162,12 @@ static void rs_step_bf16(uint16_t *const *b, int R, int64_t n, int S, int s, int
  * last reduced; the value that travels from q-1 to q at step k>0 is
  * part[q-1], at step 0 it is the bf16 input of q-1.  The last hop rounds. */
 static void rs_step_bf16_p32(uint16_t *const *b, float *const *part, int R,
-                             int64_t n, int S, int s, int k)
+                             int64_t n, int S, int s, int k, int64_t wlo, int64_t whi)
 {
     for (int q = 0; q < R; q++) {
         int c = mod(q - k - 2, R), p = mod(q - 1, R);
         int64_t lo, hi;
-        piece(n, R, S, 8, c, s, &lo, &hi);
+        piece(n, R, S, 8, c, s, wlo, whi, &lo, &hi);
         for (int64_t i = lo; i < hi; i++) {
             float in = (k == 0) ? orc_bf16_to_f32(b[p][i]) : part[p][i];
             float acc = in + orc_bf16_to_f32(b[q][i]);
@@ -179,9 +186,9 @@ int orc_ring_reduce_scatter(void *const *b, float *const *part, int R,
     if (dtype == 2 && R > 1 && part == NULL) return ORC_EINVAL;
     for (int s = 0; s < S; s++)
         for (int k = 0; k + 1 < R; k++) {
-            if (dtype == 0) rs_step_f32((float *const *)b, R, n, S, s, k);
-            else if (dtype == 1) rs_step_bf16((uint16_t *const *)b, R, n, S, s, k);
-            else rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k);
+            if (dtype == 0) rs_step_f32((float *const *)b, R, n, S, s, k, 0, n);
+            else if (dtype == 1) rs_step_bf16((uint16_t *const *)b, R, n, S, s, k, 0, n);
+            else rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k, 0, n);
         }
     return ORC_OK;
 }
@@ -190,7 +197,7 @@ int orc_ring_all_gather(void *const *b, int R, int64_t n, int S, int esize)
 {
     if (R < 1 || S < 1 || n < 0 || (esize != 2 && esize != 4)) return ORC_EINVAL;
     for (int s = 0; s < S; s++)
-        for (int k = 0; k + 1 < R; k++) ag_step(b, R, n, S, s, k, esize);
+        for (int k = 0; k + 1 < R; k++) ag_step(b, R, n, S, s, k, esize, 0, n);
     return ORC_OK;
 }
 
@@ -202,14 +209,14 @@ int orc_ring_step(void *const *b, float *const *part, int R, int64_t n, int S,
     if (R < 1 || S < 1 || n < 0 || dtype < 0 || dtype > 2) return ORC_EINVAL;
     if (s < 0 || s >= S || k < 0 || k > R - 2 || phase < 0 || phase > 1) return ORC_EINVAL;
     if (phase == 1) {
-        ag_step(b, R, n, S, s, k, dtype == 0 ? 4 : 2);
+        ag_step(b, R, n, S, s, k, dtype == 0 ? 4 : 2, 0, n);
     } else if (dtype == 0) {
-        rs_step_f32((float *const *)b, R, n, S, s, k);
+        rs_step_f32((float *const *)b, R, n, S, s, k, 0, n);
     } else if (dtype == 1) {
-        rs_step_bf16((uint16_t *const *)b, R, n, S, s, k);
+        rs_step_bf16((uint16_t *const *)b, R, n, S, s, k, 0, n);
     } else {
         if (part == NULL) return ORC_EINVAL;
-        rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k);
+        rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k, 0, n);
     }
     return ORC_OK;
 }
@@ -224,11 +231,34 @@ int orc_ring_allreduce(void *const *b, float *const *part, int R, int64_t n,
     int esize = dtype == 0 ? 4 : 2;
     for (int s = 0; s < S; s++) {
         for (int k = 0; k + 1 < R; k++) {
-            if (dtype == 0) rs_step_f32((float *const *)b, R, n, S, s, k);
-            else if (dtype == 1) rs_step_bf16((uint16_t *const *)b, R, n, S, s, k);
-            else rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k);
+            if (dtype == 0) rs_step_f32((float *const *)b, R, n, S, s, k, 0, n);
+            else if (dtype == 1) rs_step_bf16((uint16_t *const *)b, R, n, S, s, k, 0, n);
+            else rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k, 0, n);
         }
-        for (int k = 0; k + 1 < R; k++) ag_step(b, R, n, S, s, k, esize);
+        for (int k = 0; k + 1 < R; k++) ag_step(b, R, n, S, s, k, esize, 0, n);
+    }
+    return ORC_OK;
+}
+
+/* The same all-reduce on the elements of the window [wlo, whi) only: every
+ * hop, in the same order, restricted to those indices.  Each element's
+ * result depends only on that element of every rank, so running disjoint
+ * windows that cover [0, n) -- one after the other or on separate threads --
+ * leaves the buffers exactly as orc_ring_allreduce does. */
+int orc_ring_allreduce_range(void *const *b, float *const *part, int R, int64_t n,
+                             int S, int dtype, int64_t wlo, int64_t whi)
+{
+    if (R < 1 || S < 1 || n < 0 || dtype < 0 || dtype > 2) return ORC_EINVAL;
+    if (dtype == 2 && R > 1 && part == NULL) return ORC_EINVAL;
+    if (wlo < 0 || whi > n || wlo > whi) return ORC_EINVAL;
+    int esize = dtype == 0 ? 4 : 2;
+    for (int s = 0; s < S; s++) {
+        for (int k = 0; k + 1 < R; k++) {
+            if (dtype == 0) rs_step_f32((float *const *)b, R, n, S, s, k, wlo, whi);
+            else if (dtype == 1) rs_step_bf16((uint16_t *const *)b, R, n, S, s, k, wlo, whi);
+            else rs_step_bf16_p32((uint16_t *const *)b, part, R, n, S, s, k, wlo, whi);
+        }
+        for (int k = 0; k + 1 < R; k++) ag_step(b, R, n, S, s, k, esize, wlo, whi);
     }
     return ORC_OK;
 }

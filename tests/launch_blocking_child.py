@@ -35,7 +35,7 @@ def main(src, dst):
     send = [to_dev(x[: x.size // 8 * 8]) for x in xs]  # whole 16-byte vectors
     recv = [torch.zeros_like(t) for t in send]
     with ccr.Context(0, ccr.Config(staging_chunk_bytes=64 << 10, staging_slots=2)) as c:
-        ccr.ccr_sendrecv(c, send, recv)
+        ccr.ccr_sendrecv_batch(c, send, recv)
         torch.cuda.synchronize()
     for q, t in enumerate(recv):
         out[f"sendrecv_{q}"] = to_host(t)

@@ -32,7 +32,7 @@ def test_sendrecv_bytes(ccr_mod, mode, nbytes, chunk, slots, m):
                                            staging_slots=slots)) as c:
         s = [raw_to_dev(x) for x in srcs]
         r = [torch.zeros_like(x) for x in s]
-        ccr_mod.ccr_sendrecv(c, s, r)
+        ccr_mod.ccr_sendrecv_batch(c, s, r)
         torch.cuda.synchronize()
         dsts, _ = oracle.staged_copy(srcs, chunk, slots)
         for a, b in zip(r, dsts):
@@ -50,7 +50,7 @@ def test_sendrecv_full_pp_activations(ccr_mod, mode):
                                            staging_slots=w.slots)) as c:
         s = [to_dev(x) for x in mb]
         r = [torch.empty_like(x) for x in s]
-        ccr_mod.ccr_sendrecv(c, s, r)
+        ccr_mod.ccr_sendrecv_batch(c, s, r)
         torch.cuda.synchronize()
         for a, x in zip(r, mb):
             np.testing.assert_array_equal(to_host(a), x)
@@ -72,7 +72,7 @@ def test_alltoall_bytes(ccr_mod, mode, R, row_bytes):
     with ccr_mod.Context(0, cfg) as c:
         s = [raw_to_dev(x) if x.size else torch.zeros(16, dtype=torch.uint8, device="cuda") for x in sends]
         r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
-        ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
+        ccr_mod.ccr_alltoall_rows(c, s, r, counts, row_bytes)
         torch.cuda.synchronize()
         for a, b in zip(r, ref):
             assert to_host(a)[:b.size].tobytes() == b.tobytes()
@@ -154,7 +154,7 @@ def test_dma_deadline_paces_every_sdma_call(ccr_mod):
             # all-to-all: every segment once
             sd = [raw_to_dev(x) for x in sends]
             rv = [torch.zeros(x.size, dtype=torch.uint8, device="cuda") for x in a2a_ref]
-            ccr_mod.ccr_alltoall(c, sd, rv, counts, row)
+            ccr_mod.ccr_alltoall_rows(c, sd, rv, counts, row)
             torch.cuda.synchronize()
             assert ccr_mod.ccr_dma_rate(c)[1] == ccr_mod.ccr_dma_pace(int(counts.sum()) * row,
                                                                       deadline, gbs, E)
@@ -163,7 +163,7 @@ def test_dma_deadline_paces_every_sdma_call(ccr_mod):
             # staged send/recv: a fill and a drain per byte
             s = [raw_to_dev(x) for x in mbs]
             r = [torch.zeros_like(x) for x in s]
-            ccr_mod.ccr_sendrecv(c, s, r)
+            ccr_mod.ccr_sendrecv_batch(c, s, r)
             torch.cuda.synchronize()
             # staged: ccr_dma_pace's count until a staged job has shown its cost per
             # chunk step, then the fewest engines whose modelled time fits -- never fewer
@@ -194,7 +194,7 @@ def test_sdma_staged_slot_state_machine(ccr_mod, m, nbytes, chunk, slots, stripe
                                            dma_engines=engines)) as c:
         s = [raw_to_dev(x) for x in srcs]
         r = [torch.zeros_like(x) for x in s]
-        ccr_mod.ccr_sendrecv(c, s, r)
+        ccr_mod.ccr_sendrecv_batch(c, s, r)
         torch.cuda.synchronize()
         for a, b in zip(r, srcs):
             assert to_host(a).tobytes() == b.tobytes()
@@ -214,7 +214,7 @@ def test_sdma_staged_slot_state_machine(ccr_mod, m, nbytes, chunk, slots, stripe
 
 @pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
 def test_sdma_watchdog_reports_a_slow_operation(ccr_mod, sync):
-    """With the proxy holding the finish flag, a bounded wait on the stream
+    """With the proxy holding the release, a bounded wait on the stream
     times out; the stream is released afterwards and the result is exact."""
     import torch
     R, n = 4, 40000
@@ -241,15 +241,15 @@ def test_sendrecv_edges(ccr_mod, mode):
     say(f"sendrecv edges {mode}")
     with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, staging_chunk_bytes=4096,
                                            staging_slots=2, dma_stripe=7)) as c:
-        ccr_mod.ccr_sendrecv(c, [], [])
+        ccr_mod.ccr_sendrecv_batch(c, [], [])
         e = torch.zeros(0, dtype=torch.uint8, device="cuda")
-        ccr_mod.ccr_sendrecv(c, [e], [torch.zeros(0, dtype=torch.uint8, device="cuda")])
+        ccr_mod.ccr_sendrecv_batch(c, [e], [torch.zeros(0, dtype=torch.uint8, device="cuda")])
         for m, nbytes in ((9, 4096 * 2 + 16), (3, 48), (2, 16), (5, 4096 * 5 - 16)):
             rng = np.random.default_rng(m * 1000 + nbytes)
             srcs = [rng.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(m)]
             s = [raw_to_dev(x) for x in srcs]
             r = [torch.zeros_like(x) for x in s]
-            ccr_mod.ccr_sendrecv(c, s, r)
+            ccr_mod.ccr_sendrecv_batch(c, s, r)
             torch.cuda.synchronize()
             dsts, _ = oracle.staged_copy(srcs, 4096, 2)
             for a, b in zip(r, dsts):
@@ -272,7 +272,7 @@ def test_alltoall_skewed_flows(ccr_mod, mode, chunk):
     with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, dma_chunk_bytes=chunk)) as c:
         s = [raw_to_dev(x) for x in sends]
         r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
-        ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
+        ccr_mod.ccr_alltoall_rows(c, s, r, counts, row_bytes)
         torch.cuda.synchronize()
         for a, b in zip(r, ref):
             assert to_host(a)[:b.size].tobytes() == b.tobytes()
@@ -294,13 +294,13 @@ def test_alltoall_max_ranks_and_empty(ccr_mod, mode):
     with ccr_mod.Context(0, cfg) as c:
         s = [raw_to_dev(x) if x.size else torch.zeros(16, dtype=torch.uint8, device="cuda") for x in sends]
         r = [torch.zeros(max(16, x.size), dtype=torch.uint8, device="cuda") for x in ref]
-        ccr_mod.ccr_alltoall(c, s, r, counts, row_bytes)
+        ccr_mod.ccr_alltoall_rows(c, s, r, counts, row_bytes)
         torch.cuda.synchronize()
         for a, b in zip(r, ref):
             assert to_host(a)[:b.size].tobytes() == b.tobytes()
         zero = np.zeros((R, R), np.int64)
         keep = [to_host(x) for x in r[:3]]
-        ccr_mod.ccr_alltoall(c, s, r, zero, row_bytes)
+        ccr_mod.ccr_alltoall_rows(c, s, r, zero, row_bytes)
         torch.cuda.synchronize()
         for a, b in zip(r[:3], keep):
             assert to_host(a).tobytes() == b.tobytes()
@@ -316,11 +316,154 @@ def test_staging_allocation_failure_is_reported(ccr_mod):
     y = torch.zeros_like(x)
     with ccr_mod.Context(0, ccr_mod.Config(staging_chunk_bytes=1 << 42, staging_slots=2)) as c:
         with pytest.raises(ccr_mod.CcrError) as e:
-            ccr_mod.ccr_sendrecv(c, [x], [y])
+            ccr_mod.ccr_sendrecv_batch(c, [x], [y])
         assert e.value.status == ccr_mod.CCR_ERR_OOM, ccr_mod.ccr_last_error()
         torch.cuda.synchronize()
         assert not y.any()
         c.set_config(ccr_mod.Config())
-        ccr_mod.ccr_sendrecv(c, [x], [y])
+        ccr_mod.ccr_sendrecv_batch(c, [x], [y])
         torch.cuda.synchronize()
         assert torch.equal(x, y)
+
+
+# --------------------------------------------- the ring shift and element all-to-all
+@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+@pytest.mark.parametrize("R,count,dt", [(1, 8, "f32"), (2, 4096 * 3 + 8, "bf16"), (5, 100000, "f32"),
+                                        (8, 1 << 20, "bf16")])
+def test_sendrecv_ring_shift(ccr_mod, mode, R, count, dt):
+    """ccr_sendrecv: rank q receives rank q-1's buffer, through the staging
+    slots (1 MiB chunks, 3 slots), byte for byte as the oracle's ring shift."""
+    import torch
+    xs = workloads.random_buffers(R, count, dt, seed=R * 101 + count, dist="normal")
+    ref, _ = oracle.ring_sendrecv([x.view(np.uint8) for x in xs], 1 << 20, 3)
+    say(f"sendrecv ring shift {mode} R={R} count={count} {dt}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, staging_chunk_bytes=1 << 20,
+                                           staging_slots=3)) as c:
+        s = [to_dev(x) for x in xs]
+        r = [torch.zeros_like(x) for x in s]
+        ccr_mod.ccr_sendrecv(c, s, r)
+        torch.cuda.synchronize()
+        for q in range(R):
+            assert to_host(r[q]).view(np.uint8).tobytes() == ref[q].tobytes(), f"rank {q}"
+
+
+def test_sendrecv_ring_shift_rejects_bad_arguments(ccr_mod):
+    import torch
+    say("sendrecv ring shift: invalid arguments")
+    a = [torch.zeros(1000, device="cuda") for _ in range(3)]
+    b = [torch.zeros(1000, device="cuda") for _ in range(3)]
+    with ccr_mod.Context(0) as c:
+        lib = ccr_mod._lib
+        with pytest.raises(ccr_mod.CcrError) as e:  # 999 fp32: not whole 16-byte vectors
+            ccr_mod.ccr_sendrecv(c, [x[:999] for x in a], [x[:999] for x in b])
+        assert e.value.status == ccr_mod.CCR_ERR_INVALID_ARG and "16-byte" in ccr_mod.ccr_last_error()
+        with pytest.raises(ccr_mod.CcrError):  # a receive buffer that is also a send buffer
+            ccr_mod.ccr_sendrecv(c, a, [b[0], a[2], b[2]])
+        assert lib.ccr_sendrecv(c.handle, ccr_mod._ptrs(a), ccr_mod._ptrs(b), 0, 1000, 0, None) == \
+            ccr_mod.CCR_ERR_INVALID_ARG
+        assert lib.ccr_sendrecv(c.handle, ccr_mod._ptrs(a), ccr_mod._ptrs(b), 3, 1000, 7, None) == \
+            ccr_mod.CCR_ERR_INVALID_ARG
+        assert lib.ccr_sendrecv(c.handle, ccr_mod._ptrs(a), ccr_mod._ptrs(b), 3, 0, 0, None) == ccr_mod.CCR_OK
+
+
+def _compositions(rng, R, K):
+    """R rows of R non-negative integers, each row summing to K."""
+    return np.stack([rng.multinomial(K, rng.dirichlet(np.ones(R))) for _ in range(R)])
+
+
+@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+@pytest.mark.parametrize("R,dt,uniform", [(1, "f32", True), (3, "bf16", False), (8, "f32", True),
+                                          (8, "bf16", False), (16, "f32", False), (64, "bf16", True)])
+def test_alltoall_elements(ccr_mod, mode, R, dt, uniform):
+    """ccr_alltoall over (count, dtype): counts in elements or NULL for
+    count / R each; byte for byte as the oracle's all-to-all of one-element
+    rows."""
+    import torch
+    V, esize = (4, 4) if dt == "f32" else (8, 2)
+    rng = np.random.default_rng(R * 7 + (1 if uniform else 0))
+    if uniform:
+        count = R * V * 37
+        counts = np.full((R, R), count // R, np.int64)
+    else:
+        K = 41 * R
+        counts = _compositions(rng, R, K) * V
+        count = K * V
+        counts[R - 1, 0] = counts[R - 1, 0] + counts[R - 1, R - 1] if R > 1 else counts[0, 0]
+        if R > 1:
+            counts[R - 1, R - 1] = 0  # an empty segment
+    xs = workloads.random_buffers(R, count, dt, seed=R, dist="normal")
+    ref = oracle.alltoall([x.view(np.uint8) for x in xs], counts, esize)
+    say(f"alltoall elements {mode} R={R} {dt} uniform={uniform}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode)) as c:
+        s = [to_dev(x) for x in xs]
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        r = [torch.zeros(int(counts[:, d].sum()), dtype=tdt, device="cuda") for d in range(R)]
+        ccr_mod.ccr_alltoall(c, s, r, None if uniform else counts)
+        torch.cuda.synchronize()
+        for d in range(R):
+            assert to_host(r[d]).view(np.uint8).tobytes() == ref[d].tobytes(), f"rank {d}"
+        if R > 1:  # a ragged segment and a row that does not sum to count are refused
+            bad = counts.copy()
+            bad[0, 0] += 1
+            bad[0, 1] -= 1 if bad[0, 1] > 0 else 0
+            with pytest.raises(ccr_mod.CcrError):
+                ccr_mod.ccr_alltoall(c, s, r, bad)
+            bad = counts.copy()
+            bad[0, 0] += V
+            with pytest.raises(ccr_mod.CcrError) as e:
+                ccr_mod.ccr_alltoall(c, s, r, bad)
+            assert "not count" in ccr_mod.ccr_last_error()
+
+
+# ------------------------------------------------------- proxy shutdown
+@pytest.mark.parametrize("sync", ["host_func", "stream_flags"])
+def test_destroy_abandons_jobs_whose_stream_has_not_arrived(ccr_mod, monkeypatch, sync):
+    """A context destroyed while its SDMA job still waits behind a GPU sleep
+    on the caller's stream: after the (shortened) wait the job is abandoned,
+    ccr_ctx_destroy reports it, and the stream, reaching the job later, goes
+    on without it.  Every kernel here ends on its own (the sleep is bounded);
+    the condition is forced from the host."""
+    import time
+
+    import torch
+    R, n = 4, 40000
+    xs = workloads.random_buffers(R, n, "f32", seed=12, dist="normal")
+    say(f"destroy with a queued SDMA job, sync={sync}")
+    # calibrate the GPU sleep: about one second
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(10_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    # (about 5 ms at the GPU's clock; the factor is bounded, so the sleep
+    # lasts at most 400 times the calibration run)
+    cycles = int(10_000_000 * min(400.0, 1000.0 / max(1e-3, e0.elapsed_time(e1))))
+    s = torch.cuda.Stream()
+    ts = [to_dev(x) for x in xs]
+    c = ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma", dma_sync=sync))
+    ccr_mod.ccr_allreduce(c, ts)  # starts the proxy
+    torch.cuda.synchronize()
+    monkeypatch.setenv("CCR_DESTROY_TIMEOUT_MS", "100")
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(cycles)
+        ccr_mod.ccr_allreduce(c, ts, stream=s)
+    t0 = time.perf_counter()
+    st = ccr_mod._lib.ccr_ctx_destroy(c.handle)
+    c.handle = ctypes_null()
+    dt = time.perf_counter() - t0
+    assert st == ccr_mod.CCR_ERR_TIMEOUT and "abandoned" in ccr_mod.ccr_last_error(), ccr_mod.ccr_last_error()
+    assert dt < 0.9, dt
+    s.synchronize()  # the stream passes the abandoned job once the sleep ends
+    monkeypatch.delenv("CCR_DESTROY_TIMEOUT_MS")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode="sdma", dma_sync=sync)) as c2:  # the GPU works on
+        ts = [to_dev(x) for x in xs]
+        ccr_mod.ccr_allreduce(c2, ts)
+        torch.cuda.synchronize()
+        ref = oracle.ring_allreduce(xs)
+        for q, t in enumerate(ts):
+            np.testing.assert_array_equal(to_host(t), ref[q])
+
+
+def ctypes_null():
+    import ctypes
+    return ctypes.c_void_p()

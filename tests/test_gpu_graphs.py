@@ -34,8 +34,8 @@ def _replays(torch, g, reset, check, other):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("mode", [dict(), dict(slices=2), dict(cu_budget=64, overlap=True, slices=2)],
-                         ids=["default", "slices2", "budget-overlap"])
+@pytest.mark.parametrize("mode", [dict(), dict(slices=2), dict(overlap=True, slices=2)],
+                         ids=["default", "slices2", "overlap"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_captured_allreduce_replays(ccr_mod, mode, dt):
     import torch
@@ -94,7 +94,7 @@ def test_captured_alltoall_permute_topk_replays(ccr_mod):
         d_src = torch.from_numpy(src_rows).cuda()
         d_idx = torch.from_numpy(idx).cuda()
         d_dst = torch.zeros(nrows, 32, dtype=torch.uint8, device="cuda")
-        calls = lambda: (ccr_mod.ccr_alltoall(c, s_d, r_d, counts, row),  # noqa: E731
+        calls = lambda: (ccr_mod.ccr_alltoall_rows(c, s_d, r_d, counts, row),  # noqa: E731
                          ccr_mod.ccr_moe_topk(c, d_logits, d_topk),
                          ccr_mod.ccr_permute_rows(c, d_dst, d_src, d_idx))
         calls()
@@ -127,9 +127,13 @@ def test_calls_that_cannot_replay_are_refused(ccr_mod):
              ("fp32-partials all-reduce", dict(bf16_acc="fp32_partials"),
               lambda c, b, m: ccr_mod.ccr_allreduce(c, b)),
              ("staged send/recv", dict(),
-              lambda c, b, m: ccr_mod.ccr_sendrecv(c, b[:2], b[2:])),
+              lambda c, b, m: ccr_mod.ccr_sendrecv_batch(c, b[:2], b[2:])),
              ("sdma all-to-all", dict(copy_mode="sdma"),
-              lambda c, b, m: ccr_mod.ccr_alltoall(c, m[0], m[1], np.ones((R, R), np.int64), 16))]
+              lambda c, b, m: ccr_mod.ccr_alltoall_rows(c, m[0], m[1], np.ones((R, R), np.int64), 16)),
+             ("all-reduce with a CU budget", dict(cu_budget=64),
+              lambda c, b, m: ccr_mod.ccr_allreduce(c, b)),
+             ("all-to-all with a CU budget", dict(cu_budget=32),
+              lambda c, b, m: ccr_mod.ccr_alltoall_rows(c, m[0], m[1], np.ones((R, R), np.int64), 16))]
     for name, cfg, call in cases:
         say(f"graph refusal: {name}")
         with ccr_mod.Context(0, ccr_mod.Config(**cfg)) as c:

@@ -69,7 +69,7 @@ def test_staging_and_alltoall_guards(ccr_mod, mode):
         src = [guarded(nbytes, torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).cuda())
                for _ in range(3)]
         dst = [guarded(nbytes) for _ in range(3)]
-        ccr_mod.ccr_sendrecv(c, [b for _, b in src], [b for _, b in dst])
+        ccr_mod.ccr_sendrecv_batch(c, [b for _, b in src], [b for _, b in dst])
         torch.cuda.synchronize()
         for (w, b), (_, s) in zip(dst, src):
             assert intact(w, nbytes) and torch.equal(b, s)
@@ -79,7 +79,7 @@ def test_staging_and_alltoall_guards(ccr_mod, mode):
         rsizes = [int(counts[:, d].sum()) * row for d in range(R)]
         send = [guarded(sz, torch.from_numpy(rng.integers(0, 256, sz, dtype=np.uint8)).cuda()) for sz in sizes]
         recv = [guarded(sz) for sz in rsizes]
-        ccr_mod.ccr_alltoall(c, [b for _, b in send], [b for _, b in recv], counts, row)
+        ccr_mod.ccr_alltoall_rows(c, [b for _, b in send], [b for _, b in recv], counts, row)
         torch.cuda.synchronize()
         for (w, _), sz in zip(recv + send, rsizes + sizes):
             assert intact(w, sz)

@@ -333,3 +333,64 @@ def test_full_size_workloads(ccr_mod, w, how):
         err32 = np.max(np.abs(oracle.bf16_to_f32(ref32) - exact)) / np.max(np.abs(exact))
         say(f"{w.name}: fp32 partials normalised max error vs fp64 = {err32:.4f}")
         assert err32 <= err
+
+
+# SDMA all-gathers at the gradient bucket's full size, in the settings the
+# benchmark times under its GEMM load: every engine with least-loaded link
+# placement, engine caps (8 and 2), and deadline pacing.
+SDMA_FULL = [dict(copy_mode="sdma"), dict(copy_mode="sdma", dma_engines=8),
+             dict(copy_mode="sdma", dma_engines=2), dict(copy_mode="sdma", dma_deadline_us=3000)]
+
+
+@pytest.fixture(scope="module")
+def bucket_inputs():
+    w = workloads.DP_BUCKET_BF16
+    say(f"full-size {w.name}: generating inputs and the oracle's fold")
+    xs = workloads.ring_inputs(w)
+    return xs, oracle.fold(xs)
+
+
+@pytest.mark.parametrize("cfg", SDMA_FULL, ids=lambda c: "-".join(f"{k}={v}" for k, v in c.items()))
+def test_full_size_bucket_with_sdma_all_gather(ccr_mod, bucket_inputs, cfg):
+    """8 ranks x 25 Mi bf16: every element of every rank equals the oracle's
+    fold, with the all-gather on the SDMA engines (links of up to 8 MiB cut
+    into sub-chains and placed on the least-loaded engine as they become
+    ready)."""
+    import torch
+    xs, ref = bucket_inputs
+    w = workloads.DP_BUCKET_BF16
+    say(f"full-size {w.name} with {cfg}")
+    with ccr_mod.Context(0, ccr_mod.Config(slices=w.slices, **cfg)) as c:
+        ts = [to_dev(x) for x in xs]
+        ccr_mod.ccr_allreduce(c, ts)
+        torch.cuda.synchronize()
+        used = ccr_mod.ccr_dma_rate(c)[1]
+        for q, t in enumerate(ts):
+            g = to_host(t)
+            if g.tobytes() != ref.tobytes():
+                bad = np.nonzero(g != ref)[0]
+                raise AssertionError(f"{cfg}: rank {q} differs at {bad.size} elements, first {bad[:5]}")
+    if "dma_engines" in cfg:
+        assert used <= cfg["dma_engines"]
+
+
+def test_full_size_rs_then_sdma_all_gather_r32(ccr_mod):
+    """32 ranks x 8 Mi fp32 (1 GiB): the reduce-scatter call, then the
+    all-gather call with SDMA copies; every element equals the oracle's fold."""
+    import torch
+    w = workloads.RS_AG_R32_F32
+    say(f"full-size {w.name}: generating inputs")
+    xs = workloads.ring_inputs(w)
+    ref = oracle.fold(xs)
+    say(f"full-size {w.name}: reduce-scatter, then SDMA all-gather (S={w.slices})")
+    with ccr_mod.Context(0, ccr_mod.Config(slices=w.slices, copy_mode="sdma")) as c:
+        ts = [to_dev(x) for x in xs]
+        del xs
+        ccr_mod.ccr_reduce_scatter(c, ts)
+        ccr_mod.ccr_all_gather(c, ts)
+        torch.cuda.synchronize()
+        for q, t in enumerate(ts):
+            g = to_host(t)
+            if g.tobytes() != ref.tobytes():
+                bad = np.nonzero(g != ref)[0]
+                raise AssertionError(f"rank {q} differs at {bad.size} elements, first {bad[:5]}")

@@ -94,3 +94,66 @@ def test_two_contexts_on_two_streams(ccr_mod, modes):
     finally:
         for c in ctxs:
             c.close()
+
+
+def _kfd_queues():
+    """Hardware queues the kernel driver lists for this process, or None
+    where its per-process sysfs directory cannot be read."""
+    import os
+    d = f"/sys/class/kfd/kfd/proc/{os.getpid()}/queues"
+    try:
+        return len(os.listdir(d))
+    except OSError:
+        return None
+
+
+def test_contexts_hold_no_hardware_queue_until_a_call_needs_one(ccr_mod):
+    """Ten contexts making kernel-copy calls that need no second stream hold
+    no side stream (and, where the driver lists the process's hardware
+    queues, add none); a CU budget makes the budgeted stream with the
+    context; an overlapped all-gather or an SDMA one over several slices
+    makes the second stream on its first call; the graph cache captures on a
+    plain stream.  Results stay those of the oracle."""
+    import torch
+    R, n = 8, 65536 + 8
+    xs = workloads.random_buffers(R, n, "f32", seed=21, dist="normal")
+    ref = oracle.ring_allreduce(xs, S=1)
+    say("side streams are made on demand")
+    ts = [to_dev(x) for x in xs]
+    torch.cuda.synchronize()
+    q0 = _kfd_queues()
+    ctxs = [ccr_mod.Context(0, ccr_mod.Config(graph_cache=False)) for _ in range(10)]
+    try:
+        for c in ctxs:
+            for t, x in zip(ts, xs):
+                t.copy_(to_dev(x))
+            ccr_mod.ccr_allreduce(c, ts)
+            ccr_mod.ccr_sendrecv_batch(c, ts[:2], ts[2:4])
+            torch.cuda.synchronize()
+            assert ccr_mod.ccr_ctx_streams(c) == (0, 0)
+        q1 = _kfd_queues()
+        if q0 is not None and q1 is not None:
+            assert q1 == q0, (q0, q1)
+    finally:
+        for c in ctxs:
+            c.close()
+    cases = [(dict(cu_budget=16), (1, 0), (1, 0)), (dict(overlap=True, slices=2), (0, 0), (1, 0)),
+             (dict(copy_mode="sdma", slices=2), (0, 0), (1, 0)), (dict(copy_mode="sdma"), (0, 0), (0, 0)),
+             (dict(cu_budget=16, overlap=True, slices=2), (1, 0), (2, 0))]
+    for cfg, at_create, after_call in cases:
+        with ccr_mod.Context(0, ccr_mod.Config(graph_cache=False, **cfg)) as c:
+            assert ccr_mod.ccr_ctx_streams(c) == at_create, cfg
+            for t, x in zip(ts, xs):
+                t.copy_(to_dev(x))
+            ccr_mod.ccr_allreduce(c, ts)
+            torch.cuda.synchronize()
+            assert ccr_mod.ccr_ctx_streams(c) == after_call, cfg
+            for q, t in enumerate(ts):
+                assert to_host(t).tobytes() == ref[q].tobytes(), f"{cfg} rank {q}"
+    small = [to_dev(x[:4096]) for x in xs]
+    with ccr_mod.Context(0) as c:  # graph cache: captured on the second call
+        for _ in range(3):
+            ccr_mod.ccr_allreduce(c, small)
+        torch.cuda.synchronize()
+        assert ccr_mod.ccr_ctx_streams(c) == (0, 1)
+        assert ccr_mod.ccr_graph_cache_stats(c)[1] >= 1

@@ -93,3 +93,19 @@ def test_staging_workload_shape():
     mb = workloads.staging_inputs(w, rows=8)
     assert len(mb) == 4 and mb[0].shape == (8, 4096) and mb[0].dtype == np.uint16
     assert w.rows * w.cols * 2 == 16 << 20 and w.chunk_bytes == 4 << 20
+
+
+@pytest.mark.parametrize("R,nbytes,chunk,slots", [(1, 64, 16, 2), (2, 4096 * 3, 4096, 2),
+                                                  (5, 1000, 96, 3), (8, 48, 4096, 2)])
+def test_ring_sendrecv_shifts_each_rank_to_its_successor(R, nbytes, chunk, slots):
+    """Rank q receives exactly what rank q-1 sent (tagged bytes name the
+    sender), through the same slot discipline as the directed transfers:
+    transfer r's chunks come r-th in the slot sequence."""
+    sends = [np.full(nbytes, (r * 37 + 11) % 256, np.uint8) for r in range(R)]
+    recvs, ev = oracle.ring_sendrecv(sends, chunk, slots)
+    for q in range(R):
+        assert recvs[q].tobytes() == bytes([((q - 1) % R * 37 + 11) % 256]) * nbytes
+    per = -(-nbytes // chunk)
+    fills = [int(ch) for ch, sl, st in ev if st == 1]
+    assert fills == list(range(R * per))
+    assert all(sl == ch % slots for ch, sl, _ in ev)

@@ -268,3 +268,31 @@ def test_bf16_rounding_matches_torch_cast():
     np.testing.assert_array_equal(got, ref)
     # widening is exact: bf16 -> f32 -> bf16 is the identity
     np.testing.assert_array_equal(oracle.f32_to_bf16(oracle.bf16_to_f32(ref)), ref)
+
+
+@pytest.mark.parametrize("dt,acc", [("f32", "per_hop"), ("bf16", "per_hop"), ("bf16", "fp32_partials")])
+@pytest.mark.parametrize("R,n,S", [(1, 50, 1), (2, 1001, 2), (5, 40013, 3), (8, 65536 + 9, 1)])
+def test_range_entry_point_equals_the_unsplit_oracle(dt, acc, R, n, S):
+    """Running the all-reduce over disjoint element windows that cover the
+    buffers -- at cut points that fall inside chunks, slices and 16-byte
+    vectors, with empty windows among them, sequentially and on threads --
+    leaves every buffer bit for bit as the unsplit oracle does."""
+    if dt == "f32" and acc != "per_hop":
+        pytest.skip("fp32 has one accumulation mode")
+    xs = workloads.random_buffers(R, n, dt, seed=R * 13 + n, dist="normal", scale=1.0)
+    ref = oracle.ring_allreduce(xs, S=S, bf16_acc=acc)
+    rng = np.random.default_rng(n)
+    cuts = np.unique(np.concatenate([[0, n, n // 3, n // 3], rng.integers(0, n + 1, 6)]))
+    cuts = np.concatenate([cuts, [n]])  # an empty last window
+    bufs = [x.copy() for x in xs]
+    part = [np.zeros(n, np.float32) for _ in range(R)] if acc == "fp32_partials" else None
+    order = rng.permutation(len(cuts) - 1)
+    for i in order:  # windows in a shuffled order
+        oracle.ring_allreduce_range(bufs, int(cuts[i]), int(cuts[i + 1]), S, acc, part)
+    for q in range(R):
+        assert bufs[q].tobytes() == ref[q].tobytes(), f"rank {q}"
+    got = oracle.ring_allreduce_threads(xs, 5, S=S, bf16_acc=acc)
+    for q in range(R):
+        assert got[q].tobytes() == ref[q].tobytes(), f"threads, rank {q}"
+    with pytest.raises(ValueError):
+        oracle.ring_allreduce_range([x.copy() for x in xs], 0, n + 1, S, acc, part)
