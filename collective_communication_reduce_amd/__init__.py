@@ -75,6 +75,7 @@ _SIGNATURES = {
     "ccr_all_gather": [_vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_sendrecv": [_vp, _vp, _vp, _i32, _i64, _i32, _vp],
     "ccr_sendrecv_batch": [_vp, _vp, _vp, _i32, _i64, _vp],
+    "ccr_sendrecv_batch_noalloc": [_vp, _vp, _vp, _i32, _i64, _vp],
     "ccr_alltoall": [_vp, _vp, _vp, _i32, _i64, _vp, _i32, _vp],
     "ccr_alltoall_rows": [_vp, _vp, _vp, _i32, _vp, _i64, _vp],
     "ccr_permute_rows": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp],
@@ -370,6 +371,18 @@ def ccr_sendrecv_batch(ctx: Context, send: Sequence, recv: Sequence, stream=None
         raise ValueError("every transfer moves the same number of bytes")
     _check(_lib.ccr_sendrecv_batch(ctx.handle, _ptrs(send), _ptrs(recv), len(send), nbytes,
                                    _stream(stream)))
+
+
+def ccr_sendrecv_batch_noalloc(ctx: Context, send: Sequence, recv: Sequence, stream=None):
+    """ccr_sendrecv_batch staged through the GPU's fixed 16 MiB scratch: no
+    allocation (kernel copies; slots x chunk <= 16 MiB)."""
+    if len(send) != len(recv):
+        raise ValueError("send and recv need the same number of transfers")
+    nbytes = send[0].numel() * send[0].element_size() if send else 0
+    if any(t.numel() * t.element_size() != nbytes for t in list(send) + list(recv)):
+        raise ValueError("every transfer moves the same number of bytes")
+    _check(_lib.ccr_sendrecv_batch_noalloc(ctx.handle, _ptrs(send), _ptrs(recv), len(send), nbytes,
+                                           _stream(stream)))
 
 
 def ccr_alltoall(ctx: Context, send: Sequence, recv: Sequence, counts=None, stream=None):

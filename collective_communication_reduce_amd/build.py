@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libccr.so")
-SOURCES = ["ccr_api.cpp", "ccr_dma.cpp", "ccr_schedule.cpp", "ccr_kernels.hip", "ccr_moe_kernels.hip"]
+SOURCES = ["ccr_api.cpp", "ccr_dma.cpp", "ccr_schedule.cpp", "ccr_kernels.hip", "ccr_moe_kernels.hip",
+           "ccr_scratch.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 arithmetic;

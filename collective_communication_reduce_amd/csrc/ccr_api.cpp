@@ -154,6 +154,7 @@ struct ccr_ctx {
   };
   std::vector<Timed> timed;
   std::vector<hipEvent_t> timing_pool;
+  std::string scratch_error;  // why the fixed scratch's address could not be resolved
 };
 
 namespace {
@@ -1102,6 +1103,15 @@ ccr_status_t ccr_ctx_create(int device, const ccr_config_t* cfg, ccr_ctx_t* out)
   hipError_t e = hipDeviceGetAttribute(&ctx->num_cus, hipDeviceAttributeMultiprocessorCount, device);
   ccr_status_t st = e == hipSuccess ? make_streams(ctx) : hip_fail(e, "hipDeviceGetAttribute");
   if (st == CCR_OK) st = events(ctx, 8);
+  if (st == CCR_OK) {
+    // the device's fixed scratch (the no-allocation entry points): resolved
+    // here, with the device current, once per device
+    const hipError_t se = resolve_scratch(device);
+    if (se != hipSuccess) {
+      (void)hipGetLastError();
+      ctx->scratch_error = std::string("hipGetSymbolAddress: ") + hipGetErrorString(se);
+    }
+  }
   if (st != CCR_OK) {
     std::string msg = g_last_error;
     ccr_ctx_destroy(ctx);
@@ -1263,10 +1273,12 @@ ccr_status_t ccr_all_gather(ccr_ctx_t ctx, void* const* bufs, int R, int64_t cou
 namespace {
 
 // Transfers m = 0..n-1, each nbytes from send[m] to recv[m], in order,
-// through the context's staging slots (the batch and ring-shift forms of
-// the staged send/recv).
+// through staging slots (the batch and ring-shift forms of the staged
+// send/recv).  fixed_slots: NULL = the context's staging slots (allocated
+// on demand); otherwise slots in memory the caller guarantees is large
+// enough, used with kernel copies only and with nothing allocated.
 ccr_status_t run_sendrecv(ccr_ctx* ctx, const void* const* send, void* const* recv, int n,
-                          int64_t nbytes, hipStream_t caller) {
+                          int64_t nbytes, hipStream_t caller, char* fixed_slots = nullptr) {
   CCR_TRY(check_ctx(ctx));
   if (n < 0 || nbytes < 0) return fail(CCR_ERR_INVALID_ARG, "n or nbytes < 0");
   if (nbytes % 16 != 0) return fail(CCR_ERR_INVALID_ARG, "%lld bytes per transfer is not a multiple of 16", (long long)nbytes);
@@ -1282,9 +1294,12 @@ ccr_status_t run_sendrecv(ccr_ctx* ctx, const void* const* send, void* const* re
   }
   CCR_TRY(check_disjoint(ranges, "send/recv"));
   ctx->footprint = 2 * (int64_t)n * nbytes + ctx->cfg.staging_chunk_bytes * ctx->cfg.staging_slots;
-  CCR_TRY(refuse_capture(caller, "a staged send/recv (context staging slots)"));
-  CCR_TRY(ensure_staging(ctx));
-  if (ctx->cfg.copy_mode == CCR_COPY_SDMA) {
+  if (!fixed_slots) {
+    CCR_TRY(refuse_capture(caller, "a staged send/recv (context staging slots)"));
+    CCR_TRY(ensure_staging(ctx));
+  }
+  char* const slots_mem = fixed_slots ? fixed_slots : ctx->staging;
+  if (ctx->cfg.copy_mode == CCR_COPY_SDMA && !fixed_slots) {
     // One DMA job: the proxy runs the slot state machine itself, each fill
     // and drain striped over several engines.
     CCR_TRY(ensure_dma(ctx));
@@ -1335,7 +1350,7 @@ ccr_status_t run_sendrecv(ccr_ctx* ctx, const void* const* send, void* const* re
     copies.clear();
     for (int p = 0; p < P; p++) {
       const int64_t a = (r - 1) * P + p, b = r * P + p;  // chunk drained, chunk filled
-      char* slot = ctx->staging + (int64_t)p * C;
+      char* slot = slots_mem + (int64_t)p * C;
       const bool drain = r >= 1 && a < T, fill = r < rounds && b < T;
       char* to = drain ? chunk_dst(a) : nullptr;
       const char* from = fill ? chunk_src(b) : nullptr;
@@ -1347,9 +1362,19 @@ ccr_status_t run_sendrecv(ccr_ctx* ctx, const void* const* send, void* const* re
     }
     for (size_t i = 0; i < fused.size(); i += kMaxPieces) {
       const int m = (int)std::min<size_t>(kMaxPieces, fused.size() - i);
-      CCR_TRY(launch_timed(ctx, HopKind::kDrainFill, fused.data() + i, m, s));
+      if (fixed_slots)  // no timing events: they would be created on demand
+        HIP_TRY(launch_pieces(HopKind::kDrainFill, fused.data() + i, m, call_tuning(ctx), s));
+      else
+        CCR_TRY(launch_timed(ctx, HopKind::kDrainFill, fused.data() + i, m, s));
     }
-    CCR_TRY(copy_pieces(ctx, copies.data(), copies.size(), s));
+    if (fixed_slots) {
+      for (size_t i = 0; i < copies.size(); i += kMaxPieces) {
+        const int m = (int)std::min<size_t>(kMaxPieces, copies.size() - i);
+        HIP_TRY(launch_pieces(HopKind::kCopy, copies.data() + i, m, call_tuning(ctx), s));
+      }
+    } else {
+      CCR_TRY(copy_pieces(ctx, copies.data(), copies.size(), s));
+    }
   }
   CCR_TRY(order_after(ctx, 1, s, caller));
   return CCR_OK;
@@ -1427,6 +1452,25 @@ ccr_status_t ccr_sendrecv_batch(ccr_ctx_t ctx, const void* const* send, void* co
                                 int64_t nbytes, void* stream) {
   CCR_MARK("ccr_sendrecv_batch");
   return run_sendrecv(ctx, send, recv, n, nbytes, static_cast<hipStream_t>(stream));
+}
+
+ccr_status_t ccr_sendrecv_batch_noalloc(ccr_ctx_t ctx, const void* const* send, void* const* recv,
+                                        int n, int64_t nbytes, void* stream) {
+  CCR_MARK("ccr_sendrecv_batch_noalloc");
+  CCR_TRY(check_ctx(ctx));
+  const int64_t need = ctx->cfg.staging_chunk_bytes * ctx->cfg.staging_slots;
+  if (need > kScratchBytes)
+    return fail(CCR_ERR_INVALID_ARG,
+                "staging_slots x staging_chunk_bytes = %lld bytes exceeds the %lld bytes of fixed "
+                "scratch this entry point stages through", (long long)need, (long long)kScratchBytes);
+  if (ctx->cfg.copy_mode != CCR_COPY_KERNEL)
+    return fail(CCR_ERR_UNSUPPORTED, "the no-allocation send/recv runs on kernel copies only "
+                                     "(the SDMA proxy allocates when it starts)");
+  char* slots = scratch_address(ctx->device);
+  if (!slots)
+    return fail(CCR_ERR_HIP, "the device address of the fixed scratch was not resolved (%s)",
+                ctx->scratch_error.c_str());
+  return run_sendrecv(ctx, send, recv, n, nbytes, static_cast<hipStream_t>(stream), slots);
 }
 
 ccr_status_t ccr_alltoall(ccr_ctx_t ctx, const void* const* send, void* const* recv, int R,

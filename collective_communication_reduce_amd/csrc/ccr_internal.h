@@ -115,5 +115,12 @@ hipError_t launch_moe_plan(const int32_t* topk, int64_t T, int E, int K, int elo
 // One wave64 workgroup per block; writes (XCC id, SE id, CU id) per block.
 hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream);
 
+// Fixed device scratch of the entry points that allocate nothing: one
+// array of kScratchBytes per GPU, held until the process ends (its device
+// address is resolved once per device, with that device current, by
+// resolve_scratch; scratch_address returns it, or NULL before that).
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+hipError_t resolve_scratch(int device);
+char* scratch_address(int device);
 
 }  // namespace ccr

@@ -356,6 +356,21 @@ ccr_status_t ccr_sendrecv(ccr_ctx_t ctx, const void *const *send, void *const *r
                           int64_t count, int dtype, void *stream);
 ccr_status_t ccr_sendrecv_batch(ccr_ctx_t ctx, const void *const *send, void *const *recv, int n,
                                 int64_t nbytes, void *stream);
+/* ccr_sendrecv_batch for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * transfers, arguments, order and errors, but the staging slots live in a
+ * fixed device array of 16 MiB per GPU that the library holds from its
+ * first context on that GPU until the process ends, so the call allocates
+ * no device or pinned memory and creates no stream or event.  Limits:
+ * staging_slots x staging_chunk_bytes <= 16 MiB (CCR_ERR_INVALID_ARG
+ * otherwise); kernel copies only (CCR_ERR_UNSUPPORTED with copy_mode SDMA,
+ * whose proxy allocates when it starts).  It may be captured into a graph.
+ * Every call on one GPU, from any context, shares that GPU's array: calls
+ * that can overlap on the GPU (different streams with nothing ordering
+ * them) race on it.  The array keeps the last call's contents; no call
+ * needs it cleared. */
+ccr_status_t ccr_sendrecv_batch_noalloc(ccr_ctx_t ctx, const void *const *send,
+                                        void *const *recv, int n, int64_t nbytes, void *stream);
 
 /* ----------------------------------------------------------------------
  * All-to-all over R ranks (HOCCL §6.2, Fig. 8c-d All-to-All; §2.1: the
