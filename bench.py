@@ -114,7 +114,100 @@ def contention_rate(intervals, window_ms, n_cu):
     return held / (n_cu * window_ms)
 
 
-PAIRS = 9  # interleaved GEMM-alone / loaded window pairs per overlap configuration
+PAIRS = 15  # interleaved GEMM-alone / loaded window pairs per overlap configuration
+
+
+def ci95(xs):
+    """(mean, lower, upper) of the two-sided 95% t-interval of the mean."""
+    a = np.asarray(xs, dtype=np.float64)
+    n = a.size
+    m = float(a.mean()) if n else float("nan")
+    if n < 2:
+        return m, m, m
+    try:
+        from scipy.stats import t as student_t
+        q = float(student_t.ppf(0.975, n - 1))
+    except ImportError:  # normal approximation
+        q = 1.96
+    h = q * float(a.std(ddof=1)) / np.sqrt(n)
+    return m, m - h, m + h
+
+
+def diff_ci95(a, b):
+    """(mean, lower, upper) of mean(a) - mean(b), Welch's 95% interval."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    d = float(a.mean() - b.mean())
+    va, vb = a.var(ddof=1) / a.size, b.var(ddof=1) / b.size
+    se = float(np.sqrt(va + vb))
+    if se == 0.0:
+        return d, d, d
+    df = (va + vb) ** 2 / (va ** 2 / (a.size - 1) + vb ** 2 / (b.size - 1))
+    try:
+        from scipy.stats import t as student_t
+        q = float(student_t.ppf(0.975, df))
+    except ImportError:
+        q = 1.96
+    return d, d - q * se, d + q * se
+
+
+def run_label(r):
+    """Short name of an overlap run: copy mode, CU budget, SDMA engines."""
+    if r["copy_mode"] == "kernel":
+        return f"kernel/B{r['cu_budget']}"
+    tail = "deadline" if "dma_deadline" in r else (f"E{r['dma_engines']}" if r["dma_engines"] != "all" else "Eall")
+    if r.get("dma_sync") == "stream_flags":
+        tail += "/flags"
+    return f"sdma/B{r['cu_budget']}/{tail}"
+
+
+def pareto(points):
+    """Labels of the points no other point beats on both axes (collective
+    time under load, GEMM slowdown: lower is better on each), by time."""
+    out = []
+    for lab, t, sd in points:
+        if not any((t2 <= t and s2 <= sd) and (t2 < t or s2 < sd) for _, t2, s2 in points):
+            out.append((t, lab))
+    return [lab for _, lab in sorted(out)]
+
+
+def sdma_verdict(runs):
+    """Kernel copies against SDMA copies under a concurrent GEMM, from the
+    per-pair slowdowns of each overlap run (host-function gates only):
+    - equal budget: at each CU budget B both modes were run at, SDMA on all
+      engines minus kernel copies, with Welch's 95% interval;
+    - matched time: each SDMA run against the kernel run whose collectives
+      took the nearest time under load;
+    - the Pareto set over (collective time under load, GEMM slowdown)."""
+    rs = [r for r in runs if r.get("dma_sync") in (None, "host_func")]
+    kern = {r["cu_budget"]: r for r in rs if r["copy_mode"] == "kernel"}
+    sdma_all = {r["cu_budget"]: r for r in rs if r["copy_mode"] == "sdma" and r["dma_engines"] == "all"
+                and "dma_deadline" not in r}
+    equal = []
+    for B in sorted(set(kern) & set(sdma_all), reverse=True):
+        d, lo, hi = diff_ci95(sdma_all[B]["pairs_pct"], kern[B]["pairs_pct"])
+        equal.append({"cu_budget": B, "kernel_pct": round(kern[B]["slowdown_mean_pct"], 2),
+                      "sdma_pct": round(sdma_all[B]["slowdown_mean_pct"], 2),
+                      "sdma_minus_kernel_pp": [round(d, 2), round(lo, 2), round(hi, 2)],
+                      "sdma_lower": bool(hi < 0), "sdma_higher": bool(lo > 0)})
+    matched = []
+    for r in rs:
+        if r["copy_mode"] != "sdma" or r["cu_budget"] != 256:
+            continue
+        k = min(kern.values(), key=lambda x: abs(x["collectives_under_load_ms"] - r["collectives_under_load_ms"]))
+        d, lo, hi = diff_ci95(r["pairs_pct"], k["pairs_pct"])
+        matched.append({"sdma": run_label(r), "kernel": run_label(k),
+                        "coll_ms": [round(r["collectives_under_load_ms"], 2),
+                                    round(k["collectives_under_load_ms"], 2)],
+                        "slowdown_pct": [round(r["slowdown_mean_pct"], 2), round(k["slowdown_mean_pct"], 2)],
+                        "sdma_minus_kernel_pp": [round(d, 2), round(lo, 2), round(hi, 2)],
+                        "sdma_lower": bool(hi < 0)})
+    front = pareto([(run_label(r), r["collectives_under_load_ms"], r["slowdown_mean_pct"]) for r in rs])
+    full = next((e for e in equal if e["cu_budget"] == 256), None)
+    return {"equal_budget": equal, "matched_time": matched, "pareto": front,
+            "target_sdma_lower_at_full_cus": None if full is None else full["sdma_lower"],
+            "sdma_lower_at_some_matched_time": any(m["sdma_lower"] for m in matched),
+            "sdma_on_pareto": [lab for lab in front if lab.startswith("sdma")]}
 
 
 def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
@@ -202,27 +295,110 @@ def overlap_runs(ccr, collective, runs, gemm_dims, n_gemm, n_coll):
                 b_runs.append(window(ctx))
             alone_i = sorted(a_ms)[PAIRS // 2]
             gemm, coll, span = sorted(b_runs)[PAIRS // 2]
+            # paired slowdowns: each loaded window against the alone window just before it
+            pairs_pct = [100.0 * (b[0] / a - 1.0) for a, b in zip(a_ms, b_runs)]
+            mean, lo, hi = ci95(pairs_pct)
+            coll_ms = sorted(b[1] for b in b_runs)[PAIRS // 2]
             i_coll = contention(ctx)
             paced = None
             if conf["copy_mode"] == "sdma" and conf.get("dma_deadline_us"):
                 gbs, used = ccr.ccr_dma_rate(ctx)
                 paced = {"deadline_us": conf["dma_deadline_us"], "engine_gbs": round(gbs, 1),
                          "engines_used": used}
-            out["runs"].append({
+            run = {
                 "copy_mode": conf["copy_mode"], "cu_budget": conf.get("cu_budget", 0) or 256,
                 "dma_sync": conf.get("dma_sync", "host_func") if conf["copy_mode"] == "sdma" else None,
                 "dma_engines": (conf.get("dma_engines", 0) or "all") if conf["copy_mode"] == "sdma" else None,
                 "gemm_alone_ms": round(alone_i, 3),
                 "gemm_ms": round(gemm, 3), "slowdown_pct": round(100.0 * (gemm / alone_i - 1.0), 2),
-                "slowdown_pct_spread": [round(100.0 * (min(r[0] for r in b_runs) / alone_i - 1.0), 2),
-                                        round(100.0 * (max(r[0] for r in b_runs) / alone_i - 1.0), 2)],
+                "slowdown_mean_pct": round(mean, 3), "slowdown_ci95_pct": [round(lo, 3), round(hi, 3)],
+                "pairs_pct": [round(x, 3) for x in pairs_pct],
+                "slowdown_pct_spread": [round(min(pairs_pct), 2), round(max(pairs_pct), 2)],
                 "collective_alone_ms": round(t1 * 1e3, 4),
-                "collectives_under_load_ms": round(coll, 3),
+                "collectives_under_load_ms": round(coll_ms, 3),
                 "makespan_ms": round(span, 3),
                 "makespan_over_gemm_alone_pct": round(100.0 * (span / alone_i - 1.0), 2),
                 "contention_rate": round(i_coll, 4),
-                **({"dma_deadline": paced} if paced else {})})
+                **({"dma_deadline": paced} if paced else {})}
+            run["label"] = run_label(run)
+            log(f"  {run['label']}: slowdown {mean:.2f}% [{lo:.2f}, {hi:.2f}], "
+                f"collectives {coll_ms:.2f} ms under load")
+            out["runs"].append(run)
+    out["verdict"] = sdma_verdict(out["runs"])
     return out
+
+
+def compact_verdict(o):
+    """A few hundred characters of an overlap run's verdict: kernel against
+    SDMA at full CUs (GEMM slowdown %, mean over the pairs, and the SDMA
+    minus kernel difference with its 95% interval), each SDMA run against
+    the kernel run of the nearest collective time under load, and the
+    Pareto set."""
+    v = o["verdict"]
+    full = next((e for e in v["equal_budget"] if e["cu_budget"] == 256), None)
+    return {"pairs": PAIRS,
+            "full_cus": None if full is None else
+            {"kernel_pct": full["kernel_pct"], "sdma_pct": full["sdma_pct"],
+             "sdma_minus_kernel_pp_ci95": full["sdma_minus_kernel_pp"]},
+            "matched_time": [f"{m['sdma']} {m['coll_ms'][0]}ms {m['slowdown_pct'][0]}% vs {m['kernel']} "
+                             f"{m['coll_ms'][1]}ms {m['slowdown_pct'][1]}%: {m['sdma_minus_kernel_pp'][0]} "
+                             f"[{m['sdma_minus_kernel_pp'][1]}, {m['sdma_minus_kernel_pp'][2]}] pp"
+                             for m in v["matched_time"]],
+            "pareto": v["pareto"],
+            "sdma_lower_at_full_cus": v["target_sdma_lower_at_full_cus"],
+            "sdma_lower_at_some_matched_time": v["sdma_lower_at_some_matched_time"]}
+
+
+def reduce_hops_by_position(iv, bytes_per_launch, calls):
+    """The plain reduce hops of `calls` all-reduces split by position: the
+    first reduce-scatter hop, whose two operands were last written six or
+    more hops earlier (out of the 256 MB MALL by then), and the later ones,
+    whose incoming operand is the previous hop's output, read back from the
+    MALL.  iv: (n, 3) intervals in issue order."""
+    if calls <= 0 or len(iv) == 0 or len(iv) % calls:
+        return None
+    per = len(iv) // calls
+    d = (iv[:, 1] - iv[:, 0]).reshape(calls, per)  # ms
+    out = {}
+    for name, sel, bound, note in (
+            ("first_hop", d[:, :1], "hbm", "both operands last written 6 or more hops earlier: read from HBM"),
+            ("later_hops", d[:, 1:], "hbm+mall",
+             "the incoming operand is the previous hop's output, read back from the 256 MB MALL")):
+        if sel.size == 0:
+            continue
+        us = float(sel.mean()) * 1e3
+        gbs = bytes_per_launch / (us * 1e-6) / 1e9
+        out[name] = {"bound": bound, "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "mean_launch_us": round(us, 3), "launches": int(sel.size), "note": note}
+    return out
+
+
+def contention_from_trace(rows, n_cu=256, allowed=256):
+    """HOCCL Eq. 1 from a rocprofv3 kernel trace of one loaded window: the
+    compute units the collective's kernels hold while the compute kernels
+    run, over n_cu times the compute kernels' active time.  rows: the trace's
+    records (dicts with Kernel_Name, Start_Timestamp, End_Timestamp,
+    Grid_Size_X, Workgroup_Size_X).  The window starts after the last GPU
+    sleep kernel (which releases both streams); compute is every other
+    kernel that is not the library's, active from the first one's start to
+    the last one's end; a collective kernel holds min(its workgroups,
+    allowed) compute units while it runs."""
+    recs = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+             int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) for r in rows]
+    sleeps = [e for b, e, n, _ in recs if "sleep" in n.lower()]
+    t_from = max(sleeps) if sleeps else min(b for b, _, _, _ in recs)
+    recs = [x for x in recs if x[0] >= t_from]
+    coll = [x for x in recs if "ccr::" in x[2]]
+    comp = [x for x in recs if "ccr::" not in x[2] and "sleep" not in x[2].lower()]
+    if not comp:
+        return None
+    t0 = min(b for b, _, _, _ in comp)
+    t1 = max(e for _, e, _, _ in comp)
+    iv = [((b - t0) * 1e-6, (e - t0) * 1e-6, min(wg, allowed)) for b, e, _, wg in coll]
+    return {"contention_rate": contention_rate(iv, (t1 - t0) * 1e-6, n_cu),
+            "compute_active_ms": round((t1 - t0) * 1e-6, 3), "compute_kernels": len(comp),
+            "collective_kernels": len(coll),
+            "collective_kernel_ms": round(sum(e - b for b, e, _, _ in coll) * 1e-6, 3)}
 
 
 def slowdown_key(r):
@@ -232,6 +408,22 @@ def slowdown_key(r):
     if r["dma_engines"] in (None, "all"):
         return r["copy_mode"]
     return f"sdma_{r['dma_engines']}_engines"
+
+
+def back_to_back_ms(fn, calls, warm=5):
+    """Time per call of `calls` calls enqueued back to back between two
+    events (how nccl-tests times a collective), after `warm` calls."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
 
 
 def event_times(fn, reps=20, warm=5, before=None):
@@ -358,6 +550,50 @@ def moe_probe(ccr, workloads, steps):
     log(f"moe probe: {steps} fused dispatch + combine")
 
 
+def loaded_window_probe(ccr, workloads, mode, n_gemm=20, n_coll=6):
+    """One loaded window only (the run behind the contention-rate trace):
+    n_gemm back-to-back 8192^3 bf16 GEMMs on one stream and n_coll bucket
+    all-reduces (full CUs, kernel or SDMA copies) on another, released
+    together by an event after a GPU sleep.  Prints the event-based
+    contention bound of the same window."""
+    import torch
+    w = workloads.DP_BUCKET_BF16
+    bufs = [to_dev(x) for x in workloads.ring_inputs(w)]
+    A = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    B = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    C = torch.empty(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    g, c, s0 = own_queue_stream(0), own_queue_stream(1), own_queue_stream(2)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    with ccr.Context(0, ccr.Config(copy_mode=mode)) as ctx:
+        with torch.cuda.stream(g):
+            for _ in range(2):
+                torch.matmul(A, B, out=C)
+        ccr.ccr_allreduce(ctx, bufs, stream=c)
+        torch.cuda.synchronize()
+        ccr.ccr_profile_enable(ctx, True)
+        go = torch.cuda.Event()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        with torch.cuda.stream(s0):
+            torch.cuda._sleep(20_000_000)
+            go.record(s0)
+        g.wait_event(go)
+        c.wait_event(go)
+        with torch.cuda.stream(g):
+            ev[0].record(g)
+            for _ in range(n_gemm):
+                torch.matmul(A, B, out=C)
+            ev[1].record(g)
+        for _ in range(n_coll):
+            ccr.ccr_allreduce(ctx, bufs, stream=c)
+        torch.cuda.synchronize()
+        iv = np.concatenate([ccr.ccr_profile_intervals(ctx, k, ev[0])
+                             for k in ("reduce", "copy_kernel", "reduce_forward")])
+        ccr.ccr_profile_enable(ctx, False)
+    gemm = ev[0].elapsed_time(ev[1])
+    print(json.dumps({"loaded_window": mode, "gemm_ms": round(gemm, 3),
+                      "event_bound_contention_rate": round(contention_rate(iv, gemm, n_cu), 4)}), flush=True)
+
+
 PROBE_WORKLOADS = ("ring_allreduce_r4_1m_f32", "rs_ag_r32_8m_f32", "pp_sendrecv_4x2048x4096_bf16",
                    "moe_dispatch_combine_three_stage")
 
@@ -410,10 +646,13 @@ def workload_timings(ccr, workloads):
         bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
         b, R, N = 4, w.R, w.count
         cold = cold_ts = None
+        b2b = None
         with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
             if how == "allreduce":
                 ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs))
                 algo = b * N * (3 * (R - 1) + 1 + 2 * (R - 2))
+                # per call as nccl-tests times it: calls back to back between two events
+                b2b = back_to_back_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 100)
                 if R * N * b <= (128 << 20):  # fits the 256 MB MALL: also time it cold
                     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
                     cold_ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs),
@@ -427,6 +666,9 @@ def workload_timings(ccr, workloads):
         ms = sorted(ts)[len(ts) // 2]
         out[w.name] = {"ms": round(ms, 4), **spread(ts), "cold_ms": None if cold is None else round(cold, 4),
                        **({"cold": spread(cold_ts)} if cold_ts else {}),
+                       **({"back_to_back_ms": round(b2b, 4),
+                           "back_to_back_hbm_frac": round(algo / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                          if b2b else {}),
                        "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
                        "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "slices": w.slices}
@@ -449,10 +691,19 @@ def workload_timings(ccr, workloads):
                      "dispatch": spread(d_ts), "combine": spread(c_ts),
                      "dispatch_algorithmic_gbs": round(3 * 2 * moved / (d_ms * 1e-3) / 1e9, 1),
                      "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1)}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = lambda: scratch.fill_(1)  # noqa: E731
     with ccr.Context(0) as ctx:
         d_ts = event_times(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp))
         c_ts = event_times(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb))
         d_ms, c_ms = sorted(d_ts)[len(d_ts) // 2], sorted(c_ts)[len(c_ts) // 2]
+        # cold: a 512 MiB scratch write before each call evicts the MALL
+        dc_ts = event_times(lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp), before=flush)
+        cc_ts = event_times(lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb), before=flush)
+        k_cold = None
+        with ccr.Context(0, ccr.Config(copy_mode="kernel")) as kctx:
+            k_cold = event_times(lambda: ccr.ccr_moe_dispatch(kctx, xs, src_tok, ecnt, K, send, recv, exp),
+                                 before=flush)
         gbs = {}
         for name, fn in (("dispatch", lambda: ccr.ccr_moe_dispatch_fused(ctx, xs, src_tok, ecnt, K, exp)),
                          ("combine", lambda: ccr.ccr_moe_combine_fused(ctx, exp, slot, ecnt, T, K, outb))):
@@ -469,7 +720,11 @@ def workload_timings(ccr, workloads):
                     "dispatch_algorithmic_gbs": round(2 * moved / (d_ms * 1e-3) / 1e9, 1),
                     "exchange_algbw_gbs": round(moved / (d_ms * 1e-3) / 1e9, 1),
                     "dispatch_gather_kernel": {"gbs": gbs["dispatch"][0], "us": gbs["dispatch"][1]},
-                    "combine_gather_kernel": {"gbs": gbs["combine"][0], "us": gbs["combine"][1]}}
+                    "combine_gather_kernel": {"gbs": gbs["combine"][0], "us": gbs["combine"][1]},
+                    "cold": {"dispatch_ms": round(sorted(dc_ts)[len(dc_ts) // 2], 4), "dispatch": spread(dc_ts),
+                             "combine_ms": round(sorted(cc_ts)[len(cc_ts) // 2], 4), "combine": spread(cc_ts),
+                             "note": "512 MiB scratch write before each call"}}
+    res["kernel"]["cold_dispatch_ms"] = round(sorted(k_cold)[len(k_cold) // 2], 4)
     out[m.name] = res
     # pipeline-parallel activations through the staging slots, each copy mode
     pw = workloads.PP_STAGING_BF16
@@ -481,12 +736,19 @@ def workload_timings(ccr, workloads):
         with ccr.Context(0, ccr.Config(copy_mode=mode, staging_chunk_bytes=pw.chunk_bytes,
                                        staging_slots=pw.slots)) as ctx:
             ts = event_times(lambda: ccr.ccr_sendrecv_batch(ctx, mbs, outs))
+            cold_ts = event_times(lambda: ccr.ccr_sendrecv_batch(ctx, mbs, outs), before=flush)
+            b2b = back_to_back_ms(lambda: ccr.ccr_sendrecv_batch(ctx, mbs, outs), 50)
         ms = sorted(ts)[len(ts) // 2]
+        cms = sorted(cold_ts)[len(cold_ts) // 2]
         # every chunk is copied in (fill) and out (drain): 2 reads + 2 writes per byte
-        pp[mode] = {"ms": round(ms, 4), **spread(ts),
+        pp[mode] = {"ms": round(ms, 4), **spread(ts), "cold_ms": round(cms, 4), "cold": spread(cold_ts),
+                    "cold_algorithmic_gbs": round(4 * payload / (cms * 1e-3) / 1e9, 1),
+                    "back_to_back_ms": round(b2b, 4),
+                    "back_to_back_algorithmic_gbs": round(4 * payload / (b2b * 1e-3) / 1e9, 1),
                     "algbw_gbs": round(payload / (ms * 1e-3) / 1e9, 1),
                     "algorithmic_gbs": round(4 * payload / (ms * 1e-3) / 1e9, 1)}
     out[pw.name] = pp
+    del scratch
     return out
 
 
@@ -675,24 +937,26 @@ def cpu_baseline(xs, R, count, esize, S, budget_s=12.0):
     out = {"value": bus, "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"the full workload, {n} all-reduce(s), single-threaded C oracle",
            "ms_per_step": t * 1e3, "host_cpus": os.cpu_count(), "cpu_model": model}
-    # The same oracle, unchanged, on T host cores at once: T independent
-    # all-reduces of the bucket in T threads (the C oracle releases the GIL),
-    # reported as aggregate throughput beside the one-core figure.
+    # The same oracle arithmetic on T host cores: each all-reduce's element
+    # range cut into T parts, every part run through all hops on a thread
+    # of its own (oracle.ring_allreduce_threads: bit for bit the one-thread
+    # result, pinned by the oracle tests), timed per call.
     T = min(16, os.cpu_count() or 1)
     if T > 1:
-        from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(T) as ex:
-            t0 = time.perf_counter()
-            rounds = 0
-            while True:
-                list(ex.map(lambda _: oracle.ring_allreduce(xs, S=S), range(T)))
-                rounds += 1
-                if time.perf_counter() - t0 >= budget_s or rounds >= 4:
-                    break
-            tt = (time.perf_counter() - t0) / (rounds * T)
+        oracle.ring_allreduce_threads(xs, T, S=S)  # warm the pool's first call
+        t0 = time.perf_counter()
+        calls = 0
+        while True:
+            oracle.ring_allreduce_threads(xs, T, S=S)
+            calls += 1
+            if time.perf_counter() - t0 >= budget_s or calls >= 40:
+                break
+        tt = (time.perf_counter() - t0) / calls
         out["threads"] = {"cores": T, "value": esize * count / tt * 2 * (R - 1) / R / 1e9,
                           "ms_per_step": tt * 1e3,
-                          "sample": f"{rounds * T} all-reduces, {T} at a time on {T} threads"}
+                          "sample": f"{calls} all-reduces of the full workload, each split over {T} "
+                                    "threads by element range (the same per-element operations in "
+                                    "the same order)"}
     return out
 
 
@@ -717,7 +981,16 @@ def main():
                     help="only run --steps fused MoE dispatch + combine calls (gather kernel profiles)")
     ap.add_argument("--workload-probe", choices=PROBE_WORKLOADS, default=None,
                     help="only run --steps calls of one of the other workloads (kernel-trace profiles)")
+    ap.add_argument("--loaded-window", choices=("kernel", "sdma"), default=None,
+                    help="only run one GEMM + bucket all-reduce window (the contention-rate trace)")
+    ap.add_argument("--trace-contention", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="no GPU: HOCCL Eq. 1 of the loaded window in a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.trace_contention:
+        import csv
+        rows = list(csv.DictReader(open(args.trace_contention)))
+        print(json.dumps(contention_from_trace(rows)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -736,6 +1009,9 @@ def main():
         return
     if args.workload_probe:
         workload_probe(ccr, workloads, args.workload_probe, max(1, args.steps))
+        return
+    if args.loaded_window:
+        loaded_window_probe(ccr, workloads, args.loaded_window)
         return
 
     w = workloads.DP_BUCKET_BF16
@@ -758,15 +1034,19 @@ def main():
 
     log("bench: per-launch reduce kernel timing")
     ccr.ccr_profile_enable(ctx, True)
+    ref_ev = torch.cuda.Event(enable_timing=True)
+    ref_ev.record()
     for _ in range(args.steps):
         step()
     red = ccr.ccr_profile_read(ctx, "reduce")
     fwd = ccr.ccr_profile_read(ctx, "reduce_forward")
     cpy = ccr.ccr_profile_read(ctx, "copy_kernel")
     dma = ccr.ccr_profile_read(ctx, "sdma")
+    red_iv = ccr.ccr_profile_intervals(ctx, "reduce", ref_ev)
     ccr.ccr_profile_enable(ctx, False)
     red_gbs = red["bytes"] / (red["ms"] * 1e6)
     cpy_gbs = cpy["bytes"] / (cpy["ms"] * 1e6) if cpy["ms"] else None
+    by_position = reduce_hops_by_position(red_iv, red["bytes"] // max(1, red["launches"]), args.steps)
 
     # Every part after the timed steps is context: a part that fails (e.g. no
     # usable SDMA engine on a machine) is reported under "errors" instead of
@@ -794,8 +1074,11 @@ def main():
     gemm = pp = occ = launch = None
     if not args.no_gemm:
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
+        # kernel copies over CU budgets, SDMA copies over the same budgets
+        # (reduce kernels budgeted) and over engine counts at full CUs
         runs = [dict(cfg, copy_mode=m, cu_budget=b) for b in (0, 64, 32, 16) for m in ("kernel", "sdma")]
-        runs += [dict(cfg, copy_mode="sdma", dma_engines=e) for e in (8, 4, 2)]
+        runs.insert(2, dict(cfg, copy_mode="kernel", cu_budget=128))
+        runs += [dict(cfg, copy_mode="sdma", dma_engines=e) for e in (8, 4, 2, 1)]
         runs.append(dict(cfg, copy_mode="sdma", dma_deadline_us="window"))
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
         gemm = guarded("gemm_slowdown", lambda: overlap_runs(
@@ -808,8 +1091,9 @@ def main():
         stg = dict(staging_chunk_bytes=pw.chunk_bytes, staging_slots=pw.slots)
         pp = guarded("pp_staging_gemm_slowdown", lambda: overlap_runs(
             ccr, lambda ctx, st: ccr.ccr_sendrecv_batch(ctx, mbs, outs, stream=st),
-            [dict(stg, copy_mode="kernel"), dict(stg, copy_mode="sdma"),
-             dict(stg, copy_mode="sdma", dma_engines=4), dict(stg, copy_mode="sdma", dma_engines=2),
+            [dict(stg, copy_mode="kernel", cu_budget=b) for b in (0, 64, 32, 16)] +
+            [dict(stg, copy_mode="sdma"), dict(stg, copy_mode="sdma", dma_engines=4),
+             dict(stg, copy_mode="sdma", dma_engines=2), dict(stg, copy_mode="sdma", dma_engines=1),
              dict(stg, copy_mode="sdma", dma_deadline_us="window")],
             (4096, 4096, 16384), 20, 20))
         if pp is not None:
@@ -868,7 +1152,8 @@ def main():
                                "partial_kernel<kFirst/kMid/kLast*, 16>: the reduce-scatter hops with fp32 partials",
                      "launches": red["launches"],
                      "bytes_per_launch": red["bytes"] // max(1, red["launches"]),
-                     "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3)},
+                     "mean_launch_us": round(red["ms"] * 1e3 / max(1, red["launches"]), 3),
+                     "by_position": by_position},
         "protocol": {"timed_region": f"{args.steps} back-to-back in-place all-reduces, host clock, "
                                      "synchronised on both sides",
                      "restored_inputs": None if restored is None else dict(
@@ -888,7 +1173,7 @@ def main():
             "achieved": round(cpy_gbs, 1), "launches": cpy["launches"],
             "mean_launch_us": round(cpy["ms"] * 1e3 / max(1, cpy["launches"]), 3)},
         "gemm_slowdown_pct": None if gemm is None else {
-            slowdown_key(r): r["slowdown_pct"] for r in gemm["runs"]
+            slowdown_key(r): r["slowdown_mean_pct"] for r in gemm["runs"]
             if r["cu_budget"] == 256 and r["dma_sync"] in (None, "host_func")},
         "gemm_slowdown": gemm,
         "pp_staging_gemm_slowdown": pp,
@@ -898,6 +1183,9 @@ def main():
         "cpu_baseline": cpu,
         **({"errors": errors} if errors else {}),
     }
+    # last, so that a tail of the output line still shows it
+    line["sdma_vs_kernel"] = {k: compact_verdict(v) for k, v in (("bucket", gemm), ("pp_staging", pp))
+                              if v is not None}
     ctx.close()
     print(json.dumps(line), flush=True)
 

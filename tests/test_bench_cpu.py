@@ -95,3 +95,79 @@ def test_slowdown_summary_names_every_full_cu_run_apart():
             {"copy_mode": "sdma", "dma_engines": "all", "dma_deadline": {"deadline_us": 2900}}]
     keys = [bench.slowdown_key(r) for r in runs]
     assert keys == ["kernel", "sdma", "sdma_2_engines", "sdma_deadline"]
+
+
+def test_ci95_against_scipy_and_a_normal_sample():
+    from scipy import stats
+    rng = np.random.default_rng(1)
+    x = rng.normal(2.0, 0.5, 15)
+    m, lo, hi = bench.ci95(x)
+    want = stats.t.interval(0.95, 14, loc=x.mean(), scale=stats.sem(x))
+    assert m == pytest.approx(x.mean()) and (lo, hi) == pytest.approx(want)
+    d, lo, hi = bench.diff_ci95(x + 1.0, x)
+    assert d == pytest.approx(1.0) and lo < 1.0 < hi
+    assert bench.ci95([3.0]) == (3.0, 3.0, 3.0)
+
+
+def test_pareto_keeps_only_undominated_points():
+    pts = [("a", 19.0, 0.7), ("b", 30.0, 0.2), ("c", 24.0, 1.5), ("d", 26.0, 7.0), ("e", 19.0, 0.9)]
+    assert bench.pareto(pts) == ["a", "b"]
+    assert bench.pareto([("x", 1.0, 1.0)]) == ["x"]
+
+
+def _run(mode, B, eng, pairs, coll, **kw):
+    r = {"copy_mode": mode, "cu_budget": B, "dma_engines": eng,
+         "dma_sync": "host_func" if mode == "sdma" else None, "pairs_pct": list(pairs),
+         "slowdown_mean_pct": float(np.mean(pairs)), "collectives_under_load_ms": coll, **kw}
+    r["label"] = bench.run_label(r)
+    return r
+
+
+def test_sdma_verdict_compares_equal_budgets_and_matched_times():
+    rng = np.random.default_rng(2)
+    noise = lambda m: m + rng.normal(0, 0.05, 15)  # noqa: E731
+    runs = [_run("kernel", 256, None, noise(0.6), 19.0), _run("kernel", 16, None, noise(7.0), 26.5),
+            _run("sdma", 256, "all", noise(1.6), 21.6), _run("sdma", 16, "all", noise(9.0), 26.4),
+            _run("sdma", 256, 2, noise(0.2), 30.0), _run("sdma", 256, 4, noise(1.2), 26.0),
+            _run("sdma", 256, "all", noise(12.0), 15.0, dma_sync="stream_flags")]
+    v = bench.sdma_verdict(runs)
+    eq = {e["cu_budget"]: e for e in v["equal_budget"]}
+    assert set(eq) == {256, 16}
+    assert eq[256]["sdma_higher"] and not eq[256]["sdma_lower"] and v["target_sdma_lower_at_full_cus"] is False
+    m = {x["sdma"]: x for x in v["matched_time"]}
+    # SDMA on 4 engines (26.0 ms) is matched with kernel copies at 16 CUs (26.5 ms) and beats them
+    assert m["sdma/B256/E4"]["kernel"] == "kernel/B16" and m["sdma/B256/E4"]["sdma_lower"]
+    assert v["sdma_lower_at_some_matched_time"]
+    assert "sdma/B256/Eall/flags" not in str(v)  # flag-handshake runs stay out of the comparison
+    assert v["pareto"] == ["kernel/B256", "sdma/B256/E2"]
+    c = bench.compact_verdict({"verdict": v})
+    assert len(json_dumps(c)) < 1500 and c["sdma_lower_at_full_cus"] is False
+
+
+def json_dumps(o):
+    import json
+    return json.dumps(o)
+
+
+def test_contention_from_trace_rows():
+    def row(name, b, e, grid, wg=256):
+        return {"Kernel_Name": name, "Start_Timestamp": str(b), "End_Timestamp": str(e),
+                "Grid_Size_X": str(grid * wg), "Workgroup_Size_X": str(wg)}
+    rows = [row("void ccr::pieces_kernel<...>", 0, 500, 6400),  # before the window: ignored
+            row("at::cuda::sleep(long)", 1000, 2000, 1),
+            row("Cijk_gemm", 2000, 12000, 1024), row("Cijk_gemm", 12000, 22000, 1024),
+            row("void ccr::pieces_kernel<...>", 5000, 7000, 6400),   # 256 CUs for 2 us
+            row("void ccr::pieces_kernel<...>", 20000, 25000, 64)]   # 64 CUs, 2 us inside the window
+    got = bench.contention_from_trace(rows)
+    want = (256 * 2000 + 64 * 2000) / (256 * 20000)
+    assert got["contention_rate"] == pytest.approx(want)
+    assert got["compute_kernels"] == 2 and got["collective_kernels"] == 2
+
+
+def test_reduce_hops_by_position():
+    iv = np.array([[0.0, 0.033, 256], [0.04, 0.064, 256], [0.07, 0.094, 256]] * 2)
+    out = bench.reduce_hops_by_position(iv, 157286400, 2)
+    assert out["first_hop"]["mean_launch_us"] == pytest.approx(33.0)
+    assert out["later_hops"]["mean_launch_us"] == pytest.approx(24.0)
+    assert out["first_hop"]["bound"] == "hbm" and out["later_hops"]["bound"] == "hbm+mall"
+    assert bench.reduce_hops_by_position(iv, 1, 4) is None
