@@ -373,7 +373,23 @@ def reduce_hops_by_position(iv, bytes_per_launch, calls):
     return out
 
 
-def contention_from_trace(rows, n_cu=256, allowed=256):
+def kernel_means(rows):
+    """Mean duration (ns) per kernel name in a rocprofv3 kernel trace."""
+    acc = {}
+    for r in rows:
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        n, t = acc.get(r["Kernel_Name"], (0, 0))
+        acc[r["Kernel_Name"]] = (n + 1, t + d)
+    return {k: t / n for k, (n, t) in acc.items()}
+
+
+def _releases(name):
+    """The GPU sleep that releases both streams of a loaded window."""
+    n = name.lower()
+    return "sleep" in n or "spin_kernel" in n
+
+
+def contention_from_trace(rows, n_cu=256, allowed=256, alone=None):
     """HOCCL Eq. 1 from a rocprofv3 kernel trace of one loaded window: the
     compute units the collective's kernels hold while the compute kernels
     run, over n_cu times the compute kernels' active time.  rows: the trace's
@@ -381,24 +397,42 @@ def contention_from_trace(rows, n_cu=256, allowed=256):
     Grid_Size_X, Workgroup_Size_X).  The window starts after the last GPU
     sleep kernel (which releases both streams); compute is every other
     kernel that is not the library's, active from the first one's start to
-    the last one's end; a collective kernel holds min(its workgroups,
-    allowed) compute units while it runs."""
+    the last one's end.
+    - interval_bound: a collective kernel holds min(its workgroups, allowed)
+      compute units for its whole traced interval (as the event-based
+      figure does); a kernel starved behind the compute kernels stretches
+      over much of the window, so this is an upper bound;
+    - work_estimate (when `alone` maps kernel names to their durations in
+      ns with nothing else running): a kernel holds those units only for its
+      unloaded duration, the compute-unit time it needs, counted in
+      proportion to the part of its interval inside the window."""
     recs = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
              int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))) for r in rows]
-    sleeps = [e for b, e, n, _ in recs if "sleep" in n.lower()]
-    t_from = max(sleeps) if sleeps else min(b for b, _, _, _ in recs)
+    rel = [e for b, e, n, _ in recs if _releases(n)]
+    t_from = max(rel) if rel else min(b for b, _, _, _ in recs)
     recs = [x for x in recs if x[0] >= t_from]
     coll = [x for x in recs if "ccr::" in x[2]]
-    comp = [x for x in recs if "ccr::" not in x[2] and "sleep" not in x[2].lower()]
+    comp = [x for x in recs if "ccr::" not in x[2] and not _releases(x[2])]
     if not comp:
         return None
     t0 = min(b for b, _, _, _ in comp)
     t1 = max(e for _, e, _, _ in comp)
+    win = (t1 - t0) * 1e-6
     iv = [((b - t0) * 1e-6, (e - t0) * 1e-6, min(wg, allowed)) for b, e, _, wg in coll]
-    return {"contention_rate": contention_rate(iv, (t1 - t0) * 1e-6, n_cu),
-            "compute_active_ms": round((t1 - t0) * 1e-6, 3), "compute_kernels": len(comp),
-            "collective_kernels": len(coll),
-            "collective_kernel_ms": round(sum(e - b for b, e, _, _ in coll) * 1e-6, 3)}
+    out = {"interval_bound": round(contention_rate(iv, win, n_cu), 4),
+           "compute_active_ms": round(win, 3), "compute_kernels": len(comp),
+           "collective_kernels": len(coll),
+           "collective_kernel_ms": round(sum(e - b for b, e, _, _ in coll) * 1e-6, 3)}
+    if alone:
+        work = 0.0  # compute-unit nanoseconds
+        for b, e, name, wg in coll:
+            inside = max(0, min(e, t1) - max(b, t0))
+            if inside <= 0 or e <= b:
+                continue
+            need = min(e - b, alone.get(name, e - b))
+            work += need * (inside / (e - b)) * min(wg, allowed)
+        out["work_estimate"] = round(work / (n_cu * (t1 - t0)), 4)
+    return out
 
 
 def slowdown_key(r):
@@ -613,6 +647,17 @@ def workload_probe(ccr, workloads, name, steps):
                     ccr.ccr_reduce_scatter(ctx, bufs)
                     ccr.ccr_all_gather(ctx, bufs)
             torch.cuda.synchronize()
+            if name == "ring_allreduce_r4_1m_f32":
+                # references of the same size in the same trace: torch's copy of
+                # one rank's 4 MiB (the bytes of one copy hop), and a kernel of
+                # 512 one-wave workgroups that only records its CU ids (the
+                # launch alone, at the copy hop's workgroup count)
+                dst = torch.empty_like(bufs[0])
+                ids = torch.zeros(512, 3, dtype=torch.int32, device="cuda")
+                for _ in range(steps):
+                    dst.copy_(bufs[0])
+                    ccr._check(ccr._lib.ccr_probe_cu_ids(ctx.handle, ids.data_ptr(), 512, None))
+                torch.cuda.synchronize()
     elif name == "pp_sendrecv_4x2048x4096_bf16":
         pw = workloads.PP_STAGING_BF16
         mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
@@ -985,11 +1030,15 @@ def main():
                     help="only run one GEMM + bucket all-reduce window (the contention-rate trace)")
     ap.add_argument("--trace-contention", metavar="KERNEL_TRACE_CSV", default=None,
                     help="no GPU: HOCCL Eq. 1 of the loaded window in a rocprofv3 kernel trace")
+    ap.add_argument("--alone-trace", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="with --trace-contention: a trace of the same kernels with nothing else "
+                         "running, for the work-based estimate")
     args = ap.parse_args()
     if args.trace_contention:
         import csv
         rows = list(csv.DictReader(open(args.trace_contention)))
-        print(json.dumps(contention_from_trace(rows)), flush=True)
+        alone = kernel_means(list(csv.DictReader(open(args.alone_trace)))) if args.alone_trace else None
+        print(json.dumps(contention_from_trace(rows, alone=alone)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the R ranks are virtual ranks in one GPU's HBM; "

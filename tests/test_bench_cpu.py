@@ -160,8 +160,17 @@ def test_contention_from_trace_rows():
             row("void ccr::pieces_kernel<...>", 20000, 25000, 64)]   # 64 CUs, 2 us inside the window
     got = bench.contention_from_trace(rows)
     want = (256 * 2000 + 64 * 2000) / (256 * 20000)
-    assert got["contention_rate"] == pytest.approx(want)
+    assert got["interval_bound"] == pytest.approx(want, abs=1e-4)
     assert got["compute_kernels"] == 2 and got["collective_kernels"] == 2
+    # torch's GPU sleep is named spin_kernel on this stack
+    rows[1]["Kernel_Name"] = "at::cuda::(anonymous namespace)::spin_kernel(long)"
+    assert bench.contention_from_trace(rows)["compute_kernels"] == 2
+    # the work-based estimate: each kernel needs 500 ns alone; the second one
+    # lies 2/5 inside the window
+    got = bench.contention_from_trace(rows, alone={"void ccr::pieces_kernel<...>": 500})
+    want = (500 * 256 + 500 * (2000 / 5000) * 64) / (256 * 20000)
+    assert got["work_estimate"] == pytest.approx(want, abs=1e-4)
+    assert bench.kernel_means(rows)["Cijk_gemm"] == pytest.approx(10000)
 
 
 def test_reduce_hops_by_position():
