@@ -625,8 +625,11 @@ int64_t auto_chunk(int64_t total, int engines) {
 // (2 bf16, twice when forwarding).
 ccr_status_t launch_partials_timed(ccr_ctx* ctx, PartialKind kind, const PartialPiece* p, int n,
                                    hipStream_t s) {
+  // the first hop's operands stream like the other hops' incoming ones when
+  // the call's buffers exceed the MALL
+  const bool nt_first = call_tuning(ctx).nontemporal != 0;
   if (!ctx->prof_on) {
-    HIP_TRY(launch_partials(kind, p, n, s));
+    HIP_TRY(launch_partials(kind, p, n, nt_first, s));
     return CCR_OK;
   }
   int64_t elems = 0;
@@ -636,7 +639,7 @@ ccr_status_t launch_partials_timed(ccr_ctx* ctx, PartialKind kind, const Partial
   hipEvent_t start, stop;
   CCR_TRY(timing_event(ctx, &start));
   CCR_TRY(timing_event(ctx, &stop));
-  HIP_TRY(launch_partials(kind, p, n, s, start, stop));
+  HIP_TRY(launch_partials(kind, p, n, nt_first, s, start, stop));
   ctx->timed.push_back(ccr_ctx::Timed{kProfReduce, start, stop, elems * per,
                                       cus_held(ctx, (elems + 8 * kBlock * 2 - 1) / (8 * kBlock * 2))});
   return CCR_OK;

@@ -65,8 +65,9 @@ struct PartialPiece {
 
 enum class PartialKind : int { kFirst = 0, kMid = 1, kLast = 2, kLastFwd = 3 };
 
-hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
-                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// nt_first: the first hop (kFirst) loads its two bf16 operands non-temporally.
+hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, bool nt_first,
+                           hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Enqueue one batched launch over `n` pieces (n <= kMaxPieces).  With
 // start/stop events, the launch goes through hipExtLaunchKernelGGL so that

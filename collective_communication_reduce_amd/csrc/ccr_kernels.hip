@@ -289,15 +289,18 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
 // One group of 8 elements: out = in + float(loc).  The loads and the
 // stores are split so that a tile issues all its loads before its first
 // store (the compiler may not move a load above a store that could alias).
-// Temporal loads throughout: a non-temporal load of the incoming partial
-// made the 8-rank bucket's all-reduce in this mode 9% slower.
-template <PartialKind K>
+// NT: the first hop's two bf16 operands, both last written long before and
+// dead after this hop, are loaded non-temporally (the bucket's first hop
+// 39.3 -> 35.8 us); every other load is temporal: a non-temporal load of the
+// incoming partial made the 8-rank bucket's all-reduce in this mode 9% slower.
+template <PartialKind K, bool NT>
 __device__ __forceinline__ void partial_load(const PartialPiece& pc, int64_t g, u32x4* loc,
                                              f32x4* in) {
-  *loc = reinterpret_cast<const u32x4*>(pc.loc)[g];
+  constexpr bool nt_first = NT && K == PartialKind::kFirst;
+  *loc = load16<nt_first>(reinterpret_cast<const u32x4*>(pc.loc) + g);
   if constexpr (K == PartialKind::kFirst) {
     float f[8];
-    unpack_bf16x8(reinterpret_cast<const u32x4*>(pc.in)[g], f);
+    unpack_bf16x8(load16<nt_first>(reinterpret_cast<const u32x4*>(pc.in) + g), f);
     in[0] = f32x4{f[0], f[1], f[2], f[3]};
     in[1] = f32x4{f[4], f[5], f[6], f[7]};
   } else {
@@ -341,7 +344,7 @@ __device__ __forceinline__ void partial_one(const PartialPiece& pc, int64_t i) {
   }
 }
 
-template <PartialKind K, int NP>
+template <PartialKind K, int NP, bool NT>
 __global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
   const int b = blockIdx.x;
   const int lo = piece_of<NP>(a.tile_start, b);
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
     f32x4 in[kPartialUnroll][2];
 #pragma unroll
     for (int u = 0; u < kPartialUnroll; u++)
-      partial_load<K>(pc, first + u * kBlock + threadIdx.x, &loc[u], in[u]);
+      partial_load<K, NT>(pc, first + u * kBlock + threadIdx.x, &loc[u], in[u]);
 #pragma unroll
     for (int u = 0; u < kPartialUnroll; u++)
       partial_store<K>(pc, first + u * kBlock + threadIdx.x, loc[u], in[u]);
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(kBlock) void partial_kernel(PartialArgs<NP> a) {
       if (g < ngroups) {
         u32x4 loc;
         f32x4 in[2];
-        partial_load<K>(pc, g, &loc, in);
+        partial_load<K, NT>(pc, g, &loc, in);
         partial_store<K>(pc, g, loc, in);
       }
     }
@@ -443,7 +446,7 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
 namespace {
 
 template <int NP>
-hipError_t launch_partials_np(PartialKind kind, const PartialPiece* pieces, int n,
+hipError_t launch_partials_np(PartialKind kind, const PartialPiece* pieces, int n, bool nt_first,
                               hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   PartialArgs<NP> a;
   const int64_t per_tile = (int64_t)kBlock * kPartialUnroll;
@@ -464,22 +467,25 @@ hipError_t launch_partials_np(PartialKind kind, const PartialPiece* pieces, int 
     else kernel<<<grid, block, 0, stream>>>(a);
   };
   switch (kind) {
-    case PartialKind::kFirst: go(partial_kernel<PartialKind::kFirst, NP>); break;
-    case PartialKind::kMid: go(partial_kernel<PartialKind::kMid, NP>); break;
-    case PartialKind::kLast: go(partial_kernel<PartialKind::kLast, NP>); break;
-    default: go(partial_kernel<PartialKind::kLastFwd, NP>); break;
+    case PartialKind::kFirst:
+      if (nt_first) go(partial_kernel<PartialKind::kFirst, NP, true>);
+      else go(partial_kernel<PartialKind::kFirst, NP, false>);
+      break;
+    case PartialKind::kMid: go(partial_kernel<PartialKind::kMid, NP, false>); break;
+    case PartialKind::kLast: go(partial_kernel<PartialKind::kLast, NP, false>); break;
+    default: go(partial_kernel<PartialKind::kLastFwd, NP, false>); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, hipStream_t stream,
-                           hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_partials(PartialKind kind, const PartialPiece* pieces, int n, bool nt_first,
+                           hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (n <= 0) return hipSuccess;
   if (n > kMaxPieces) return hipErrorInvalidValue;
-  if (n <= 16) return launch_partials_np<16>(kind, pieces, n, stream, start, stop);
-  return launch_partials_np<kMaxPieces>(kind, pieces, n, stream, start, stop);
+  if (n <= 16) return launch_partials_np<16>(kind, pieces, n, nt_first, stream, start, stop);
+  return launch_partials_np<kMaxPieces>(kind, pieces, n, nt_first, stream, start, stop);
 }
 
 hipError_t launch_probe_cu_ids(int32_t* out, int nblocks, hipStream_t stream) {
