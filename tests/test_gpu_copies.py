@@ -467,3 +467,38 @@ def test_destroy_abandons_jobs_whose_stream_has_not_arrived(ccr_mod, monkeypatch
 def ctypes_null():
     import ctypes
     return ctypes.c_void_p()
+
+
+@pytest.mark.parametrize("mode", ["kernel", "sdma"])
+def test_ring_shift_and_element_alltoall_at_workload_sizes(ccr_mod, mode):
+    """The boundary's two §8(b) forms at the workloads' sizes: the ring shift
+    over R = 2 (a pipeline pair exchanging one 2048 x 4096 bf16 activation in
+    each direction through two 4 MiB slots) and the uniform element
+    all-to-all over 8 ranks of 4096 x 2048 bf16 (each rank's buffer cut into
+    8 equal segments); both byte for byte against the oracle."""
+    import torch
+    w = workloads.PP_STAGING_BF16
+    mb = workloads.staging_inputs(w)[:2]
+    ref, _ = oracle.ring_sendrecv([x.view(np.uint8) for x in mb], w.chunk_bytes, w.slots)
+    say(f"ring shift R=2 at {w.name} size, {mode}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode, staging_chunk_bytes=w.chunk_bytes,
+                                           staging_slots=w.slots)) as c:
+        s = [to_dev(x) for x in mb]
+        r = [torch.zeros_like(x) for x in s]
+        ccr_mod.ccr_sendrecv(c, s, r)
+        torch.cuda.synchronize()
+        for q in range(2):
+            assert to_host(r[q]).view(np.uint8).tobytes() == ref[q].tobytes(), f"rank {q}"
+    m = workloads.MOE_DISPATCH_BF16
+    xs, _ = workloads.moe_inputs(m)
+    count = m.tokens * m.hidden
+    counts = np.full((m.R, m.R), count // m.R, np.int64)
+    ref = oracle.alltoall([x.view(np.uint8) for x in xs], counts, 2)
+    say(f"uniform element all-to-all at {m.name} size, {mode}")
+    with ccr_mod.Context(0, ccr_mod.Config(copy_mode=mode)) as c:
+        s = [to_dev(x.reshape(-1)) for x in xs]
+        r = [torch.zeros_like(x) for x in s]
+        ccr_mod.ccr_alltoall(c, s, r)
+        torch.cuda.synchronize()
+        for d in range(m.R):
+            assert to_host(r[d]).view(np.uint8).tobytes() == ref[d].tobytes(), f"rank {d}"
