@@ -871,18 +871,28 @@ def host_call_us(ccr, call, reps=50):
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "ring_allreduce_dp_bucket_r8_bf16_hbm_counters.md")
-KERNELS = os.path.join(ROOT, "collective_communication_reduce_amd", "csrc", "ccr_kernels.hip")
+# the sources of the streaming kernels the counters measured
+KERNELS = [os.path.join(ROOT, "collective_communication_reduce_amd", "csrc", f)
+           for f in ("ccr_device.h", "ccr_kernels.hip", "ccr_ring.hip")]
+
+
+def kernel_source_sha256(paths=None):
+    """sha256 over the streaming kernels' sources, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths or KERNELS:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(key="reduce_hop_traffic_bytes_per_launch"):
     """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
     or None when the kernel source has changed since the counters were
     taken."""
-    import hashlib
     try:
         fields = dict(l.split(": ", 1) for l in open(COUNTERS).read().splitlines() if ": " in l
                       and not l.startswith(("|", "#", "`")))
-        sha = hashlib.sha256(open(KERNELS, "rb").read()).hexdigest()
+        sha = kernel_source_sha256()
     except OSError:
         return None
     if fields.get("kernel_source_sha256", "").strip() != sha:
@@ -1196,7 +1206,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.bf16_acc == "per_hop" else None,
-                     "kernel": "pieces_kernel<kReduceBf16, 2, 2, 8>: one reduce-scatter hop, all 8 ranks, incoming operand loaded non-temporally"
+                     "kernel": "ring_hop_kernel<kReduceBf16, 2, 8>: one reduce-scatter hop, all 8 ranks, incoming operand loaded non-temporally"
                                if args.bf16_acc == "per_hop" else
                                "partial_kernel<kFirst/kMid/kLast*, 16>: the reduce-scatter hops with fp32 partials",
                      "launches": red["launches"],

@@ -18,8 +18,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libccr.so")
-SOURCES = ["ccr_api.cpp", "ccr_dma.cpp", "ccr_schedule.cpp", "ccr_kernels.hip", "ccr_moe_kernels.hip",
-           "ccr_scratch.hip"]
+SOURCES = ["ccr_api.cpp", "ccr_dma.cpp", "ccr_schedule.cpp", "ccr_kernels.hip", "ccr_ring.hip",
+           "ccr_moe_kernels.hip", "ccr_scratch.hip"]
+# Per-source additions: the ring-hop kernels take their leading scalar
+# arguments preloaded into registers (gfx950 kernel-argument preloading), so
+# a workgroup's first scalar memory access is the load of its base addresses.
+SOURCE_FLAGS = {"ccr_ring.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 arithmetic;
@@ -46,7 +50,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         noise = "is not a recognized feature for this target"
         err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -516,6 +516,81 @@ ccr_status_t launch_timed(ccr_ctx* ctx, HopKind kind, const Piece* p, int n, hip
   return CCR_OK;
 }
 
+// Ring hops go through launch_ring_hop (rank base addresses, one chunk
+// geometry) unless CCR_RING_HOPS=table asks for the piece-table launch.
+bool ring_hops_from_bases() {
+  static const bool on = [] {
+    const char* e = getenv("CCR_RING_HOPS");
+    return !(e && strcmp(e, "table") == 0);
+  }();
+  return on;
+}
+
+// Hop k of `phase` on slice s as a RingHop: the operations hop_ops lists
+// by rank, listed by chunk.  Rank q works on chunk c = q - k - 2 (reduce-
+// scatter) or q - k - 1 (all-gather) and reads rank q - 1, so chunk c goes
+// from rank c + k + 1 (resp. c + k) to the rank after it.  Chunks below
+// count / L are whole and share slice s's offsets within a chunk; the chunk
+// after them holds the ragged end (or nothing).
+RingHop ring_hop_desc(int phase, int k, int s, int R, int64_t count, int S, int V, int esize,
+                      void* const* bufs) {
+  RingHop h;
+  h.R = R;
+  h.shift = (phase == kRS ? k + 1 : k) % R;
+  const int64_t L = align_up(ceil_div(count, R), V);
+  h.stride = L * esize;
+  h.nfull = L > 0 ? (int)std::min<int64_t>(R, count / L) : 0;
+  int64_t lo, hi;
+  slice_range(0, L, S, V, s, &lo, &hi);
+  h.full_off = lo * esize;
+  h.full_len = (hi - lo) * esize;
+  if (h.nfull < R) {
+    int64_t clo, chi;
+    chunk_range(count, R, V, h.nfull, &clo, &chi);
+    slice_range(clo, chi, S, V, s, &lo, &hi);
+    h.rag_c = h.nfull;
+    h.rag_off = lo * esize;
+    h.rag_len = (hi - lo) * esize;
+  }
+  // Full chunks in destination-rank order, as hop_ops lists them: from the
+  // chunk the previous hop wrote last, whose tiles the caches most likely
+  // still hold (on MI355X the bf16 bucket's all-reduce 2% faster than from
+  // chunk 0; walking every other hop backwards instead was slower still).
+  const int first = (2 * R - h.shift - 1) % R;
+  h.rot = first < h.nfull ? first : 0;
+  h.base = reinterpret_cast<char* const*>(bufs);
+  return h;
+}
+
+// One ring hop in the base-address form, timed like launch_timed; *done is
+// false (and nothing is launched) when the form does not take the hop under
+// the call's tuning, and the caller launches its pieces instead.
+ccr_status_t ring_hop_timed(ccr_ctx* ctx, HopKind kind, const RingHop& h, hipStream_t s,
+                            int nt_override, bool* done) {
+  LaunchTuning tune = call_tuning(ctx);
+  if (nt_override >= 0) tune.nontemporal = nt_override;
+  *done = false;
+  if (!ring_hops_from_bases() || tune.unroll != 2 || tune.grid > 0 ||
+      !ring_hop_supported(h, kind, tune.nontemporal))
+    return CCR_OK;
+  *done = true;
+  if (!ctx->prof_on) {
+    HIP_TRY(launch_ring_hop(kind, h, tune.nontemporal, s));
+    return CCR_OK;
+  }
+  const bool fwd = kind == HopKind::kReduceFwdF32 || kind == HopKind::kReduceFwdBf16;
+  const bool reduce = fwd || kind == HopKind::kReduceF32 || kind == HopKind::kReduceBf16;
+  hipEvent_t start, stop;
+  CCR_TRY(timing_event(ctx, &start));
+  CCR_TRY(timing_event(ctx, &stop));
+  HIP_TRY(launch_ring_hop(kind, h, tune.nontemporal, s, start, stop));
+  const int64_t payload_bytes = (int64_t)h.nfull * h.full_len + h.rag_len;
+  ctx->timed.push_back(ccr_ctx::Timed{fwd ? kProfReduceFwd : reduce ? kProfReduce : kProfCopyKernel,
+                                      start, stop, payload_bytes * (fwd ? 4 : reduce ? 3 : 2),
+                                      cus_held(ctx, ring_hop_workgroups(h))});
+  return CCR_OK;
+}
+
 // ------------------------------------------------------------- SDMA path
 ccr_status_t ensure_dma(ccr_ctx* ctx) {
   if (ctx->dma) return CCR_OK;
@@ -936,9 +1011,16 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
   for (int s = 0; s < S; s++) {
     if (which != kWhichAG) {
       for (int k = 0; k + 1 < R; k++) {
+        const bool forward = fuse && k == R - 2;
+        const int nt_hop = k == 0 ? first_hop_nontemporal() : -1;
+        if (!partials) {
+          bool done;
+          CCR_TRY(ring_hop_timed(ctx, forward ? reduce_fwd : reduce,
+                                 ring_hop_desc(kRS, k, s, R, count, S, V, esize, bufs), rs, nt_hop, &done));
+          if (done) continue;
+        }
         ops.clear();
         hop_ops(kRS, k, s, R, count, S, V, &ops);
-        const bool forward = fuse && k == R - 2;
         if (partials) {
           int n = 0;
           for (const ccr_ring_op_t& o : ops) {
@@ -967,8 +1049,7 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
         }
         int n;
         to_pieces(&n, forward);
-        CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs,
-                             k == 0 ? first_hop_nontemporal() : -1));
+        CCR_TRY(launch_timed(ctx, forward ? reduce_fwd : reduce, pieces.data(), n, rs, nt_hop));
       }
     }
     if (which != kWhichRS && sdma) {
@@ -983,6 +1064,10 @@ ccr_status_t enqueue_ring(ccr_ctx* ctx, void* const* bufs, int R, int64_t count,
     } else if (which != kWhichRS) {
       if (ag != rs) CCR_TRY(order_after(ctx, ev_slice0 + (size_t)s, rs, ag));
       for (int k = fuse ? 1 : 0; k + 1 < R; k++) {
+        bool done;
+        CCR_TRY(ring_hop_timed(ctx, HopKind::kCopy, ring_hop_desc(kAG, k, s, R, count, S, V, esize, bufs),
+                               ag, -1, &done));
+        if (done) continue;
         ops.clear();
         hop_ops(kAG, k, s, R, count, S, V, &ops);
         int n;

@@ -1,5 +1,5 @@
 // Internal interface between the host runtime (ccr_api.cpp) and the device
-// kernels (ccr_kernels.hip).  Not part of the public ABI.
+// kernels (the .hip sources).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,8 +76,37 @@ hipError_t launch_pieces(HopKind kind, const Piece* pieces, int n, LaunchTuning 
                          hipStream_t stream, hipEvent_t start = nullptr,
                          hipEvent_t stop = nullptr);
 
-// dst row i = src row idx[i] for i < nrows; rows of row_bytes (multiple of
-// 16); entries outside [0, nsrc) are skipped.
+// One ring hop over R rank buffers: chunk c moves from rank (c + shift) mod R
+// to the next rank (kReduce*: added into it; kReduceFwd*: also written to
+// the rank after; kCopy: copied).  Chunks 0..nfull-1 start `stride` bytes
+// apart and the hop touches full_len bytes at full_off within each; chunk
+// rag_c (>= nfull), if rag_len > 0, touches rag_len bytes at absolute byte
+// offset rag_off.  stride, full_off and full_len are 16-byte multiples;
+// rag_off too, and rag_len a multiple of the element size.  The full chunks
+// are taken in the order rot, rot + 1, ..., nfull - 1, 0, ..., rot - 1.
+struct RingHop {
+  int R = 0;
+  int shift = 0;
+  int rot = 0;
+  int64_t stride = 0;
+  int nfull = 0;
+  int64_t full_off = 0, full_len = 0;
+  int rag_c = 0;
+  int64_t rag_off = 0, rag_len = 0;
+  char* const* base = nullptr;  // R rank buffers
+};
+constexpr int kRingHopMaxRanks = 64;
+
+// Whether launch_ring_hop takes this hop (hop kinds of the ring, load modes
+// 0, 2 and 3, R <= 64, full-piece offsets within 2^31 vectors).
+bool ring_hop_supported(const RingHop& h, HopKind kind, int ntm);
+// Workgroups of its launch: one per 2 x kBlock 16-byte vectors of a piece.
+int64_t ring_hop_workgroups(const RingHop& h);
+// One launch for the hop (2 vectors per operand per thread, load mode ntm as
+// in LaunchTuning::nontemporal); start/stop as for launch_pieces.
+hipError_t launch_ring_hop(HopKind kind, const RingHop& h, int ntm, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
 // Fused MoE dispatch / combine (one gather per row).  Per source rank r:
 // `rows` is x[r] (dispatch) or out[r] (combine) and `idx` is src_tok[r]
 // (pack position -> token) or slot[r] ((t, k) -> pack position).  Per
@@ -102,6 +131,8 @@ hipError_t launch_moe_gather(int combine, const MoeRank* ranks, const MoeSeg* se
                              int64_t rows_per_rank, int64_t idx_limit, int64_t row_bytes,
                              bool nt_load, hipStream_t stream, hipEvent_t start = nullptr,
                              hipEvent_t stop = nullptr);
+// dst row i = src row idx[i] for i < nrows; rows of row_bytes (multiple of
+// 16); entries outside [0, nsrc) are skipped.
 hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, int64_t nrows,
                                int64_t nsrc, int64_t row_bytes, hipStream_t stream);
 

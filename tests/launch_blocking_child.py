@@ -1,8 +1,9 @@
 """Child process of the environment-invariance tests: runs all-reduces and a
 staged send/recv through the library on inputs from an .npz file and saves
 the results.  Started with a variable in its environment that is read once
-per process (HIP_LAUNCH_BLOCKING=1, read when HIP initialises, or a forced
-CCR_NONTEMPORAL mode), so each setting needs a process of its own
+per process (HIP_LAUNCH_BLOCKING=1, read when HIP initialises, a forced
+CCR_NONTEMPORAL mode, or CCR_RING_HOPS), so each setting needs a process of
+its own
 (marshalling only: no reference arithmetic here)."""
 import os
 import sys

@@ -44,10 +44,12 @@ def test_measured_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     got = bench.measured_traffic()
     assert got is not None and abs(got - 157_286_400) / 157_286_400 < 0.01
     assert bench.measured_traffic("copy_hop_traffic_bytes_per_launch") is not None
-    changed = tmp_path / "ccr_kernels.hip"
-    changed.write_bytes(open(bench.KERNELS, "rb").read() + b"\n// edited\n")
-    monkeypatch.setattr(bench, "KERNELS", str(changed))
-    assert bench.measured_traffic() is None
+    for i in range(len(bench.KERNELS)):  # an edit of any of the kernel sources
+        changed = tmp_path / f"edited_{i}"
+        changed.write_bytes(open(bench.KERNELS[i], "rb").read() + b"\n// edited\n")
+        monkeypatch.setattr(bench, "KERNELS", bench.KERNELS[:i] + [str(changed)] + bench.KERNELS[i + 1:])
+        assert bench.measured_traffic() is None
+        monkeypatch.undo()
 
 
 def test_percentiles():

@@ -211,14 +211,16 @@ def test_profile_intervals(ccr_mod, budget):
 
 
 @pytest.mark.parametrize("env", [{"HIP_LAUNCH_BLOCKING": "1"}, {"CCR_NONTEMPORAL": "0"},
-                                 {"CCR_NONTEMPORAL": "1"}, {"CCR_NONTEMPORAL": "2"}],
+                                 {"CCR_NONTEMPORAL": "1"}, {"CCR_NONTEMPORAL": "2"},
+                                 {"CCR_RING_HOPS": "table"}],
                          ids=lambda e: "-".join(f"{k}={v}" for k, v in e.items()))
 def test_process_settings_do_not_change_bits(ccr_mod, tmp_path, env):
     """Settings read once per process leave the bits unchanged in every
-    mode: HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one)
-    and each forced non-temporal mode of the streaming kernels (none, every
-    load and store, the incoming load only).  Each case runs in a child
-    process of its own."""
+    mode: HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one),
+    each forced non-temporal mode of the streaming kernels (none, every
+    load and store, the incoming load only), and ring hops launched from
+    the piece table instead of the rank base addresses.  Each case runs in
+    a child process of its own."""
     import os
     import subprocess
     import sys
