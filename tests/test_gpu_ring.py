@@ -55,6 +55,28 @@ def test_allreduce_bitwise(ccr_mod, ctx, dt, R, n, S):
     _assert_bitwise(got, oracle.ring_allreduce(xs, S=S), f"allreduce {dt} R={R} n={n}")
 
 
+SLICED = [(2, 17), (3, 1001), (7, 3), (5, 5 * 8192), (16, 4099), (33, 70001), (64, 131077)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("R,n", SLICED)
+@pytest.mark.parametrize("S", [2, 5])
+def test_sliced_ring_hops_bitwise(ccr_mod, ctx, dt, R, n, S):
+    """Slices run as separate launches only when something overlaps them:
+    with overlap on, every hop of slice s covers slice s of each chunk, so
+    the ring-hop kernel's slice geometry is exercised (offsets inside whole
+    chunks, the ragged chunk's own slices, empty slices of tiny chunks, the
+    16-, 32- and 64-slot rank tables)."""
+    ctx.set_config(ccr_mod.Config(overlap=True, slices=S))
+    xs = workloads.random_buffers(R, n, dt, seed=R * 7 + n + S, dist="normal", scale=1.0)
+    say(f"sliced allreduce {dt} R={R} n={n} S={S}")
+    got = _run(ccr_mod, ctx, xs)
+    _assert_bitwise(got, oracle.ring_allreduce(xs, S=S), f"sliced allreduce {dt} R={R} n={n} S={S}")
+    rs = _run(ccr_mod, ctx, xs, "reduce_scatter")
+    _assert_bitwise(rs, oracle.ring_reduce_scatter(xs, S=S), f"reduce_scatter {dt} R={R} n={n}")
+    ctx.set_config(ccr_mod.Config())
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("R,n", [(3, 1000), (8, 65536 + 9), (32, 40961)])
 def test_reduce_scatter_and_all_gather_bitwise(ccr_mod, ctx, dt, R, n):
