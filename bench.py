@@ -691,13 +691,15 @@ def workload_timings(ccr, workloads):
         bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
         b, R, N = 4, w.R, w.count
         cold = cold_ts = None
-        b2b = None
+        b2b = host_us = None
         with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
             if how == "allreduce":
                 ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs))
                 algo = b * N * (3 * (R - 1) + 1 + 2 * (R - 2))
                 # per call as nccl-tests times it: calls back to back between two events
                 b2b = back_to_back_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 100)
+                # host time to enqueue one call (its five launches), through the binding
+                host_us = host_call_us(ccr, lambda: ccr.ccr_allreduce(ctx, bufs))
                 if R * N * b <= (128 << 20):  # fits the 256 MB MALL: also time it cold
                     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
                     cold_ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs),
@@ -712,7 +714,8 @@ def workload_timings(ccr, workloads):
         out[w.name] = {"ms": round(ms, 4), **spread(ts), "cold_ms": None if cold is None else round(cold, 4),
                        **({"cold": spread(cold_ts)} if cold_ts else {}),
                        **({"back_to_back_ms": round(b2b, 4),
-                           "back_to_back_hbm_frac": round(algo / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "back_to_back_hbm_frac": round(algo / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "host_us_per_call": host_us}
                           if b2b else {}),
                        "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
                        "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),

@@ -67,6 +67,7 @@ _SIGNATURES = {
     "ccr_ctx_set_config": [_vp, ctypes.POINTER(ccr_config_t)],
     "ccr_ctx_get_config": [_vp, ctypes.POINTER(ccr_config_t)],
     "ccr_ring_schedule": [_i32, _i64, _i32, _i32, _i32, _vp, _i64, ctypes.POINTER(_i64)],
+    "ccr_ring_hop_layout": [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _i64, ctypes.POINTER(_i64)],
     "ccr_traffic_matrix": [_vp, _i32, _vp, _vp, _vp],
     "ccr_schedule_stages": [_vp, _i32, _vp, _vp, _i64, _i64, _vp, _i64, ctypes.POINTER(_i64), _vp,
                             _i64, ctypes.POINTER(_i64)],
@@ -292,6 +293,20 @@ def ccr_ring_schedule(R: int, count: int, slices: int, dtype: int, which: int = 
     out = np.zeros(n.value, RING_OP_DTYPE)
     _check(_lib.ccr_ring_schedule(R, count, slices, dtype, which,
                                   out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
+    return out
+
+
+def ccr_ring_hop_layout(R: int, count: int, slices: int, dtype: int, phase: int, step: int,
+                        slice: int = 0) -> np.ndarray:
+    """[workgroups x 5] int64: source rank, destination rank, byte offset and
+    byte length of the piece, tile index -- per workgroup of one ring-hop
+    launch, as the kernel maps them."""
+    n = ctypes.c_int64()
+    _check(_lib.ccr_ring_hop_layout(R, count, slices, dtype, phase, step, slice, None, 0,
+                                    ctypes.byref(n)))
+    out = np.zeros((n.value, 5), np.int64)
+    _check(_lib.ccr_ring_hop_layout(R, count, slices, dtype, phase, step, slice,
+                                    out.ctypes.data if n.value else None, n.value, ctypes.byref(n)))
     return out
 
 

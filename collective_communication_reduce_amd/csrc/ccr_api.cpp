@@ -1288,6 +1288,26 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
   return CCR_OK;
 }
 
+ccr_status_t ccr_ring_hop_layout(int R, int64_t count, int slices, int dtype, int phase, int step,
+                                 int slice, int64_t* rows, int64_t max_wg, int64_t* n_wg) {
+  if (!n_wg) return fail(CCR_ERR_INVALID_ARG, "n_wg is NULL");
+  if (R < 1 || R > kMaxRanks) return fail(CCR_ERR_INVALID_ARG, "R = %d outside [1, %d]", R, kMaxRanks);
+  if (count < 0 || slices < 1 || slices > 1024 || max_wg < 0)
+    return fail(CCR_ERR_INVALID_ARG, "bad count, slices or max_wg");
+  if (phase != kRS && phase != kAG) return fail(CCR_ERR_INVALID_ARG, "phase %d is not 0 or 1", phase);
+  if (step < 0 || step >= R - 1 || slice < 0 || slice >= slices)
+    return fail(CCR_ERR_INVALID_ARG, "step %d or slice %d out of range", step, slice);
+  const int esize = dtype_size(dtype);
+  if (!esize) return fail(CCR_ERR_INVALID_ARG, "dtype %d is not f32 (0) or bf16 (1)", dtype);
+  if (max_wg > 0 && !rows) return fail(CCR_ERR_INVALID_ARG, "rows is NULL");
+  const std::vector<void*> none((size_t)R, nullptr);  // the layout reads no base address
+  const RingHop h = ring_hop_desc(phase, step, slice, R, count, slices, 16 / esize, esize, none.data());
+  if (!ring_hop_supported(h, HopKind::kCopy, 0))
+    return fail(CCR_ERR_UNSUPPORTED, "the ring-hop kernel does not take this hop");
+  *n_wg = ring_hop_layout(h, rows, rows ? max_wg : 0);
+  return CCR_OK;
+}
+
 ccr_status_t ccr_traffic_matrix(const int64_t* C, int G, const int32_t* node, const int32_t* peer,
                                 int64_t* T) {
   CCR_MARK("ccr_traffic_matrix");

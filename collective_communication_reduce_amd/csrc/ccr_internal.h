@@ -97,6 +97,42 @@ struct RingHop {
 };
 constexpr int kRingHopMaxRanks = 64;
 
+// The scalar arguments of a ring-hop launch (16-byte vectors, int32): tiles
+// per full-chunk piece, full chunks, their stride, the slice's offset and
+// length inside a full chunk, and the rotation of the walk.
+struct RingLaunch {
+  int32_t tpp, nfull, stride_v, off_v, len_v, rot;
+};
+
+// Where workgroup b of a ring-hop launch works: chunk c, the tile of the
+// chunk's piece, and that piece's byte offset and length in every rank
+// buffer.  Workgroups below nfull * tpp take full chunks in the order rot,
+// rot + 1, ..., nfull - 1, 0, ..., rot - 1; the ones after them the ragged
+// chunk's piece.  Used by the kernel and, on the host, by ring_hop_layout.
+struct RingTile {
+  int c;
+  int64_t tile, off, len;
+};
+__host__ __device__ inline RingTile ring_tile(int b, const RingLaunch& g, int rag_c, int64_t rag_off,
+                                              int64_t rag_len) {
+  RingTile t;
+  const int nf = g.nfull * g.tpp;
+  if (b < nf) {
+    const int j = b / g.tpp;
+    t.tile = b - j * g.tpp;
+    const int c = j + g.rot;
+    t.c = c >= g.nfull ? c - g.nfull : c;
+    t.off = ((int64_t)t.c * g.stride_v + g.off_v) << 4;
+    t.len = (int64_t)g.len_v << 4;
+  } else {
+    t.c = rag_c;
+    t.tile = b - nf;
+    t.off = rag_off;
+    t.len = rag_len;
+  }
+  return t;
+}
+
 // Whether launch_ring_hop takes this hop (hop kinds of the ring, load modes
 // 0, 2 and 3, R <= 64, full-piece offsets within 2^31 vectors).
 bool ring_hop_supported(const RingHop& h, HopKind kind, int ntm);
@@ -106,6 +142,11 @@ int64_t ring_hop_workgroups(const RingHop& h);
 // in LaunchTuning::nontemporal); start/stop as for launch_pieces.
 hipError_t launch_ring_hop(HopKind kind, const RingHop& h, int ntm, hipStream_t stream,
                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The launch's workgroups as the kernel maps them, on the host: per
+// workgroup b, rows[5b..5b+4] = source rank, destination rank, byte offset
+// and byte length of its piece, tile index.  Returns the workgroup count
+// (rows written for at most max_wg of them).
+int64_t ring_hop_layout(const RingHop& h, int64_t* rows, int64_t max_wg);
 
 // Fused MoE dispatch / combine (one gather per row).  Per source rank r:
 // `rows` is x[r] (dispatch) or out[r] (combine) and `idx` is src_tok[r]

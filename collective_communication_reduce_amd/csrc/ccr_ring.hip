@@ -42,79 +42,71 @@ struct RingRest {
   char* base[NB + 2];
 };
 
-// Workgroup b < nfull * tpp: tile b - j * tpp of full chunk c = (j + rot)
-// mod nfull, j = b / tpp; the piece is len_v vectors at vector offset c * stride_v +
-// off_v of each rank buffer.  The workgroups after them: tiles of the ragged
-// chunk's piece.  Source rank (c + shift) mod R, destination the next rank,
-// forwarding to the one after.
+// Workgroup b works on the tile ring_tile gives it.  Source rank (c + shift)
+// mod R, destination the next rank, forwarding to the one after.  The
+// RingLaunch fields arrive as separate scalars: only scalar arguments are
+// preloaded into registers, a by-value struct would be read from memory.
 template <HopKind K, int NTM, int NB>
 __global__ __launch_bounds__(kBlock) void ring_hop_kernel(int32_t R, int32_t shift, int32_t tpp,
                                                           int32_t nfull, int32_t stride_v, int32_t off_v,
                                                           int32_t len_v, int32_t rot, RingRest<NB> a) {
-  const int b = blockIdx.x;
-  const int nf = nfull * tpp;
-  int c;
-  int64_t tile, off, len;
-  if (b < nf) {
-    const int j = b / tpp;
-    tile = b - j * tpp;
-    c = j + rot;
-    c = c >= nfull ? c - nfull : c;
-    off = ((int64_t)c * stride_v + off_v) << 4;
-    len = (int64_t)len_v << 4;
-  } else {
-    c = a.rag_c;
-    tile = b - nf;
-    off = a.rag_off;
-    len = a.rag_len;
-  }
-  int s = c + shift;  // c < R and shift < R
+  const RingLaunch g{tpp, nfull, stride_v, off_v, len_v, rot};
+  const RingTile t = ring_tile(blockIdx.x, g, a.rag_c, a.rag_off, a.rag_len);
+  int s = t.c + shift;  // c < R and shift < R
   s = s >= R ? s - R : s;
   char* const* const ranks = a.base + s;  // source, destination, the rank after
   char* dst2 = nullptr;
-  if constexpr (forwards<K>()) dst2 = ranks[2] + off;
-  hop_tile<K, 2, NTM>(ranks[1] + off, ranks[0] + off, dst2, len, tile);
+  if constexpr (forwards<K>()) dst2 = ranks[2] + t.off;
+  hop_tile<K, 2, NTM>(ranks[1] + t.off, ranks[0] + t.off, dst2, t.len, t.tile);
+}
+
+constexpr int64_t kTileBytes = (int64_t)kBlock * 2 * 16;
+
+RingLaunch ring_launch(const RingHop& h) {
+  RingLaunch g;
+  g.tpp = (int32_t)((h.full_len + kTileBytes - 1) / kTileBytes);
+  g.nfull = h.nfull;
+  g.stride_v = (int32_t)(h.stride >> 4);
+  g.off_v = (int32_t)(h.full_off >> 4);
+  g.len_v = (int32_t)(h.full_len >> 4);
+  g.rot = h.rot;
+  return g;
 }
 
 template <HopKind K, int NTM, int NB>
-hipError_t launch_nb(const RingHop& h, unsigned grid, int32_t tpp, hipStream_t s, hipEvent_t start,
-                     hipEvent_t stop) {
+hipError_t launch_nb(const RingHop& h, unsigned grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   RingRest<NB> a{};
   a.rag_off = h.rag_off;
   a.rag_len = h.rag_len;
   a.rag_c = h.rag_c;
   for (int r = 0; r < h.R + 2; r++) a.base[r] = h.base[r % h.R];
-  const int32_t stride_v = (int32_t)(h.stride >> 4), off_v = (int32_t)(h.full_off >> 4),
-                len_v = (int32_t)(h.full_len >> 4);
+  const RingLaunch g = ring_launch(h);
   if (start && stop)
     hipExtLaunchKernelGGL(ring_hop_kernel<K, NTM, NB>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0,
-                          h.R, h.shift, tpp, h.nfull, stride_v, off_v, len_v, h.rot, a);
+                          h.R, h.shift, g.tpp, g.nfull, g.stride_v, g.off_v, g.len_v, g.rot, a);
   else
-    ring_hop_kernel<K, NTM, NB><<<grid, kBlock, 0, s>>>(h.R, h.shift, tpp, h.nfull, stride_v, off_v,
-                                                        len_v, h.rot, a);
+    ring_hop_kernel<K, NTM, NB><<<grid, kBlock, 0, s>>>(h.R, h.shift, g.tpp, g.nfull, g.stride_v, g.off_v,
+                                                        g.len_v, g.rot, a);
   return hipGetLastError();
 }
 
 template <HopKind K, int NTM>
-hipError_t launch_ntm(const RingHop& h, unsigned grid, int32_t tpp, hipStream_t s, hipEvent_t start,
-                      hipEvent_t stop) {
-  if (h.R <= 8) return launch_nb<K, NTM, 8>(h, grid, tpp, s, start, stop);
-  if (h.R <= 16) return launch_nb<K, NTM, 16>(h, grid, tpp, s, start, stop);
-  if (h.R <= 32) return launch_nb<K, NTM, 32>(h, grid, tpp, s, start, stop);
-  return launch_nb<K, NTM, 64>(h, grid, tpp, s, start, stop);
+hipError_t launch_ntm(const RingHop& h, unsigned grid, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  if (h.R <= 8) return launch_nb<K, NTM, 8>(h, grid, s, start, stop);
+  if (h.R <= 16) return launch_nb<K, NTM, 16>(h, grid, s, start, stop);
+  if (h.R <= 32) return launch_nb<K, NTM, 32>(h, grid, s, start, stop);
+  return launch_nb<K, NTM, 64>(h, grid, s, start, stop);
 }
 
 template <HopKind K>
-hipError_t launch_kind(const RingHop& h, int ntm, unsigned grid, int32_t tpp, hipStream_t s,
-                       hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_kind(const RingHop& h, int ntm, unsigned grid, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop) {
   switch (ntm) {
-    case 2: return launch_ntm<K, 2>(h, grid, tpp, s, start, stop);
-    case 3: return launch_ntm<K, 3>(h, grid, tpp, s, start, stop);
-    default: return launch_ntm<K, 0>(h, grid, tpp, s, start, stop);
+    case 2: return launch_ntm<K, 2>(h, grid, s, start, stop);
+    case 3: return launch_ntm<K, 3>(h, grid, s, start, stop);
+    default: return launch_ntm<K, 0>(h, grid, s, start, stop);
   }
 }
-
-constexpr int64_t kTileBytes = (int64_t)kBlock * 2 * 16;
 
 }  // namespace
 
@@ -143,21 +135,36 @@ int64_t ring_hop_workgroups(const RingHop& h) {
 hipError_t launch_ring_hop(HopKind kind, const RingHop& h, int ntm, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
   if (!ring_hop_supported(h, kind, ntm)) return hipErrorInvalidValue;
-  const int32_t tpp = (int32_t)((h.full_len + kTileBytes - 1) / kTileBytes);
   const int64_t grid = ring_hop_workgroups(h);
   if (grid == 0) return hipSuccess;
   switch (kind) {
     case HopKind::kReduceF32:
-      return launch_kind<HopKind::kReduceF32>(h, ntm, (unsigned)grid, tpp, stream, start, stop);
+      return launch_kind<HopKind::kReduceF32>(h, ntm, (unsigned)grid, stream, start, stop);
     case HopKind::kReduceBf16:
-      return launch_kind<HopKind::kReduceBf16>(h, ntm, (unsigned)grid, tpp, stream, start, stop);
+      return launch_kind<HopKind::kReduceBf16>(h, ntm, (unsigned)grid, stream, start, stop);
     case HopKind::kReduceFwdF32:
-      return launch_kind<HopKind::kReduceFwdF32>(h, ntm, (unsigned)grid, tpp, stream, start, stop);
+      return launch_kind<HopKind::kReduceFwdF32>(h, ntm, (unsigned)grid, stream, start, stop);
     case HopKind::kReduceFwdBf16:
-      return launch_kind<HopKind::kReduceFwdBf16>(h, ntm, (unsigned)grid, tpp, stream, start, stop);
+      return launch_kind<HopKind::kReduceFwdBf16>(h, ntm, (unsigned)grid, stream, start, stop);
     default:
-      return launch_kind<HopKind::kCopy>(h, ntm, (unsigned)grid, tpp, stream, start, stop);
+      return launch_kind<HopKind::kCopy>(h, ntm, (unsigned)grid, stream, start, stop);
   }
+}
+
+int64_t ring_hop_layout(const RingHop& h, int64_t* rows, int64_t max_wg) {
+  const int64_t n = ring_hop_workgroups(h);
+  const RingLaunch g = ring_launch(h);
+  for (int64_t b = 0; b < n && b < max_wg; b++) {
+    const RingTile t = ring_tile((int)b, g, h.rag_c, h.rag_off, h.rag_len);
+    const int s = (t.c + h.shift) % h.R;
+    int64_t* row = rows + 5 * b;
+    row[0] = s;
+    row[1] = (s + 1) % h.R;
+    row[2] = t.off;
+    row[3] = t.len;
+    row[4] = t.tile;
+  }
+  return n;
 }
 
 }  // namespace ccr

@@ -238,6 +238,20 @@ typedef struct {
 ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int which,
                                ccr_ring_op_t *ops, int64_t max_ops, int64_t *n_ops);
 
+/* The workgroups of one ring-hop launch, as the kernel maps them (host only,
+ * no device work; the kernel's index arithmetic, computed by the same
+ * function on the host, for tests).  Hop `step` of `phase` (0 = reduce-
+ * scatter, 1 = all-gather) on slice `slice`, over the partition above.  The
+ * launch has one workgroup per 2 x 256 16-byte vectors of each rank's
+ * piece; per workgroup five int64: source rank, destination rank, byte
+ * offset and byte length of its piece (the same in every rank buffer), and
+ * the tile index within the piece.  Writes at most max_wg rows (rows holds
+ * 5 * max_wg values); *n_wg receives the workgroup count (query with
+ * rows = NULL, max_wg = 0).  CCR_ERR_UNSUPPORTED when the ring-hop kernel
+ * does not take the hop (it then runs from a piece table). */
+ccr_status_t ccr_ring_hop_layout(int R, int64_t count, int slices, int dtype, int phase, int step,
+                                 int slice, int64_t *rows, int64_t max_wg, int64_t *n_wg);
+
 /* ----------------------------------------------------------------------
  * Stage schedule of a collective's traffic (host only, no device work).
  *

@@ -154,3 +154,78 @@ def test_dma_pace_is_the_fewest_engines_that_meet_the_deadline(nbytes, deadline_
     assert ccr.ccr_dma_pace(nbytes, deadline_us, 0.0, max_e) == max_e
     assert ccr.ccr_dma_pace(0, deadline_us, gbs, max_e) == max_e
     assert ccr.ccr_dma_pace(nbytes, deadline_us, gbs, 0) == 0
+
+
+TILE_BYTES = 2 * 256 * 16  # a ring-hop workgroup's tile: 2 x 256 16-byte vectors
+
+
+@pytest.mark.parametrize("R,count,S,dtype", [
+    (2, 1, 1, 0), (2, 1000, 3, 1), (3, 8, 1, 0), (3, 1001, 2, 0), (4, 4096 * 3 + 5, 1, 0),
+    (5, 5 * 8192, 5, 1), (7, 3, 2, 1), (8, 26214400, 1, 1), (16, 4099, 5, 0), (17, 100003, 1, 1),
+    (32, 8 * 1048576, 1, 0), (33, 70001, 2, 1), (64, 131077, 5, 0), (64, 2049, 1, 1),
+    (4, 64, 5, 1), (6, 3 * 65536 + 11, 4, 0)])
+def test_ring_hop_layout_covers_the_schedule(R, count, S, dtype):
+    """The ring-hop kernel's own index arithmetic (the function the kernel
+    runs, called on the host): for every hop, its workgroups cover exactly
+    the pieces the ring schedule lists for that hop -- every byte of every
+    piece once, each piece's tiles contiguous and in order, the full chunks
+    in destination-rank order (the ragged chunk last), so a hop starts on
+    the chunk the previous hop wrote last."""
+    esize = 4 if dtype == 0 else 2
+    ops = ccr.ccr_ring_schedule(R, count, S, dtype, which=0)
+    for s in range(S):
+        for phase in (0, 1):
+            for k in range(R - 1):
+                hop = ops[(ops["slice"] == s) & (ops["phase"] == phase) & (ops["step"] == k)]
+                want = sorted((int(o["src_rank"]), int(o["dst_rank"]), int(o["lo"]) * esize,
+                               int(o["hi"] - o["lo"]) * esize) for o in hop if o["hi"] > o["lo"])
+                rows = ccr.ccr_ring_hop_layout(R, count, S, dtype, phase, k, s)
+                pieces = [tuple(int(x) for x in r[:4]) for r in rows]
+                # runs of one piece each, tiles 0, 1, ... in workgroup order
+                runs = []
+                for i, p in enumerate(pieces):
+                    if not runs or runs[-1][0] != p:
+                        runs.append((p, []))
+                    runs[-1][1].append(int(rows[i, 4]))
+                assert sorted(p for p, _ in runs) == want, (s, phase, k)
+                for p, tiles in runs:
+                    assert tiles == list(range(-(-p[3] // TILE_BYTES))), (p, tiles[:4])
+                # whole chunks (c < count // L) before the ragged one, in
+                # destination-rank order
+                V = 16 // esize
+                L = -(-(-(-count // R)) // V) * V
+                chunk = [p[2] // (L * esize) for p, _ in runs]
+                whole = [c for c in chunk if c < count // L]
+                assert chunk[:len(whole)] == whole and len(chunk) <= len(whole) + 1
+                if len(whole) == R:
+                    assert [p[1] for p, _ in runs] == list(range(R)), [p[1] for p, _ in runs]
+
+
+def test_ring_hop_layout_past_32_bit_offsets():
+    """3 ranks of 2^31 + 12345 bf16: byte offsets past 4 GiB, the ragged end
+    in the last chunk; vectorised over the ~525,000 workgroups of a hop."""
+    R, count = 3, (1 << 31) + 12345
+    for phase, k in ((0, 0), (0, 1), (1, 1)):
+        rows = ccr.ccr_ring_hop_layout(R, count, 1, 1, phase, k, 0)
+        ops = ccr.ccr_ring_schedule(R, count, 1, 1, which=0)
+        hop = ops[(ops["phase"] == phase) & (ops["step"] == k)]
+        want = sorted((int(o["src_rank"]), int(o["dst_rank"]), int(o["lo"]) * 2,
+                       int(o["hi"] - o["lo"]) * 2) for o in hop)
+        keys, first = np.unique(rows[:, :4], axis=0, return_index=True)
+        assert sorted(tuple(int(x) for x in r) for r in keys) == want
+        for key in keys:
+            t = rows[np.all(rows[:, :4] == key, axis=1), 4]
+            assert np.array_equal(t, np.arange(-(-int(key[3]) // TILE_BYTES)))
+
+
+def test_ring_hop_layout_refuses_what_the_kernel_does_not_take():
+    # a chunk stride past 2^31 16-byte vectors (32 GiB per chunk): the hop
+    # runs from a piece table instead
+    with pytest.raises(ccr.CcrError) as e:
+        ccr.ccr_ring_hop_layout(2, 1 << 36, 1, 0, 0, 0)
+    assert e.value.status == ccr.CCR_ERR_UNSUPPORTED
+    for args in [(1, 10, 1, 0, 0, 0), (4, 10, 1, 0, 2, 0), (4, 10, 1, 0, 0, 3), (4, 10, 2, 0, 0, 0, 2),
+                 (4, 10, 1, 5, 0, 0)]:
+        with pytest.raises(ccr.CcrError) as e:
+            ccr.ccr_ring_hop_layout(*args)
+        assert e.value.status == ccr.CCR_ERR_INVALID_ARG
