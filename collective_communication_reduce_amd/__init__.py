@@ -158,6 +158,10 @@ def ccr_last_error() -> str:
 
 
 # ------------------------------------------------------------------ config
+CCR_DMA_SYNC_HOST_FUNC, CCR_DMA_SYNC_STREAM_FLAGS = 0, 1  # ccr_dma_sync_t
+_DMA_SYNC = {"host_func": CCR_DMA_SYNC_HOST_FUNC, "stream_flags": CCR_DMA_SYNC_STREAM_FLAGS}
+
+
 @dataclass
 class Config:
     copy_mode: str = "kernel"        # "kernel" | "sdma"
@@ -175,12 +179,14 @@ class Config:
     dma_deadline_us: int = 0         # SDMA: time a call's copies may take; > 0 paces the engines
 
     def to_c(self) -> ccr_config_t:
+        if self.dma_sync not in _DMA_SYNC:
+            raise ValueError(f"dma_sync {self.dma_sync!r} is not one of {sorted(_DMA_SYNC)}")
         return ccr_config_t(CCR_COPY_SDMA if self.copy_mode == "sdma" else CCR_COPY_KERNEL,
                             self.cu_budget, self.slices, int(self.overlap),
                             self.staging_chunk_bytes, self.staging_slots,
                             CCR_BF16_ACC_FP32_PARTIALS if self.bf16_acc == "fp32_partials"
                             else CCR_BF16_ACC_PER_HOP, self.dma_stripe, self.dma_chunk_bytes,
-                            1 if self.dma_sync == "stream_flags" else 0, self.dma_engines,
+                            _DMA_SYNC[self.dma_sync], self.dma_engines,
                             int(self.graph_cache), self.dma_deadline_us)
 
     @staticmethod
@@ -189,7 +195,7 @@ class Config:
                       c.slices, bool(c.overlap), c.staging_chunk_bytes, c.staging_slots,
                       "fp32_partials" if c.bf16_acc == CCR_BF16_ACC_FP32_PARTIALS else "per_hop",
                       c.dma_stripe, c.dma_chunk_bytes,
-                      "stream_flags" if c.dma_sync == 1 else "host_func", c.dma_engines,
+                      {v: k for k, v in _DMA_SYNC.items()}.get(c.dma_sync, "host_func"), c.dma_engines,
                       bool(c.graph_cache), c.dma_deadline_us)
 
 

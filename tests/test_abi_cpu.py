@@ -229,3 +229,13 @@ def test_ring_hop_layout_refuses_what_the_kernel_does_not_take():
         with pytest.raises(ccr.CcrError) as e:
             ccr.ccr_ring_hop_layout(*args)
         assert e.value.status == ccr.CCR_ERR_INVALID_ARG
+
+
+def test_config_names_are_checked_when_marshalled():
+    """The binding maps the SDMA hand-over names to ccr_dma_sync_t values and
+    refuses a name it does not know instead of sending a default."""
+    for name, code in (("host_func", ccr.CCR_DMA_SYNC_HOST_FUNC), ("stream_flags", ccr.CCR_DMA_SYNC_STREAM_FLAGS)):
+        c = ccr.Config(copy_mode="sdma", dma_sync=name).to_c()
+        assert c.dma_sync == code and ccr.Config.from_c(c).dma_sync == name
+    with pytest.raises(ValueError):
+        ccr.Config(dma_sync="runtime").to_c()
