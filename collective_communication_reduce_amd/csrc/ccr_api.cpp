@@ -558,7 +558,7 @@ RingHop ring_hop_desc(int phase, int k, int s, int R, int64_t count, int S, int 
   // chunk 0; walking every other hop backwards instead was slower still).
   const int first = (2 * R - h.shift - 1) % R;
   h.rot = first < h.nfull ? first : 0;
-  h.base = reinterpret_cast<char* const*>(bufs);
+  h.base = bufs;
   return h;
 }
 

@@ -93,7 +93,7 @@ struct RingHop {
   int64_t full_off = 0, full_len = 0;
   int rag_c = 0;
   int64_t rag_off = 0, rag_len = 0;
-  char* const* base = nullptr;  // R rank buffers
+  void* const* base = nullptr;  // R rank buffers
 };
 constexpr int kRingHopMaxRanks = 64;
 

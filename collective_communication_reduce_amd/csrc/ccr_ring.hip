@@ -79,7 +79,7 @@ hipError_t launch_nb(const RingHop& h, unsigned grid, hipStream_t s, hipEvent_t 
   a.rag_off = h.rag_off;
   a.rag_len = h.rag_len;
   a.rag_c = h.rag_c;
-  for (int r = 0; r < h.R + 2; r++) a.base[r] = h.base[r % h.R];
+  for (int r = 0; r < h.R + 2; r++) a.base[r] = static_cast<char*>(h.base[r % h.R]);
   const RingLaunch g = ring_launch(h);
   if (start && stop)
     hipExtLaunchKernelGGL(ring_hop_kernel<K, NTM, NB>, dim3(grid), dim3(kBlock), 0, s, start, stop, 0,
