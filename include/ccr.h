@@ -218,6 +218,9 @@ ccr_status_t ccr_ctx_get_config(ccr_ctx_t ctx, ccr_config_t *cfg);
 /* ----------------------------------------------------------------------
  * Ring schedule (host only, no device work).
  *
+ * HOCCL §2.1 and Figure 1: the ring all-reduce as R-1 reduce-scatter steps
+ * and R-1 all-gather steps, each rank sending one chunk to the next rank per
+ * step; §3.3.1 cuts a chunk into slices (chunk pipelining).
  * One record per (hop, rank): the operation rank dst_rank performs in that
  * hop, on elements [lo, hi) of chunk `chunk`, reading rank src_rank's buffer.
  * phase 0 = reduce-scatter (dst += src), 1 = all-gather (dst = src).
@@ -240,7 +243,8 @@ ccr_status_t ccr_ring_schedule(int R, int64_t count, int slices, int dtype, int 
 
 /* The workgroups of one ring-hop launch, as the kernel maps them (host only,
  * no device work; the kernel's index arithmetic, computed by the same
- * function on the host, for tests).  Hop `step` of `phase` (0 = reduce-
+ * function on the host, for tests): one step of the ring of HOCCL §2.1,
+ * Figure 1, as the device runs it.  Hop `step` of `phase` (0 = reduce-
  * scatter, 1 = all-gather) on slice `slice`, over the partition above.  The
  * launch has one workgroup per 2 x 256 16-byte vectors of each rank's
  * piece; per workgroup five int64: source rank, destination rank, byte
