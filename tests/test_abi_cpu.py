@@ -163,7 +163,10 @@ TILE_BYTES = 2 * 256 * 16  # a ring-hop workgroup's tile: 2 x 256 16-byte vector
     (2, 1, 1, 0), (2, 1000, 3, 1), (3, 8, 1, 0), (3, 1001, 2, 0), (4, 4096 * 3 + 5, 1, 0),
     (5, 5 * 8192, 5, 1), (7, 3, 2, 1), (8, 26214400, 1, 1), (16, 4099, 5, 0), (17, 100003, 1, 1),
     (32, 8 * 1048576, 1, 0), (33, 70001, 2, 1), (64, 131077, 5, 0), (64, 2049, 1, 1),
-    (4, 64, 5, 1), (6, 3 * 65536 + 11, 4, 0)])
+    (4, 64, 5, 1), (6, 3 * 65536 + 11, 4, 0),
+    # whole chunks of 48 bf16 and a ragged one of 40, 5 slices: slices 3 and 4
+    # of a whole chunk are empty while slice 3 of the ragged chunk is not
+    (2, 88, 5, 1)])
 def test_ring_hop_layout_covers_the_schedule(R, count, S, dtype):
     """The ring-hop kernel's own index arithmetic (the function the kernel
     runs, called on the host): for every hop, its workgroups cover exactly

@@ -55,7 +55,8 @@ def test_allreduce_bitwise(ccr_mod, ctx, dt, R, n, S):
     _assert_bitwise(got, oracle.ring_allreduce(xs, S=S), f"allreduce {dt} R={R} n={n}")
 
 
-SLICED = [(2, 17), (3, 1001), (7, 3), (5, 5 * 8192), (16, 4099), (33, 70001), (64, 131077)]
+SLICED = [(2, 17), (3, 1001), (7, 3), (5, 5 * 8192), (16, 4099), (33, 70001), (64, 131077),
+          (2, 88)]  # bf16: whole-chunk slices 3-4 empty, the ragged chunk's slice 3 not
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
