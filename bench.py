@@ -658,6 +658,14 @@ def workload_probe(ccr, workloads, name, steps):
                     dst.copy_(bufs[0])
                     ccr._check(ccr._lib.ccr_probe_cu_ids(ctx.handle, ids.data_ptr(), 512, None))
                 torch.cuda.synchronize()
+                # the same call and the same empty kernel replayed from HIP
+                # graphs, so that the GPU dispatches them back to back with no
+                # host in the loop (the trace's gaps are then the GPU's own)
+                g_call, g_empty = launch_floor_graphs(ccr, ctx, bufs, ids)
+                for _ in range(max(1, steps // 10)):
+                    g_call.replay()
+                    g_empty.replay()
+                torch.cuda.synchronize()
     elif name == "pp_sendrecv_4x2048x4096_bf16":
         pw = workloads.PP_STAGING_BF16
         mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
@@ -681,6 +689,33 @@ def workload_probe(ccr, workloads, name, steps):
     log(f"workload probe: {steps} calls of {name}")
 
 
+def launch_floor_graphs(ccr, ctx, bufs, ids, calls=10):
+    """Two HIP graphs captured on a side stream: `calls` all-reduce calls of
+    `bufs`, and 5 * `calls` launches in a row of the empty 512-workgroup probe
+    kernel (it only records CU ids into `ids`), i.e. `calls` chains of as many
+    launches as the 4-rank call makes.  Replayed, the GPU runs them back to
+    back without waiting for the host."""
+    import torch
+    ccr._check(ccr._lib.ccr_probe_cu_ids(ctx.handle, ids.data_ptr(), 512, None))  # side stream made eagerly
+    torch.cuda.synchronize()
+    gs = torch.cuda.Stream()
+    g_call, g_empty = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_call, stream=gs):
+        for _ in range(calls):
+            ccr.ccr_allreduce(ctx, bufs)
+    with torch.cuda.graph(g_empty, stream=gs):
+        for _ in range(5 * calls):
+            ccr._check(ccr._lib.ccr_probe_cu_ids(ctx.handle, ids.data_ptr(), 512, gs.cuda_stream))
+    torch.cuda.synchronize()
+    return g_call, g_empty
+
+
+def graph_per_call_us(g, calls, reps=10):
+    """Median over `reps` replays of one replay's event time, per call (us)."""
+    ts = event_times(g.replay, reps=reps, warm=2)
+    return round(sorted(ts)[len(ts) // 2] * 1e3 / calls, 2)
+
+
 def workload_timings(ccr, workloads):
     """The other workloads, for context (each is also a full-size parity
     test): per call, 5 untimed warm-up calls, then 20 calls each timed alone
@@ -691,7 +726,7 @@ def workload_timings(ccr, workloads):
         bufs = [torch.rand(w.count, device="cuda") * 2 - 1 for _ in range(w.R)]
         b, R, N = 4, w.R, w.count
         cold = cold_ts = None
-        b2b = host_us = None
+        b2b = host_us = floor = None
         with ccr.Context(0, ccr.Config(slices=w.slices)) as ctx:
             if how == "allreduce":
                 ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs))
@@ -700,6 +735,13 @@ def workload_timings(ccr, workloads):
                 b2b = back_to_back_ms(lambda: ccr.ccr_allreduce(ctx, bufs), 100)
                 # host time to enqueue one call (its five launches), through the binding
                 host_us = host_call_us(ccr, lambda: ccr.ccr_allreduce(ctx, bufs))
+                # the GPU alone: the call, and 5 launches of an empty kernel of
+                # the copy hop's 512 workgroups, each replayed from a graph
+                ids = torch.zeros(512, 3, dtype=torch.int32, device="cuda")
+                g_call, g_empty = launch_floor_graphs(ccr, ctx, bufs, ids)
+                floor = {"graph_replay_us_per_call": graph_per_call_us(g_call, 10),
+                         "empty_5_launches_us": round(5 * graph_per_call_us(g_empty, 50), 2)}
+                del g_call, g_empty
                 if R * N * b <= (128 << 20):  # fits the 256 MB MALL: also time it cold
                     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
                     cold_ts = event_times(lambda: ccr.ccr_allreduce(ctx, bufs),
@@ -715,7 +757,7 @@ def workload_timings(ccr, workloads):
                        **({"cold": spread(cold_ts)} if cold_ts else {}),
                        **({"back_to_back_ms": round(b2b, 4),
                            "back_to_back_hbm_frac": round(algo / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "host_us_per_call": host_us}
+                           "host_us_per_call": host_us, "launch_floor": floor}
                           if b2b else {}),
                        "busbw_gbs": round(b * N / (ms * 1e-3) * 2 * (R - 1) / R / 1e9, 1),
                        "algorithmic_gbs": round(algo / (ms * 1e-3) / 1e9, 1),
@@ -861,16 +903,20 @@ def schedule_timings(ccr, workloads):
             "host_us_per_call": round(float(np.median(reps)) * 1e6, 1)}
 
 
-def host_call_us(ccr, call, reps=50):
-    """Host time per enqueue (HOCCL Fig. 9 measures CPU launch time per op)."""
+def host_call_us(ccr, call, reps=50, windows=7):
+    """Host time per enqueue (HOCCL Fig. 9 measures CPU launch time per op):
+    the median over `windows` loops of `reps` calls each, so that one
+    preemption of the host thread does not decide the figure."""
     import torch
+    per = []
+    for _ in range(windows):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            call()
+        per.append((time.perf_counter() - t) / reps)
     torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(reps):
-        call()
-    dt = (time.perf_counter() - t) / reps
-    torch.cuda.synchronize()
-    return round(dt * 1e6, 2)
+    return round(sorted(per)[len(per) // 2] * 1e6, 2)
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "ring_allreduce_dp_bucket_r8_bf16_hbm_counters.md")
