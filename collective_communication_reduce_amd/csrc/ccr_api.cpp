@@ -193,7 +193,7 @@ ccr_status_t check_config(const ccr_config_t* c) {
 }
 
 // Compute units of the CU mask for a budget of B: mask bit i is handed to
-// XCC (i mod num_xcc) by the driver, so the lowest B bits spread the budget
+// XCC (i mod num_xcc) by the kernel-mode GPU driver, so the lowest B bits spread the budget
 // evenly over the XCDs.
 std::vector<uint32_t> cu_mask_for_budget(int budget, int num_cus) {
   std::vector<uint32_t> mask((size_t)(num_cus + 31) / 32, 0u);
