@@ -27,6 +27,10 @@ constexpr int kMaxPieces = 64;
 // Threads per workgroup of the streaming kernels: four wave64 wavefronts.
 constexpr int kBlock = 256;
 
+// A dispatch counts its grid in work-items, in 32 bits, so one launch of
+// kBlock-thread workgroups takes at most this many of them (2^24 - 1).
+constexpr int64_t kMaxGridWorkgroups = int64_t(UINT32_MAX) / kBlock;
+
 // kReduce*: dst = dst + src.  kReduceFwd*: the same, and the result is also
 // written to dst2 (the last reduce-scatter hop forwarding the reduced chunk
 // to the next rank, which replaces the first all-gather hop).  kCopy:
@@ -134,7 +138,8 @@ __host__ __device__ inline RingTile ring_tile(int b, const RingLaunch& g, int ra
 }
 
 // Whether launch_ring_hop takes this hop (hop kinds of the ring, load modes
-// 0, 2 and 3, R <= 64, full-piece offsets within 2^31 vectors).
+// 0, 2 and 3, R <= 64, full-piece offsets within 2^31 vectors, at most
+// kMaxGridWorkgroups tiles).
 bool ring_hop_supported(const RingHop& h, HopKind kind, int ntm);
 // Workgroups of its launch: one per 2 x kBlock 16-byte vectors of a piece.
 int64_t ring_hop_workgroups(const RingHop& h);

@@ -70,6 +70,7 @@ template <HopKind K, int U, int NTM, int NP>
 hipError_t launch_one(const PieceArgs<NP>& a, hipStream_t s, Timing t, int grid_cap) {
   int grid = a.tile_start[a.n];
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+  if (grid > kMaxGridWorkgroups) grid = (int)kMaxGridWorkgroups;  // the workgroups loop over the rest
   if (t.start && t.stop)
     hipExtLaunchKernelGGL(pieces_kernel<K, U, NTM, NP>, dim3(grid), dim3(kBlock), 0, s, t.start,
                           t.stop, 0, a);
@@ -260,7 +261,8 @@ hipError_t launch_pieces_np(HopKind kind, const Piece* pieces, int n, LaunchTuni
     const int64_t nvec = pieces[i].nbytes >> 4;
     const int64_t units = nvec + ((pieces[i].nbytes & 15) ? 1 : 0);
     tiles += (units + per_tile - 1) / per_tile;
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    // tile indices and a workgroup's next tile (b + gridDim.x) stay in int32
+    if (tiles > INT32_MAX - kMaxGridWorkgroups) return hipErrorInvalidValue;
   }
   for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;
@@ -310,7 +312,7 @@ hipError_t launch_partials_np(PartialKind kind, const PartialPiece* pieces, int 
     a.tile_start[i] = (int32_t)tiles;
     const int64_t units = (pieces[i].n >> 3) + ((pieces[i].n & 7) ? 1 : 0);
     tiles += (units + per_tile - 1) / per_tile;
-    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    if (tiles > kMaxGridWorkgroups) return hipErrorInvalidValue;  // one workgroup per tile
   }
   for (int i = n; i <= NP; i++) a.tile_start[i] = (int32_t)tiles;
   if (tiles == 0) return hipSuccess;

@@ -232,7 +232,7 @@ hipError_t launch_permute_rows(char* dst, const char* src, const int32_t* idx, i
   if (nrows <= 0 || row_bytes <= 0) return hipSuccess;
   constexpr int kRpb = 4;
   const int64_t grid = (nrows + kRpb - 1) / kRpb;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (grid > kMaxGridWorkgroups) return hipErrorInvalidValue;
   permute_rows_kernel<kRpb><<<(unsigned)grid, kBlock, 0, stream>>>(
       reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), idx, nrows, nsrc,
       row_bytes >> 4);
@@ -245,7 +245,7 @@ hipError_t launch_gather_rpb(int combine, const MoeRank* ranks, const MoeSeg* se
                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int64_t per_rank = (rows_per_rank + RPB - 1) / RPB;
   const int64_t grid = per_rank * R;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (grid > kMaxGridWorkgroups) return hipErrorInvalidValue;
   if (start && stop)
     hipExtLaunchKernelGGL(moe_gather_kernel<RPB, NTL>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
                           start, stop, 0, ranks, segs, E, rows_per_rank, idx_limit, row_bytes >> 4,
@@ -294,7 +294,7 @@ hipError_t launch_moe_topk(const float* logits, int32_t* topk, int64_t T, int E,
   if (T <= 0 || K <= 0) return hipSuccess;
   if (E > 64 * kTopkMaxPerLane) return hipErrorInvalidValue;
   const int64_t grid = (T + kBlock / 64 - 1) / (kBlock / 64);
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (grid > kMaxGridWorkgroups) return hipErrorInvalidValue;
   topk_kernel<<<(unsigned)grid, kBlock, 0, stream>>>(logits, topk, T, E, K);
   return hipGetLastError();
 }

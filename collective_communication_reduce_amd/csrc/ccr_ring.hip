@@ -122,9 +122,11 @@ bool ring_hop_supported(const RingHop& h, HopKind kind, int ntm) {
   // full pieces: whole 16-byte vectors, offsets and lengths in int32 vectors
   if ((h.stride | h.full_off | h.full_len) & 15) return false;
   if ((h.stride >> 4) > INT32_MAX || ((h.full_off + h.full_len) >> 4) > INT32_MAX) return false;
+  // one workgroup per tile, within one dispatch's grid (the piece-table
+  // launch, whose workgroups loop over tiles, takes larger hops)
   const int64_t tpp = (h.full_len + kTileBytes - 1) / kTileBytes;
   const int64_t rag_tiles = (h.rag_len + kTileBytes - 1) / kTileBytes;
-  return (int64_t)h.nfull * tpp + rag_tiles <= INT32_MAX;
+  return (int64_t)h.nfull * tpp + rag_tiles <= kMaxGridWorkgroups;
 }
 
 int64_t ring_hop_workgroups(const RingHop& h) {

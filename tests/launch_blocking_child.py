@@ -2,8 +2,8 @@
 staged send/recv through the library on inputs from an .npz file and saves
 the results.  Started with a variable in its environment that is read once
 per process (HIP_LAUNCH_BLOCKING=1, read when HIP initialises, a forced
-CCR_NONTEMPORAL mode, or CCR_RING_HOPS), so each setting needs a process of
-its own
+CCR_NONTEMPORAL mode, CCR_RING_HOPS or a CCR_GRID cap), so each setting needs
+a process of its own
 (marshalling only: no reference arithmetic here)."""
 import os
 import sys

@@ -227,6 +227,16 @@ def test_ring_hop_layout_refuses_what_the_kernel_does_not_take():
     with pytest.raises(ccr.CcrError) as e:
         ccr.ccr_ring_hop_layout(2, 1 << 36, 1, 0, 0, 0)
     assert e.value.status == ccr.CCR_ERR_UNSUPPORTED
+    # one workgroup per 8 KiB tile, and a dispatch counts at most 2^32 - 1
+    # work-items (2^24 - 1 workgroups of 256): 8 chunks of 2^21 tiles plus one
+    # tile each are refused, 8 chunks of 2^21 - 1 tiles are taken
+    with pytest.raises(ccr.CcrError) as e:
+        ccr.ccr_ring_hop_layout(8, (1 << 35) + 64, 1, 0, 0, 0)
+    assert e.value.status == ccr.CCR_ERR_UNSUPPORTED
+    n = ctypes.c_int64()
+    assert ccr._lib.ccr_ring_hop_layout(8, (1 << 35) - (1 << 14), 1, 0, 0, 0, 0, None, 0,
+                                        ctypes.byref(n)) == ccr.CCR_OK
+    assert n.value == 8 * ((1 << 21) - 1)
     for args in [(1, 10, 1, 0, 0, 0), (4, 10, 1, 0, 2, 0), (4, 10, 1, 0, 0, 3), (4, 10, 2, 0, 0, 0, 2),
                  (4, 10, 1, 5, 0, 0)]:
         with pytest.raises(ccr.CcrError) as e:

@@ -235,15 +235,17 @@ def test_profile_intervals(ccr_mod, budget):
 
 @pytest.mark.parametrize("env", [{"HIP_LAUNCH_BLOCKING": "1"}, {"CCR_NONTEMPORAL": "0"},
                                  {"CCR_NONTEMPORAL": "1"}, {"CCR_NONTEMPORAL": "2"},
-                                 {"CCR_RING_HOPS": "table"}],
+                                 {"CCR_RING_HOPS": "table"}, {"CCR_GRID": "64"}],
                          ids=lambda e: "-".join(f"{k}={v}" for k, v in e.items()))
 def test_process_settings_do_not_change_bits(ccr_mod, tmp_path, env):
     """Settings read once per process leave the bits unchanged in every
     mode: HIP_LAUNCH_BLOCKING=1 (every launch waits for the previous one),
     each forced non-temporal mode of the streaming kernels (none, every
-    load and store, the incoming load only), and ring hops launched from
-    the piece table instead of the rank base addresses.  Each case runs in
-    a child process of its own."""
+    load and store, the incoming load only), ring hops launched from the
+    piece table instead of the rank base addresses, and piece-table launches
+    capped at 64 workgroups, each looping over many tiles (the form every
+    launch past one dispatch's 2^24 - 1 workgroups takes).  Each case runs
+    in a child process of its own."""
     import os
     import subprocess
     import sys
