@@ -296,3 +296,33 @@ def test_range_entry_point_equals_the_unsplit_oracle(dt, acc, R, n, S):
         assert got[q].tobytes() == ref[q].tobytes(), f"threads, rank {q}"
     with pytest.raises(ValueError):
         oracle.ring_allreduce_range([x.copy() for x in xs], 0, n + 1, S, acc, part)
+
+
+# a seeded sweep of the same invariants over random shapes (the GPU sweeps
+# compare against the oracle over this whole space)
+_SWEEP = [(int(R), int(n), int(S), dt, acc)
+          for R, n, S, dt, acc in (
+              (rng.choice([1, 2, 3, 4, 5, 7, 8, 13, 16, 31, 64]), int(10 ** rng.uniform(0, 4.3)),
+               rng.integers(1, 9), *[("f32", "per_hop"), ("bf16", "per_hop"),
+                                     ("bf16", "fp32_partials")][rng.integers(0, 3)])
+              for rng in [np.random.default_rng(606)] for _ in range(150))]
+
+
+@pytest.mark.parametrize("R,n,S,dt,acc", _SWEEP)
+def test_invariants_random_shapes(R, n, S, dt, acc):
+    xs = workloads.random_buffers(R, n, dt, seed=R * 31 + n, dist="normal", scale=1.0)
+    ref = oracle.ring_allreduce(xs, S=S, bf16_acc=acc)
+    one = oracle.ring_allreduce(xs, S=1, bf16_acc=acc)
+    fold = oracle.fold(xs, bf16_acc=acc)
+    for q in range(R):
+        assert ref[q].tobytes() == fold.tobytes() and one[q].tobytes() == fold.tobytes()
+    if n:
+        idx = np.random.default_rng(n).integers(0, n, 64)
+        np.testing.assert_array_equal(oracle.fold_at(xs, idx, bf16_acc=acc), fold[idx])
+    vec = 4 if dt == "f32" else 8
+    rs = oracle.ring_reduce_scatter(xs, S=S, bf16_acc=acc)
+    for c in range(R):
+        lo, hi = oracle.chunk_bounds(n, R, vec, c)
+        np.testing.assert_array_equal(rs[c][lo:hi], fold[lo:hi])
+    for q, b in enumerate(oracle.ring_all_gather(rs, S=S)):
+        assert b.tobytes() == fold.tobytes(), f"rank {q}"
