@@ -96,3 +96,38 @@ def test_noalloc_replays_from_a_graph(ccr_mod):
             torch.cuda.synchronize()
             for a, x in zip(dst, src):
                 assert to_host(a).tobytes() == to_host(x).tobytes(), f"replay {rep}"
+
+
+def _random_cases(seed=3131, n=40):
+    """(case, chunk, slots, [(transfers, bytes)] x 2, the second call smaller),
+    chunk x slots within the fixed scratch, at most ~2000 chunks per call."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        slots = int(rng.integers(1, 5))
+        calls = sorted(((int(rng.integers(1, 6)), 16 * int(10 ** rng.uniform(0, 5.5))) for _ in range(2)),
+                       key=lambda c: -c[0] * c[1])
+        top = (SCRATCH_BYTES // slots) // 16
+        low = -(-calls[0][0] * calls[0][1] // (2000 * 16))
+        chunk = 16 * int(min(top, max(low, 10 ** rng.uniform(0, np.log10(top)))))
+        out.append((i, chunk, slots, calls))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"case{c[0]}")
+def test_noalloc_random_shapes(ccr_mod, case):
+    """Random chunk sizes, slot counts and transfers: two calls in a row (the
+    second smaller), each byte for byte as the allocating call."""
+    import torch
+    i, chunk, slots, calls = case
+    with ccr_mod.Context(0, ccr_mod.Config(staging_chunk_bytes=chunk, staging_slots=slots)) as c:
+        for k, (m, nbytes) in enumerate(calls):
+            say(f"noalloc random case {i} call {k}: chunk={chunk} slots={slots} m={m} nbytes={nbytes}")
+            src = [raw_to_dev(x) for x in _sources(m, nbytes, 100 * i + k)]
+            want = [torch.zeros_like(x) for x in src]
+            got = [torch.full_like(x, 7) for x in src]
+            ccr_mod.ccr_sendrecv_batch(c, src, want)
+            assert _noalloc(ccr_mod, c, src, got) == ccr_mod.CCR_OK, ccr_mod.ccr_last_error()
+            torch.cuda.synchronize()
+            for a, b, x in zip(got, want, src):
+                assert to_host(a).tobytes() == to_host(b).tobytes() == to_host(x).tobytes()
