@@ -1179,7 +1179,7 @@ def main():
     if args.ring_only:
         args.no_gemm = args.no_cpu = True
 
-    gemm = pp = occ = launch = None
+    gemm = ag_only = pp = occ = launch = None
     if not args.no_gemm:
         log("bench: concurrent GEMM, gradient-bucket all-reduce")
         # kernel copies over CU budgets, SDMA copies over the same budgets
@@ -1191,6 +1191,14 @@ def main():
         runs.append(dict(cfg, copy_mode="sdma", dma_sync="stream_flags"))
         gemm = guarded("gemm_slowdown", lambda: overlap_runs(
             ccr, lambda ctx, st: ccr.ccr_allreduce(ctx, bufs, stream=st), runs, (8192, 8192, 8192), 20, 6))
+        log("bench: concurrent GEMM, the bucket's all-gather alone (the copy paths isolated)")
+        # the reduce-scatter runs on compute units in either mode; all-gather
+        # calls alone compare the two copy paths on the same bytes
+        ag_only = guarded("gemm_slowdown_all_gather_only", lambda: overlap_runs(
+            ccr, lambda ctx, st: ccr.ccr_all_gather(ctx, bufs, stream=st),
+            [dict(cfg, copy_mode="kernel"), dict(cfg, copy_mode="sdma"),
+             dict(cfg, copy_mode="sdma", dma_engines=4), dict(cfg, copy_mode="sdma", dma_engines=2)],
+            (8192, 8192, 8192), 20, 6))
         log("bench: concurrent GEMM, pipeline-parallel send/recv through staging")
         pw = workloads.PP_STAGING_BF16
         mbs = [torch.randn(pw.rows, pw.cols, device="cuda").to(torch.bfloat16)
@@ -1284,6 +1292,7 @@ def main():
             slowdown_key(r): r["slowdown_mean_pct"] for r in gemm["runs"]
             if r["cu_budget"] == 256 and r["dma_sync"] in (None, "host_func")},
         "gemm_slowdown": gemm,
+        "gemm_slowdown_all_gather_only": ag_only,
         "pp_staging_gemm_slowdown": pp,
         "cu_occupancy": occ,
         "host_us_per_call": launch,
@@ -1292,7 +1301,9 @@ def main():
         **({"errors": errors} if errors else {}),
     }
     # last, so that a tail of the output line still shows it
-    line["sdma_vs_kernel"] = {k: compact_verdict(v) for k, v in (("bucket", gemm), ("pp_staging", pp))
+    line["sdma_vs_kernel"] = {k: compact_verdict(v) for k, v in (("bucket", gemm),
+                                                                  ("bucket_all_gather_only", ag_only),
+                                                                  ("pp_staging", pp))
                               if v is not None}
     ctx.close()
     print(json.dumps(line), flush=True)
