@@ -166,7 +166,10 @@ TILE_BYTES = 2 * 256 * 16  # a ring-hop workgroup's tile: 2 x 256 16-byte vector
     (4, 64, 5, 1), (6, 3 * 65536 + 11, 4, 0),
     # whole chunks of 48 bf16 and a ragged one of 40, 5 slices: slices 3 and 4
     # of a whole chunk are empty while slice 3 of the ragged chunk is not
-    (2, 88, 5, 1)])
+    (2, 88, 5, 1)] + [
+    # and 60 seeded random shapes
+    (int(R), int(10 ** rng.uniform(0, 5.3 if R < 32 else 4.7)), int(rng.integers(1, 9)), int(rng.integers(0, 2)))
+    for rng in [np.random.default_rng(8080)] for R in rng.choice([2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 17, 31, 32, 64], 60)])
 def test_ring_hop_layout_covers_the_schedule(R, count, S, dtype):
     """The ring-hop kernel's own index arithmetic (the function the kernel
     runs, called on the host): for every hop, its workgroups cover exactly
