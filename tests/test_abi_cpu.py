@@ -81,7 +81,10 @@ def test_config_defaults_and_environment(monkeypatch):
 @pytest.mark.parametrize("R,count,S,dtype", [(1, 10, 1, 0), (2, 40, 1, 0), (3, 12, 1, 0),
                                              (4, 1 << 20, 2, 0), (5, 1001, 3, 1), (8, 26214400, 4, 1),
                                              (7, 3, 2, 0), (32, 8388608, 4, 0), (64, 1000, 2, 1),
-                                             (6, 0, 1, 0)])
+                                             (6, 0, 1, 0)] + [
+    # and 40 seeded random shapes
+    (int(R), int(10 ** rng.uniform(0, 7)), int(rng.integers(1, 7)), int(rng.integers(0, 2)))
+    for rng in [np.random.default_rng(5150)] for R in rng.integers(1, 34, 40)])
 def test_ring_schedule_is_the_textbook_ring(R, count, S, dtype):
     V = 4 if dtype == 0 else 8
     ops = ccr.ccr_ring_schedule(R, count, S, dtype, which=0)
